@@ -1,0 +1,134 @@
+"""CPU oracle for paged-KV causal GQA attention (fp64, plain C).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()``
+and by the CPU-baseline leg of ``bench.py``; never by the product package.
+It shares no code with the HIP library.  See ``pkv_oracle.c`` for what it
+computes and which passage of the pages each step follows.
+
+Parity status: every function here is pinned by the CPU tests in
+``tests/test_oracle.py`` (hand-worked golden cases, closed forms, a library
+routine on special cases, brute force on tiny inputs, invariants, and planted
+mistakes that the pins must catch).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pkv_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+ERRORS = {0: "ok", -1: "bad arguments", -2: "invalid block id or position", -3: "two rows target one slot",
+          -4: "out of memory"}
+
+
+def build(src: str = _SRC, out: str = LIB_PATH) -> str:
+    """Compile the oracle with gcc (C99, -O2, OpenMP)."""
+    cmd = ["gcc", "-std=c99", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", out, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_U16P = ctypes.POINTER(ctypes.c_uint16)
+_F64P = ctypes.POINTER(ctypes.c_double)
+
+
+def _p(a, typ):
+    return a.ctypes.data_as(typ)
+
+
+class Oracle:
+    """Thin ctypes front of one compiled oracle library."""
+
+    def __init__(self, path: str = LIB_PATH):
+        if not os.path.exists(path):
+            build(out=path) if path == LIB_PATH else None
+        self.lib = ctypes.CDLL(path)
+        self.lib.oracle_kv_append.restype = ctypes.c_int
+        self.lib.oracle_attention.restype = ctypes.c_int
+        self.lib.oracle_attention_rows.restype = ctypes.c_int
+        self.lib.oracle_max_threads.restype = ctypes.c_int
+
+    @staticmethod
+    def _check(rc):
+        if rc != 0:
+            raise OracleError(f"oracle error {rc}: {ERRORS.get(rc, '?')}")
+
+    def max_threads(self) -> int:
+        return int(self.lib.oracle_max_threads())
+
+    def kv_append(self, k_pool, v_pool, k_new, v_new, cu_new_lens, ctx_lens, block_table):
+        """In place on host pools ``[NB][Hkv][B][D]`` (uint16)."""
+        NB, Hkv, B, D = k_pool.shape
+        for a in (k_pool, v_pool, k_new, v_new):
+            assert a.dtype == np.uint16 and a.flags.c_contiguous
+        cu = np.ascontiguousarray(cu_new_lens, dtype=np.int32)
+        ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+        tab = np.ascontiguousarray(block_table, dtype=np.int32)
+        assert k_new.shape[1:] == (Hkv, D) and k_new.shape[0] >= cu[-1]
+        rc = self.lib.oracle_kv_append(_p(k_pool, _U16P), _p(v_pool, _U16P), _p(k_new, _U16P), _p(v_new, _U16P),
+                                       _p(cu, _I32P), _p(ctx, _I32P), _p(tab, _I32P), tab.shape[1],
+                                       ctx.shape[0], Hkv, D, B, NB)
+        self._check(rc)
+
+    def attention(self, q, cu_q_lens, k_pool, v_pool, block_table, seq_lens, num_q_heads, scale,
+                  num_threads: int = 0):
+        """All rows: returns fp64 ``[T_q][Hq][D]``; q is packed ``[T_q][Hq][D]`` uint16."""
+        NB, Hkv, B, D = k_pool.shape
+        q = np.ascontiguousarray(q)
+        cu = np.ascontiguousarray(cu_q_lens, dtype=np.int32)
+        tab = np.ascontiguousarray(block_table, dtype=np.int32)
+        sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        out = np.zeros((int(cu[-1]), num_q_heads, D), dtype=np.float64)
+        rc = self.lib.oracle_attention(_p(out, _F64P), _p(q, _U16P), _p(cu, _I32P), _p(k_pool, _U16P),
+                                       _p(v_pool, _U16P), _p(tab, _I32P), tab.shape[1], _p(sl, _I32P),
+                                       sl.shape[0], num_q_heads, Hkv, D, B, NB, ctypes.c_float(scale),
+                                       num_threads)
+        self._check(rc)
+        return out
+
+    def attention_rows(self, items, q, cu_q_lens, k_pool, v_pool, block_table, seq_lens, num_q_heads, scale,
+                       num_threads: int = 0):
+        """Selected rows: ``items`` is int [n][3] of (seq, row within the
+        sequence's chunk, q head); returns fp64 ``[n][D]``."""
+        NB, Hkv, B, D = k_pool.shape
+        items = np.asarray(items, dtype=np.int32).reshape(-1, 3)
+        s_, r_, h_ = (np.ascontiguousarray(items[:, i]) for i in range(3))
+        q = np.ascontiguousarray(q)
+        cu = np.ascontiguousarray(cu_q_lens, dtype=np.int32)
+        tab = np.ascontiguousarray(block_table, dtype=np.int32)
+        sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        out = np.zeros((items.shape[0], D), dtype=np.float64)
+        rc = self.lib.oracle_attention_rows(_p(out, _F64P), items.shape[0], _p(s_, _I32P), _p(r_, _I32P),
+                                            _p(h_, _I32P), _p(q, _U16P), _p(cu, _I32P), _p(k_pool, _U16P),
+                                            _p(v_pool, _U16P), _p(tab, _I32P), tab.shape[1], _p(sl, _I32P),
+                                            sl.shape[0], num_q_heads, Hkv, D, B, NB, ctypes.c_float(scale),
+                                            num_threads)
+        self._check(rc)
+        return out
+
+    # decode is the one-row-per-sequence case of the same definition
+    def decode(self, q, k_pool, v_pool, block_table, seq_lens, scale, num_threads: int = 0):
+        S, Hq, D = q.shape
+        cu = np.arange(S + 1, dtype=np.int32)
+        return self.attention(q.reshape(S, Hq, D), cu, k_pool, v_pool, block_table, seq_lens, Hq, scale,
+                              num_threads)
+
+
+_default = None
+
+
+def get() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default

@@ -1,0 +1,248 @@
+/*
+ * CPU oracle for paged-KV causal grouped-query attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file, and everything under oracle/, is
+ * called only by the tests, by the smoke check and by the CPU-baseline leg of
+ * the benchmark.  The product path (the HIP library) never links, loads or
+ * calls it, and it shares no code, header or table with that library.
+ *
+ * It is deliberately plain and slow: fp64 arithmetic, one query row at a time,
+ * keys gathered one by one through the block table in logical order.
+ *
+ * What it computes, and where the pages define it:
+ *
+ *  - oracle_kv_append: the paged write of new K/V rows.  "扔掉 vLLM！从零构建
+ *    Qwen3-8B 推理引擎" section 4.3.1 keeps the KV cache as fixed-size blocks
+ *    (256 tokens) taken from a pool, each with separate K and V and a fill
+ *    count, and appends a sequence's new rows into its last block, opening a
+ *    new block when that one is full.  So logical position pos of a sequence
+ *    lives in the sequence's block pos / B at slot pos % B.  "从零搭建AI工程能力：
+ *    手写KV Cache与动态批处理实战" (the SimpleKVCache listing in section 4) writes
+ *    the new rows at the current length and keeps a [heads][seq][dim] order
+ *    inside the buffer, which is the per-block order used here:
+ *    pool[block][kv_head][slot][dim].
+ *
+ *  - oracle_attention / oracle_attention_rows: softmax(Q K^T * scale) V with a
+ *    causal mask, as "从零手搓AI推理引擎：避开调包陷阱的工程实践指南" section 2.2
+ *    defines it: each position sees itself and the positions before it
+ *    (inclusive diagonal), and the softmax subtracts the row maximum before
+ *    exponentiating.  The scale is an argument (the pages use 1/sqrt(head_dim)).
+ *    Query heads are grouped as in page 1 section 4.4.2: query head h reads KV
+ *    head h / (Hq / Hkv), i.e. consecutive query heads share one KV head.
+ *    A query row r of a chunk of n rows appended to a sequence of final length
+ *    L sits at absolute position L - n + r (chunked prefill, page 3 section 3.3;
+ *    decode is the case n = 1).  Masked keys are left out of the softmax; the
+ *    pages' additive -1e9 mask gives exactly the same result in fp64 because at
+ *    least one key (the diagonal) is never masked.  The pages never meet a row
+ *    with no key at all (a decode row of an empty sequence, L = 0); such a row
+ *    is defined here as all zeros.
+ *
+ * bf16 inputs are widened exactly: the 16 bits become the top half of an IEEE
+ * binary32 word, which is then converted to double.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARGS (-1)
+#define ORACLE_ERR_BLOCK (-2)     /* a block id outside [0, num_blocks) or a position past the table */
+#define ORACLE_ERR_DUP_SLOT (-3)  /* two new rows target the same slot */
+#define ORACLE_ERR_OOM (-4)
+
+static double bf16_to_double(uint16_t h) {
+    uint32_t bits = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Sequence that owns packed row t, given cu[0..S] with cu[0] = 0. */
+static int owner_of_row(const int32_t* cu, int num_seqs, int t) {
+    int s = 0;
+    while (s + 1 < num_seqs && cu[s + 1] <= t) ++s;
+    return s;
+}
+
+int oracle_kv_append(uint16_t* k_pool, uint16_t* v_pool,
+                     const uint16_t* k_new, const uint16_t* v_new,
+                     const int32_t* cu_new_lens, const int32_t* ctx_lens,
+                     const int32_t* block_table, int max_blocks_per_seq,
+                     int num_seqs, int num_kv_heads, int head_dim, int block_size,
+                     int num_blocks) {
+    if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks < 0)
+        return ORACLE_ERR_ARGS;
+    const int total = num_seqs > 0 ? cu_new_lens[num_seqs] : 0;
+    /* one flag per physical slot, to catch two rows aimed at the same slot */
+    size_t nslots = (size_t)num_blocks * (size_t)block_size;
+    unsigned char* written = (unsigned char*)calloc(nslots ? nslots : 1, 1);
+    if (!written) return ORACLE_ERR_OOM;
+    int rc = ORACLE_OK;
+    for (int t = 0; t < total && rc == ORACLE_OK; ++t) {
+        int s = owner_of_row(cu_new_lens, num_seqs, t);
+        long pos = (long)ctx_lens[s] + (t - cu_new_lens[s]);
+        long lblock = pos / block_size;
+        long slot = pos % block_size;
+        if (pos < 0 || lblock >= max_blocks_per_seq) { rc = ORACLE_ERR_BLOCK; break; }
+        int blk = block_table[(size_t)s * max_blocks_per_seq + lblock];
+        if (blk < 0 || blk >= num_blocks) { rc = ORACLE_ERR_BLOCK; break; }
+        size_t flag = (size_t)blk * block_size + slot;
+        if (written[flag]) { rc = ORACLE_ERR_DUP_SLOT; break; }
+        written[flag] = 1;
+        for (int g = 0; g < num_kv_heads; ++g) {
+            size_t dst = (((size_t)blk * num_kv_heads + g) * block_size + slot) * head_dim;
+            size_t src = ((size_t)t * num_kv_heads + g) * head_dim;
+            memcpy(k_pool + dst, k_new + src, (size_t)head_dim * sizeof(uint16_t));
+            memcpy(v_pool + dst, v_new + src, (size_t)head_dim * sizeof(uint16_t));
+        }
+    }
+    free(written);
+    return rc;
+}
+
+/*
+ * One output row: query head h of sequence s at absolute position p attends to
+ * keys 0..p of that sequence.  out_row receives head_dim doubles.
+ * Returns ORACLE_ERR_BLOCK if a needed block id is invalid.
+ */
+static int attend_one(double* out_row, const uint16_t* q_row,
+                      const uint16_t* k_pool, const uint16_t* v_pool,
+                      const int32_t* table_row, int max_blocks_per_seq,
+                      int p, int kv_head, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, double scale,
+                      double* z /* scratch, p+1 doubles */) {
+    const int nkeys = p + 1;
+    if (nkeys <= 0) { /* no key at or before this position: the row is zero */
+        for (int d = 0; d < head_dim; ++d) out_row[d] = 0.0;
+        return ORACLE_OK;
+    }
+    if ((nkeys - 1) / block_size >= max_blocks_per_seq) return ORACLE_ERR_BLOCK;
+    /* scores z_j = scale * <q, k_j>, keys gathered through the block table */
+    double zmax = -INFINITY;
+    for (int j = 0; j < nkeys; ++j) {
+        int blk = table_row[j / block_size];
+        if (blk < 0 || blk >= num_blocks) return ORACLE_ERR_BLOCK;
+        const uint16_t* k = k_pool + (((size_t)blk * num_kv_heads + kv_head) * block_size + j % block_size) * head_dim;
+        double dot = 0.0;
+        for (int d = 0; d < head_dim; ++d) dot += bf16_to_double(q_row[d]) * bf16_to_double(k[d]);
+        z[j] = scale * dot;
+        if (z[j] > zmax) zmax = z[j];
+    }
+    /* stable softmax: subtract the maximum, exponentiate, normalise */
+    double denom = 0.0;
+    for (int j = 0; j < nkeys; ++j) {
+        z[j] = exp(z[j] - zmax);
+        denom += z[j];
+    }
+    for (int d = 0; d < head_dim; ++d) out_row[d] = 0.0;
+    for (int j = 0; j < nkeys; ++j) {
+        int blk = table_row[j / block_size];
+        const uint16_t* v = v_pool + (((size_t)blk * num_kv_heads + kv_head) * block_size + j % block_size) * head_dim;
+        for (int d = 0; d < head_dim; ++d) out_row[d] += z[j] * bf16_to_double(v[d]);
+    }
+    for (int d = 0; d < head_dim; ++d) out_row[d] /= denom;
+    return ORACLE_OK;
+}
+
+static int check_heads(int hq, int hkv, int d, int bs) {
+    return hq > 0 && hkv > 0 && hq % hkv == 0 && d > 0 && bs > 0;
+}
+
+/*
+ * Selected output rows.  Item i is (sequence item_seq[i], query row item_row[i]
+ * of that sequence's q_len_s = cu_q_lens[s+1]-cu_q_lens[s] rows, query head
+ * item_head[i]); its result goes to out[i][0..head_dim).
+ * q is packed [cu_q_lens[S]][Hq][D].  num_threads <= 0 uses the OpenMP default.
+ */
+int oracle_attention_rows(double* out, int n_items,
+                          const int32_t* item_seq, const int32_t* item_row, const int32_t* item_head,
+                          const uint16_t* q, const int32_t* cu_q_lens,
+                          const uint16_t* k_pool, const uint16_t* v_pool,
+                          const int32_t* block_table, int max_blocks_per_seq,
+                          const int32_t* seq_lens, int num_seqs,
+                          int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                          int num_blocks, float scale, int num_threads) {
+    if (!check_heads(num_q_heads, num_kv_heads, head_dim, block_size) || n_items < 0) return ORACLE_ERR_ARGS;
+    const int group = num_q_heads / num_kv_heads;
+    int max_len = 1;
+    for (int s = 0; s < num_seqs; ++s) if (seq_lens[s] > max_len) max_len = seq_lens[s];
+    int rc = ORACLE_OK;
+#ifdef _OPENMP
+    if (num_threads > 0) omp_set_num_threads(num_threads);
+#endif
+#pragma omp parallel
+    {
+        double* z = (double*)malloc(sizeof(double) * (size_t)max_len);
+        if (!z) {
+#pragma omp atomic write
+            rc = ORACLE_ERR_OOM;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int i = 0; i < n_items; ++i) {
+            if (!z) continue;
+            int s = item_seq[i], r = item_row[i], h = item_head[i];
+            int n = cu_q_lens[s + 1] - cu_q_lens[s];
+            if (s < 0 || s >= num_seqs || r < 0 || r >= n || h < 0 || h >= num_q_heads) {
+#pragma omp atomic write
+                rc = ORACLE_ERR_ARGS;
+                continue;
+            }
+            int p = seq_lens[s] - n + r; /* absolute position of this query row; < 0 only if seq_len < n */
+            const uint16_t* q_row = q + ((size_t)(cu_q_lens[s] + r) * num_q_heads + h) * head_dim;
+            int e = attend_one(out + (size_t)i * head_dim, q_row, k_pool, v_pool,
+                               block_table + (size_t)s * max_blocks_per_seq, max_blocks_per_seq,
+                               p, h / group, num_kv_heads, head_dim, block_size, num_blocks,
+                               (double)scale, z);
+            if (e != ORACLE_OK) {
+#pragma omp atomic write
+                rc = e;
+            }
+        }
+        free(z);
+    }
+    return rc;
+}
+
+/*
+ * Every output row: out is [cu_q_lens[S]][Hq][D] doubles, laid out like q.
+ */
+int oracle_attention(double* out, const uint16_t* q, const int32_t* cu_q_lens,
+                     const uint16_t* k_pool, const uint16_t* v_pool,
+                     const int32_t* block_table, int max_blocks_per_seq,
+                     const int32_t* seq_lens, int num_seqs,
+                     int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                     int num_blocks, float scale, int num_threads) {
+    if (!check_heads(num_q_heads, num_kv_heads, head_dim, block_size) || num_seqs < 0) return ORACLE_ERR_ARGS;
+    const int total = num_seqs > 0 ? cu_q_lens[num_seqs] : 0;
+    const size_t n_items = (size_t)total * num_q_heads;
+    int32_t* it = (int32_t*)malloc(sizeof(int32_t) * 3 * (n_items ? n_items : 1));
+    if (!it) return ORACLE_ERR_OOM;
+    size_t i = 0;
+    for (int s = 0; s < num_seqs; ++s)
+        for (int r = 0; r < cu_q_lens[s + 1] - cu_q_lens[s]; ++r)
+            for (int h = 0; h < num_q_heads; ++h, ++i) {
+                it[i] = s;
+                it[n_items + i] = r;
+                it[2 * n_items + i] = h;
+            }
+    /* items are enumerated in the same order as the packed output rows */
+    int rc = oracle_attention_rows(out, (int)n_items, it, it + n_items, it + 2 * n_items, q, cu_q_lens,
+                                   k_pool, v_pool, block_table, max_blocks_per_seq, seq_lens, num_seqs,
+                                   num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                                   num_threads);
+    free(it);
+    return rc;
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

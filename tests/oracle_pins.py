@@ -1,0 +1,377 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Every ``pin_*`` function takes an oracle instance and raises AssertionError on
+a mismatch, so the same pins run against the real oracle (``test_oracle.py``)
+and against copies of it with a planted mistake (``test_oracle_mutations.py``),
+which must fail at least one pin.
+
+What pins what:
+  * hand-worked cases in tests/golden (softmax weights, inclusive causal mask,
+    GQA grouping, chunk alignment, max subtraction, append addressing);
+  * a library routine on special cases: torch's CPU fp64
+    scaled_dot_product_attention with an explicit mask, KV heads expanded with
+    repeat_interleave;
+  * brute force on tiny inputs: the dense definition over contiguous K/V that
+    never went through a block table;
+  * closed forms: constant V returns V, scale 0 returns the prefix mean, a
+    single key returns its V row, an empty sequence returns zeros;
+  * invariants: permuting physical block placement, block size 16 vs 256,
+    decode = last prefill row, chunked = unchunked, GQA = MHA with expanded
+    KV heads, permuting query heads inside a group.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+from paged_kv_gqa_scatter_amd.workloads import NAN_SENTINEL, bf16_normal
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------------------
+# small helpers (bf16 bits <-> float, tiny paged cases built by plain indexing)
+# ----------------------------------------------------------------------------
+
+def to_bf16_exact(x) -> np.ndarray:
+    """Exact decimals -> bf16 bits; refuses values bf16 cannot hold."""
+    a = np.asarray(x, dtype=np.float32)
+    t = torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16)
+    assert torch.equal(t.to(torch.float32), torch.from_numpy(np.ascontiguousarray(a))), "value not exact in bf16"
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def place_rows(pool, table_row, rows, start=0):
+    """Write rows [T][Hkv][D] at logical positions start.. of one sequence by
+    plain numpy indexing (independent of any append routine)."""
+    B = pool.shape[2]
+    for t in range(rows.shape[0]):
+        pos = start + t
+        pool[table_row[pos // B], :, pos % B, :] = rows[t]
+
+
+class Tiny:
+    """A random paged case: contiguous K/V per sequence plus its paged copy."""
+
+    def __init__(self, rng, S, hq, hkv, d, bs, seq_lens, q_lens, spare=3, scale=None, perm=None):
+        self.S, self.hq, self.hkv, self.d, self.bs = S, hq, hkv, d, bs
+        self.seq_lens = np.asarray(seq_lens, np.int32)
+        self.q_lens = np.asarray(q_lens, np.int32)
+        self.cu = np.concatenate([[0], np.cumsum(self.q_lens)]).astype(np.int32)
+        nblk = [-(-int(L) // bs) for L in self.seq_lens]
+        self.mbs = max(1, max(nblk))
+        self.nb = sum(nblk) + spare
+        drawn = rng.permutation(self.nb).astype(np.int32)  # always drawn, so the samples below do not move
+        perm = drawn if perm is None else np.asarray(perm, np.int32)
+        self.table = np.full((S, self.mbs), -1, np.int32)
+        o = 0
+        for s in range(S):
+            self.table[s, :nblk[s]] = perm[o:o + nblk[s]]
+            o += nblk[s]
+        self.k = [bf16_normal(rng, (int(L), hkv, d)) for L in self.seq_lens]
+        self.v = [bf16_normal(rng, (int(L), hkv, d)) for L in self.seq_lens]
+        self.q = bf16_normal(rng, (int(self.cu[-1]), hq, d))
+        self.scale = np.float32(1.0 / math.sqrt(d) if scale is None else scale)
+        self.build_pools()
+
+    def build_pools(self):
+        shape = (self.nb, self.hkv, self.bs, self.d)
+        self.kp = np.full(shape, NAN_SENTINEL, np.uint16)
+        self.vp = np.full(shape, NAN_SENTINEL, np.uint16)
+        for s in range(self.S):
+            place_rows(self.kp, self.table[s], self.k[s])
+            place_rows(self.vp, self.table[s], self.v[s])
+
+    def run(self, orc, **kw):
+        return orc.attention(self.q, self.cu, self.kp, self.vp, self.table, self.seq_lens, self.hq, self.scale, **kw)
+
+
+def dense_reference(t: Tiny) -> np.ndarray:
+    """The dense definition over contiguous K/V (never paged): numpy fp64."""
+    G = t.hq // t.hkv
+    out = np.zeros((int(t.cu[-1]), t.hq, t.d))
+    q = bf16_to_f64(t.q)
+    for s in range(t.S):
+        K = bf16_to_f64(t.k[s])
+        V = bf16_to_f64(t.v[s])
+        n, L = int(t.q_lens[s]), int(t.seq_lens[s])
+        for r in range(n):
+            p = L - n + r
+            for h in range(t.hq):
+                if p < 0:
+                    continue
+                z = float(t.scale) * (K[:p + 1, h // G, :] @ q[t.cu[s] + r, h])
+                w = np.exp(z - z.max())
+                out[t.cu[s] + r, h] = (w @ V[:p + 1, h // G, :]) / w.sum()
+    return out
+
+
+def sdpa_reference(t: Tiny) -> np.ndarray:
+    """torch CPU fp64 scaled_dot_product_attention, KV heads expanded with
+    repeat_interleave, explicit boolean mask aligned to the end of the keys."""
+    G = t.hq // t.hkv
+    out = np.zeros((int(t.cu[-1]), t.hq, t.d))
+    for s in range(t.S):
+        n, L = int(t.q_lens[s]), int(t.seq_lens[s])
+        if n == 0 or L == 0:
+            continue
+        q = torch.from_numpy(bf16_to_f64(t.q[t.cu[s]:t.cu[s] + n])).permute(1, 0, 2)  # [Hq][n][D]
+        k = torch.from_numpy(bf16_to_f64(t.k[s])).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        v = torch.from_numpy(bf16_to_f64(t.v[s])).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        pos = torch.arange(n) + (L - n)
+        mask = torch.arange(L)[None, :] <= pos[:, None]
+        o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=float(t.scale))
+        out[t.cu[s]:t.cu[s] + n] = o.permute(1, 0, 2).numpy()
+    return out
+
+
+# ----------------------------------------------------------------------------
+# golden (hand-worked) cases
+# ----------------------------------------------------------------------------
+
+def golden_files():
+    return sorted(f for f in os.listdir(GOLDEN) if f.endswith(".json"))
+
+
+def load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def golden_pools(g):
+    shape = (g["num_blocks"], g["num_kv_heads"], g["block_size"], g["head_dim"])
+    kp = np.full(shape, NAN_SENTINEL, np.uint16)
+    vp = np.full(shape, NAN_SENTINEL, np.uint16)
+    table = np.asarray(g["block_table"], np.int32)
+    place_rows(kp, table[0], to_bf16_exact(g["k_rows"]))
+    place_rows(vp, table[0], to_bf16_exact(g["v_rows"]))
+    return kp, vp, table
+
+
+def pin_golden(orc, name):
+    g = load_golden(name)
+    if g["kind"] == "append":
+        shape = (g["num_blocks"], g["num_kv_heads"], g["block_size"], g["head_dim"])
+        kp = np.full(shape, NAN_SENTINEL, np.uint16)
+        vp = np.full(shape, NAN_SENTINEL, np.uint16)
+        orc.kv_append(kp, vp, to_bf16_exact(g["k_new"]), to_bf16_exact(g["v_new"]), g["cu_new_lens"],
+                      g["ctx_lens"], np.asarray(g["block_table"], np.int32))
+        ek = np.full(shape, NAN_SENTINEL, np.uint16)
+        ev = np.full(shape, NAN_SENTINEL, np.uint16)
+        for w in g["expected_writes"]:
+            ek[w["block"], w["kv_head"], w["slot"]] = to_bf16_exact(w["k"])
+            ev[w["block"], w["kv_head"], w["slot"]] = to_bf16_exact(w["v"])
+        assert np.array_equal(kp, ek) and np.array_equal(vp, ev), name
+        return
+    kp, vp, table = golden_pools(g)
+    q = to_bf16_exact(g["q"])
+    if g["kind"] == "decode":
+        out = orc.decode(q, kp, vp, table, g["seq_lens"], np.float32(g["scale"]))
+    else:
+        out = orc.attention(q, g["cu_q_lens"], kp, vp, table, g["seq_lens"], g["num_q_heads"],
+                            np.float32(g["scale"]))
+    exp = np.asarray(g["expected"], np.float64)
+    assert out.shape == exp.shape, name
+    err = np.abs(out - exp).max()
+    assert err <= g["tol"], f"{name}: max err {err}"
+
+
+def pin_all_golden(orc):
+    for name in golden_files():
+        pin_golden(orc, name)
+
+
+# ----------------------------------------------------------------------------
+# library routine, brute force
+# ----------------------------------------------------------------------------
+
+def _tiny_mix(seed):
+    """A few tiny shapes: several sequences, ragged lengths, chunks on cached
+    context, G in {1, 2, 4}, D in {8, 64}, blocks 4 and 16."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    cases.append(Tiny(rng, 3, 4, 1, 8, 4, [7, 13, 40], [7, 5, 1]))
+    cases.append(Tiny(rng, 2, 8, 2, 64, 16, [33, 17], [9, 17]))
+    cases.append(Tiny(rng, 3, 2, 2, 8, 4, [1, 4, 5], [1, 1, 2]))
+    return cases
+
+
+def pin_vs_sdpa(orc):
+    for i, t in enumerate(_tiny_mix(11)):
+        err = np.abs(t.run(orc) - sdpa_reference(t)).max()
+        assert err <= 1e-12, f"case {i}: |oracle - sdpa| = {err}"
+
+
+def pin_vs_dense(orc):
+    for i, t in enumerate(_tiny_mix(12)):
+        err = np.abs(t.run(orc) - dense_reference(t)).max()
+        assert err <= 1e-12, f"case {i}: |oracle - dense| = {err}"
+
+
+# ----------------------------------------------------------------------------
+# closed forms
+# ----------------------------------------------------------------------------
+
+def pin_constant_v(orc):
+    rng = np.random.default_rng(21)
+    t = Tiny(rng, 2, 4, 2, 64, 16, [37, 5], [3, 1])
+    c = bf16_normal(rng, (t.hkv, t.d))
+    t.v = [np.broadcast_to(c, v.shape).copy() for v in t.v]
+    t.build_pools()
+    out = t.run(orc)
+    G = t.hq // t.hkv
+    want = bf16_to_f64(c)[np.arange(t.hq) // G]
+    # fp64 sums of <= 37 terms: relative error <= 2 * 37 * 2^-53, |c| < 8
+    assert np.abs(out - want[None]).max() <= 2 * 37 * 2.0 ** -53 * 8
+
+
+def pin_scale_zero_mean(orc):
+    rng = np.random.default_rng(22)
+    t = Tiny(rng, 2, 4, 1, 8, 4, [9, 14], [9, 2], scale=0.0)
+    out = t.run(orc)
+    for s in range(t.S):
+        V = bf16_to_f64(t.v[s])
+        n, L = int(t.q_lens[s]), int(t.seq_lens[s])
+        for r in range(n):
+            p = L - n + r
+            want = V[:p + 1, 0, :].mean(axis=0)
+            assert np.abs(out[t.cu[s] + r] - want[None]).max() <= 1e-13
+
+
+def pin_single_key(orc):
+    rng = np.random.default_rng(23)
+    t = Tiny(rng, 2, 4, 2, 64, 16, [1, 20], [1, 20])
+    out = t.run(orc)
+    G = t.hq // t.hkv
+    for s in range(t.S):  # the first row of each sequence sees key 0 alone
+        want = bf16_to_f64(t.v[s][0])[np.arange(t.hq) // G]
+        assert np.array_equal(out[t.cu[s]], want)
+
+
+def pin_empty_sequence(orc):
+    rng = np.random.default_rng(24)
+    t = Tiny(rng, 2, 4, 1, 8, 4, [0, 6], [1, 1])
+    out = t.run(orc)
+    assert np.array_equal(out[0], np.zeros_like(out[0]))
+    assert np.isfinite(out).all()
+
+
+# ----------------------------------------------------------------------------
+# invariants
+# ----------------------------------------------------------------------------
+
+def pin_block_permutation(orc):
+    rng = np.random.default_rng(31)
+    t = Tiny(rng, 3, 4, 2, 8, 4, [11, 23, 6], [11, 3, 1])
+    a = t.run(orc)
+    t2 = Tiny(np.random.default_rng(31), 3, 4, 2, 8, 4, [11, 23, 6], [11, 3, 1],
+              perm=np.random.default_rng(99).permutation(t.nb))
+    assert not np.array_equal(t.table, t2.table)
+    assert np.array_equal(a, t2.run(orc))
+
+
+def pin_block_size_16_vs_256(orc):
+    a = Tiny(np.random.default_rng(32), 1, 4, 1, 64, 16, [308], [300])
+    b = Tiny(np.random.default_rng(32), 1, 4, 1, 64, 256, [308], [300], perm=np.arange(200)[::-1] % 3)
+    b.k, b.v, b.q = a.k, a.v, a.q
+    b.build_pools()
+    assert b.table.shape[1] == 2 and a.table.shape[1] == 20
+    assert np.array_equal(a.run(orc), b.run(orc))
+
+
+def pin_decode_is_last_prefill_row(orc):
+    rng = np.random.default_rng(33)
+    t = Tiny(rng, 1, 4, 1, 64, 16, [45], [45])
+    full = t.run(orc)
+    for L in (1, 16, 17, 45):
+        q = t.q[L - 1:L].reshape(1, t.hq, t.d)
+        dec = orc.decode(q, t.kp, t.vp, t.table, [L], t.scale)
+        assert np.array_equal(dec[0], full[L - 1])
+
+
+def pin_chunked_equals_unchunked(orc):
+    rng = np.random.default_rng(34)
+    t = Tiny(rng, 1, 4, 1, 8, 4, [30], [30])
+    full = t.run(orc)
+    # the last 12 rows as a chunk on 18 cached tokens
+    q = t.q[18:30]
+    out = orc.attention(q, [0, 12], t.kp, t.vp, t.table, [30], t.hq, t.scale)
+    assert np.array_equal(out, full[18:30])
+
+
+def pin_gqa_is_expanded_mha(orc):
+    rng = np.random.default_rng(35)
+    t = Tiny(rng, 2, 8, 2, 8, 4, [13, 7], [5, 7])
+    a = t.run(orc)
+    G = t.hq // t.hkv
+    m = Tiny(np.random.default_rng(35), 2, 8, 8, 8, 4, [13, 7], [5, 7])
+    m.table = t.table
+    m.nb = t.nb
+    m.k = [np.repeat(k, G, axis=1) for k in t.k]
+    m.v = [np.repeat(v, G, axis=1) for v in t.v]
+    m.q = t.q
+    m.scale = t.scale
+    m.build_pools()
+    assert np.array_equal(a, m.run(orc))
+
+
+def pin_head_permutation_in_group(orc):
+    rng = np.random.default_rng(36)
+    t = Tiny(rng, 1, 8, 2, 8, 4, [10], [3])
+    a = t.run(orc)
+    perm = np.array([2, 0, 3, 1, 7, 5, 4, 6])  # stays inside each group of 4
+    t.q = np.ascontiguousarray(t.q[:, perm])
+    b = t.run(orc)
+    assert np.array_equal(b, a[:, perm])
+
+
+# ----------------------------------------------------------------------------
+# kv_append
+# ----------------------------------------------------------------------------
+
+def pin_append_matches_indexing(orc):
+    rng = np.random.default_rng(41)
+    t = Tiny(rng, 3, 4, 2, 8, 4, [9, 14, 3], [1, 1, 1])
+    shape = t.kp.shape
+    kp = np.full(shape, NAN_SENTINEL, np.uint16)
+    vp = np.full(shape, NAN_SENTINEL, np.uint16)
+    ctx = np.array([2, 5, 0], np.int32)  # some rows start mid-block
+    new = t.seq_lens - ctx
+    cu = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    k_new = np.concatenate([t.k[s][ctx[s]:] for s in range(3)])
+    v_new = np.concatenate([t.v[s][ctx[s]:] for s in range(3)])
+    orc.kv_append(kp, vp, k_new, v_new, cu, ctx, t.table)
+    ek = np.full(shape, NAN_SENTINEL, np.uint16)
+    ev = np.full(shape, NAN_SENTINEL, np.uint16)
+    for s in range(3):
+        place_rows(ek, t.table[s], t.k[s][ctx[s]:], start=int(ctx[s]))
+        place_rows(ev, t.table[s], t.v[s][ctx[s]:], start=int(ctx[s]))
+    assert np.array_equal(kp, ek) and np.array_equal(vp, ev)
+
+
+def pin_append_rejects_duplicate_slot(orc):
+    import oracle as _o
+    kp = np.full((2, 1, 4, 2), NAN_SENTINEL, np.uint16)
+    vp = kp.copy()
+    rows = to_bf16_exact(np.ones((2, 1, 2)))
+    table = np.array([[1], [1]], np.int32)  # both sequences point at block 1
+    try:
+        orc.kv_append(kp, vp, rows, rows, [0, 1, 2], [0, 0], table)
+    except _o.OracleError:
+        return
+    raise AssertionError("duplicate slot not reported")
+
+
+ALL_PINS = [pin_all_golden, pin_vs_sdpa, pin_vs_dense, pin_constant_v, pin_scale_zero_mean, pin_single_key,
+            pin_empty_sequence, pin_block_permutation, pin_block_size_16_vs_256, pin_decode_is_last_prefill_row,
+            pin_chunked_equals_unchunked, pin_gqa_is_expanded_mha, pin_head_permutation_in_group,
+            pin_append_matches_indexing, pin_append_rejects_duplicate_slot]
