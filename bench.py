@@ -1,0 +1,191 @@
+"""Benchmark: paged GQA attention on one MI355X.
+
+Headline workload: one Qwen3-8B layer decode step -- 8 sequences, 32 query /
+8 KV heads, head_dim 128, bf16, 256-token blocks, cached context uniform in
+[512, 2048]; a step appends one token per sequence (kv_append) and decodes
+(paged_gqa_decode).  ``value`` is the decode KV-read rate: the unique K/V bytes
+a step must read, divided by the wall time per step.  Pool copies are rotated
+(>= 1 GiB in total) so that every step reads from HBM, not from the 256 MB
+last-level cache.
+
+The metric also names prefill: the Qwen3-8B causal prefill workload (4 prompts
+of 1024..4096 tokens) is timed in the same run and reported as causal TFLOP/s
+(4 * D * Hq flops per unmasked query/key pair) under ``prefill``.
+
+Kernel durations are measured with HIP events on the stream the kernels run
+on; ``roofline`` relates the decode call to HBM peak, ``prefill.roofline`` the
+prefill kernel to dense bf16 MFMA peak.  ``cpu_baseline`` times the fp64 CPU
+oracle on the same decode step (all host cores), a reference point only.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+ROTATE_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def time_decode_workload(args):
+    import torch
+    from paged_kv_gqa_scatter_amd import workloads as W
+    from paged_kv_gqa_scatter_amd.runner import DeviceCase
+
+    case = W.config2_decode()
+    dec = case.steps[0].decode
+    kv_bytes = W.decode_unique_kv_bytes(case, dec)
+    n_rot = max(1, -(-ROTATE_BYTES // case.pool_bytes))
+    dc = DeviceCase(case, pools=n_rot)
+    dc.run_fills()
+    step = dc.steps[0]
+    stream = torch.cuda.current_stream()
+
+    def run(i, ev=None):
+        r = i % n_rot
+        dc.append(step["append"], pool=r)
+        if ev is not None:
+            ev[0].record(stream)
+        dc.decode(step["decode"], pool=r)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        run(i, evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / args.steps
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return case, dec, kv_bytes, n_rot, step_ms, dec_ms
+
+
+def time_prefill_workload(args):
+    import torch
+    from paged_kv_gqa_scatter_amd import workloads as W
+    from paged_kv_gqa_scatter_amd.runner import DeviceCase
+
+    case = W.config3_prefill()
+    pf = case.steps[0].prefill
+    flops = W.prefill_causal_flops(case, pf)
+    dc = DeviceCase(case)
+    dc.run_fills()
+    step = dc.steps[0]
+    dc.append(step["append"])
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        dc.prefill(step["prefill"])
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.prefill_steps)]
+    for a, b in evs:
+        a.record(stream)
+        dc.prefill(step["prefill"])
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return case, flops, ms
+
+
+def cpu_baseline(case, dec, kv_bytes, seconds):
+    """The fp64 oracle on the same decode step, repeated for about `seconds`."""
+    import oracle
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    orc = oracle.get()
+    K = case.empty_pool()
+    V = case.empty_pool()
+    for f in case.fills:
+        orc.kv_append(K, V, f.k_new, f.v_new, f.cu_new_lens, f.ctx_lens, f.block_table)
+    a = case.steps[0].append
+    orc.kv_append(K, V, a.k_new, a.v_new, a.cu_new_lens, a.ctx_lens, a.block_table)
+    reps = 0
+    t = time.perf_counter()
+    while True:
+        orc.decode(dec.q, K, V, dec.block_table, dec.seq_lens, case.scale)
+        reps += 1
+        el = time.perf_counter() - t
+        if el >= seconds:
+            break
+    return {"value": round(kv_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": orc.max_threads(),
+            "kind": "oracle",
+            "sample": f"the whole decode step ({dec.seq_lens.shape[0]} seqs, {int(dec.seq_lens.sum())} keys, "
+                      f"32/8 heads, d128), fp64, repeated {reps}x over {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench needs a GPU"
+
+    case, dec, kv_bytes, n_rot, step_ms, dec_ms = time_decode_workload(args)
+    gbs = kv_bytes / (step_ms * 1e-3) / 1e9
+    dec_gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
+    line = {
+        "metric": "paged GQA attn: decode KV-read GB/s + prefill causal TFLOP/s (bf16, 1 GPU)",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3-8b one-layer decode step: kv_append + paged_gqa_decode, 8 seqs, ctx U[512,2048], "
+                               "32q/8kv heads, d128, block 256",
+                   "seqs": int(dec.seq_lens.shape[0]), "keys": int(dec.seq_lens.sum()),
+                   "unique_kv_bytes": int(kv_bytes), "pool_copies_rotated": n_rot},
+        "roofline": {"bound": "hbm", "kernel": "paged_gqa_decode (split + combine)", "achieved": round(dec_gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "ms": round(dec_ms, 5)},
+    }
+    if not args.no_prefill:
+        pcase, flops, pms = time_prefill_workload(args)
+        tfs = flops / (pms * 1e-3) / 1e12
+        line["prefill"] = {
+            "workload": "qwen3-8b one-layer causal prefill: 4 prompts U[1024,4096], 32q/8kv, d128, block 256",
+            "value": round(tfs, 2), "unit": "TFLOP/s", "causal_flops": int(flops), "ms": round(pms, 5),
+            "roofline": {"bound": "mfma", "kernel": "paged_gqa_prefill", "achieved": round(tfs, 2),
+                         "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+                         "traffic": None}}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, dec, kv_bytes, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * pkv.h - paged-KV causal grouped-query attention for AMD MI355X (gfx950).
+ *
+ * C ABI of libpkv.so.  Three operations, as the Qwen3-8B engine on the page
+ * "扔掉 vLLM！从零构建 Qwen3-8B 推理引擎" uses them:
+ *
+ *   pkv_kv_append        scatter new K/V rows into fixed-size cache blocks
+ *                        (section 4.3.1, the paged KV block manager);
+ *   pkv_paged_gqa_decode one query row per sequence, several query heads
+ *                        sharing one KV head (section 4.4.2);
+ *   pkv_paged_gqa_prefill causal attention of a chunk of query rows over the
+ *                        cached keys plus the chunk itself (section 4.4.1, and
+ *                        chunked prefill on "从零搭建AI工程能力：手写KV Cache与
+ *                        动态批处理实战" section 3.3).
+ *
+ * Attention is softmax(Q K^T * scale) V with an inclusive causal mask, as
+ * "从零手搓AI推理引擎：避开调包陷阱的工程实践指南" section 2.2 defines it.
+ *
+ * Common conventions
+ * ------------------
+ *  - bf16 tensors are passed as uint16_t bit patterns; int32 for indices.
+ *  - Every pointer is a DEVICE pointer owned by the caller.  The library
+ *    allocates nothing, frees nothing, keeps no pointer after a call returns
+ *    and has no mutable global state; calls on different streams may run
+ *    concurrently.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls validate their
+ *    scalar arguments on the host, enqueue kernels on `stream` and return
+ *    without synchronising; nothing is read back from the device.
+ *  - KV pools: K and V are separate arrays of shape
+ *      [num_blocks][num_kv_heads][block_size][head_dim]   (bf16)
+ *    so one (block, kv head) tile is contiguous.
+ *  - block_table: [num_seqs][max_blocks_per_seq] int32; logical position pos
+ *    of sequence s lives in physical block block_table[s][pos / block_size]
+ *    at slot pos % block_size.  Entries past a sequence's last block are never
+ *    read.  Different sequences may map logical blocks to the same physical
+ *    block (a shared prefix) for reading.
+ *  - Query head h uses KV head h / (num_q_heads / num_kv_heads).
+ *  - Supported: head_dim 64 or 128; block_size a power of two in [16, 256];
+ *    num_q_heads / num_kv_heads in {1, 2, 4, 8}; pointers 16-byte aligned.
+ *
+ * Errors: a non-zero return means the arguments were rejected on the host and
+ * nothing was launched or written (PKV_ERR_HIP: a launch failed; earlier
+ * kernels of the same call may have run).  Device-array contents (block ids,
+ * lengths) are preconditions: kernels never read or write outside the
+ * arrays whose sizes the arguments give, but results for invalid contents
+ * are unspecified.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+enum {
+    PKV_OK = 0,
+    PKV_ERR_NULL_POINTER = 1, /* a required pointer is NULL                       */
+    PKV_ERR_BAD_SHAPE = 2,    /* sizes negative, inconsistent or unsupported      */
+    PKV_ERR_MISALIGNED = 3,   /* a tensor pointer is not 16-byte aligned          */
+    PKV_ERR_WORKSPACE = 4,    /* decode workspace missing or too small            */
+    PKV_ERR_HIP = 5           /* a kernel launch failed                           */
+};
+
+/* Returns PKV_ABI_VERSION. */
+int32_t pkv_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* pkv_status_string(int32_t status);
+
+/*
+ * kv_append: write new K/V rows into the paged pools ("扔掉 vLLM！从零构建
+ * Qwen3-8B 推理引擎" section 4.3.1: rows go into the sequence's current block,
+ * a new block once it is full; page "从零搭建AI工程能力" section 4: writes start
+ * at the current length).
+ *
+ *   k_pool, v_pool   [num_blocks][num_kv_heads][block_size][head_dim], written in place
+ *   k_new, v_new     [total_new_tokens][num_kv_heads][head_dim], rows of all
+ *                    sequences packed in sequence order
+ *   cu_new_lens      [num_seqs + 1], cu_new_lens[0] = 0, cu_new_lens[num_seqs] = total_new_tokens;
+ *                    rows cu_new_lens[s] .. cu_new_lens[s+1]-1 belong to sequence s
+ *   ctx_lens         [num_seqs] tokens already cached: row t of sequence s goes
+ *                    to position ctx_lens[s] + t
+ *   block_table      [num_seqs][max_blocks_per_seq]
+ *
+ * A pure bit copy: each new row is copied unchanged.  Preconditions: every
+ * target position is below max_blocks_per_seq * block_size, its block id is in
+ * [0, num_blocks), and no two rows of one call target the same slot.  Rows
+ * breaking the first two are skipped (never written out of bounds).
+ */
+int32_t pkv_kv_append(uint16_t* k_pool, uint16_t* v_pool,
+                      const uint16_t* k_new, const uint16_t* v_new,
+                      const int32_t* cu_new_lens, const int32_t* ctx_lens,
+                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                      int32_t num_seqs, int32_t total_new_tokens, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                      void* stream);
+
+/*
+ * Bytes of device workspace pkv_paged_gqa_decode needs.  total_kv_tokens is a
+ * host-side upper bound on the sum of seq_lens (<= 0: num_seqs * max_seq_len
+ * is assumed).  Returns 0 for unsupported shapes.
+ */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_seq_len, int64_t total_kv_tokens);
+
+/*
+ * paged_gqa_decode: one query row per sequence attends to all seq_lens[s]
+ * keys of that sequence ("扔掉 vLLM！从零构建 Qwen3-8B 推理引擎" section 4.4.2:
+ * each group of consecutive query heads reads its KV head once).
+ *
+ *   out              [num_seqs][num_q_heads][head_dim] bf16, written
+ *   q                [num_seqs][num_q_heads][head_dim] bf16
+ *   k_pool, v_pool   as for kv_append (read only)
+ *   block_table      [num_seqs][max_blocks_per_seq]
+ *   seq_lens         [num_seqs] keys per sequence (the new token included),
+ *                    each <= max_seq_len <= max_blocks_per_seq * block_size
+ *   total_kv_tokens  host-side upper bound on sum(seq_lens) (<= 0: unknown,
+ *                    num_seqs * max_seq_len is assumed); it sizes the splits
+ *   scale            softmax scale (usually 1/sqrt(head_dim))
+ *   workspace        device scratch of workspace_bytes >=
+ *                    pkv_decode_workspace_bytes(...) with the same shapes and
+ *                    total_kv_tokens; it needs no initialisation, and calls
+ *                    that share it must be ordered
+ *
+ * Long sequences are split into chunks of keys whose partial results are
+ * merged with a log-sum-exp combine.  A sequence with seq_len 0 yields zeros.
+ * Supports num_seqs <= 8192.
+ */
+int32_t pkv_paged_gqa_decode(uint16_t* out, const uint16_t* q,
+                             const uint16_t* k_pool, const uint16_t* v_pool,
+                             const int32_t* block_table, int32_t max_blocks_per_seq,
+                             const int32_t* seq_lens, int32_t max_seq_len, int64_t total_kv_tokens,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                             float scale, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * paged_gqa_prefill: causal attention for a chunk of q_len_s query rows per
+ * sequence ("扔掉 vLLM！从零构建 Qwen3-8B 推理引擎" section 4.4.1: tiled,
+ * without the full score matrix, skipping key tiles after the query tile).
+ * Row r of sequence s sits at position seq_lens[s] - q_len_s + r and attends
+ * to keys 0 .. that position (the chunk's own K/V must already be appended).
+ *
+ *   out              [total_q_tokens][num_q_heads][head_dim] bf16, written
+ *   q                [total_q_tokens][num_q_heads][head_dim] bf16, rows packed
+ *   cu_q_lens        [num_seqs + 1], q_len_s = cu_q_lens[s+1] - cu_q_lens[s],
+ *                    each <= max_q_len and <= seq_lens[s]
+ *   seq_lens         [num_seqs] cached + chunk tokens, each <= max_seq_len
+ *                    <= max_blocks_per_seq * block_size
+ */
+int32_t pkv_paged_gqa_prefill(uint16_t* out, const uint16_t* q,
+                              const int32_t* cu_q_lens, int32_t total_q_tokens, int32_t max_q_len,
+                              const uint16_t* k_pool, const uint16_t* v_pool,
+                              const int32_t* block_table, int32_t max_blocks_per_seq,
+                              const int32_t* seq_lens, int32_t max_seq_len,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,190 @@
+"""paged_kv_gqa_scatter_amd: paged-KV causal GQA attention on AMD MI355X.
+
+A thin ctypes binding over ``libpkv.so`` (HIP kernels for gfx950 behind the C
+ABI declared in ``include/pkv.h``).  It only marshals arguments: it checks
+dtypes, shapes and devices, passes ``data_ptr()`` values and the current
+torch stream, and raises on a non-zero status.  Every step of the attention
+runs in the library's kernels; there is no fallback of any kind: the first
+call raises ImportError when the library has not been built.
+
+Tensors: bf16 tensors may be ``torch.bfloat16`` (or 16-bit integer views of the
+same bits); index tensors are ``torch.int32``; all on the same CUDA device.
+Host-side size bounds (``max_seq_len``, ``max_q_len``, ``total_kv_tokens``)
+are explicit arguments, so no call reads anything back from the device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+STATUS = {0: "PKV_OK", 1: "PKV_ERR_NULL_POINTER", 2: "PKV_ERR_BAD_SHAPE", 3: "PKV_ERR_MISALIGNED",
+          4: "PKV_ERR_WORKSPACE", 5: "PKV_ERR_HIP"}
+EXPORTS = ("pkv_abi_version", "pkv_status_string", "pkv_kv_append", "pkv_decode_workspace_bytes",
+           "pkv_paged_gqa_decode", "pkv_paged_gqa_prefill")
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({lib().pkv_status_string(status).decode()})")
+
+
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"libpkv.so is not built ({path}); run `python __graft_entry__.py build` "
+                          f"or `python -m paged_kv_gqa_scatter_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.pkv_abi_version.restype = I32
+    lib.pkv_abi_version.argtypes = []
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_status_string.argtypes = [I32]
+    lib.pkv_kv_append.restype = I32
+    lib.pkv_kv_append.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P]
+    lib.pkv_decode_workspace_bytes.restype = SZ
+    lib.pkv_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I64]
+    lib.pkv_paged_gqa_decode.restype = I32
+    lib.pkv_paged_gqa_decode.argtypes = [P, P, P, P, P, I32, P, I32, I64, I32, I32, I32, I32, I32, I32, F32, P, SZ, P]
+    lib.pkv_paged_gqa_prefill.restype = I32
+    lib.pkv_paged_gqa_prefill.argtypes = [P, P, P, I32, I32, P, P, P, I32, P, I32, I32, I32, I32, I32, I32, I32,
+                                          F32, P]
+    return lib
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libpkv.so (loaded on first use; raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
+
+_BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _bf16(t: torch.Tensor, name: str, ndim: int) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or t.dtype not in _BF16_LIKE:
+        raise TypeError(f"{name} must be a bf16 tensor")
+    if t.dim() != ndim or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous {ndim}-d CUDA tensor")
+    return t
+
+
+def _i32(t: torch.Tensor, name: str, ndim: int) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.int32:
+        raise TypeError(f"{name} must be an int32 tensor")
+    if t.dim() != ndim or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous {ndim}-d CUDA tensor")
+    return t
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _pool_shape(k_pool, v_pool):
+    _bf16(k_pool, "k_pool", 4)
+    _bf16(v_pool, "v_pool", 4)
+    if k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool must have the same shape")
+    return tuple(k_pool.shape)  # (num_blocks, num_kv_heads, block_size, head_dim)
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        raise PkvError(st, what)
+
+
+def kv_append(k_pool, v_pool, k_new, v_new, cu_new_lens, ctx_lens, block_table) -> None:
+    """Scatter rows ``k_new/v_new [T][Hkv][D]`` into the pools at positions
+    ``ctx_lens[s] ..`` of each sequence (see ``pkv_kv_append``)."""
+    NB, Hkv, B, D = _pool_shape(k_pool, v_pool)
+    _bf16(k_new, "k_new", 3)
+    _bf16(v_new, "v_new", 3)
+    if k_new.shape != v_new.shape or tuple(k_new.shape[1:]) != (Hkv, D):
+        raise ValueError("k_new/v_new must be [T][num_kv_heads][head_dim]")
+    _i32(cu_new_lens, "cu_new_lens", 1)
+    _i32(ctx_lens, "ctx_lens", 1)
+    _i32(block_table, "block_table", 2)
+    S = ctx_lens.shape[0]
+    if cu_new_lens.shape[0] != S + 1 or block_table.shape[0] != S:
+        raise ValueError("cu_new_lens must have num_seqs+1 entries and block_table num_seqs rows")
+    st = lib().pkv_kv_append(k_pool.data_ptr(), v_pool.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                            cu_new_lens.data_ptr(), ctx_lens.data_ptr(), block_table.data_ptr(),
+                            block_table.shape[1], S, k_new.shape[0], Hkv, D, B, NB, _stream())
+    _check(st, "kv_append")
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int, max_seq_len: int,
+                           total_kv_tokens: int = 0) -> int:
+    n = lib().pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                        total_kv_tokens)
+    if n == 0 and num_seqs > 0:
+        raise PkvError(2, "decode_workspace_bytes")
+    return int(n)
+
+
+def paged_gqa_decode(q, k_pool, v_pool, block_table, seq_lens, scale: float, *, max_seq_len: int,
+                     total_kv_tokens: int = 0, out=None, workspace=None):
+    """One query row per sequence: ``q [S][Hq][D]`` -> ``out [S][Hq][D]`` bf16.
+    ``workspace`` (uint8 CUDA tensor) is allocated if not given."""
+    NB, Hkv, B, D = _pool_shape(k_pool, v_pool)
+    _bf16(q, "q", 3)
+    S, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError("q head_dim differs from the pools'")
+    _i32(block_table, "block_table", 2)
+    _i32(seq_lens, "seq_lens", 1)
+    if block_table.shape[0] != S or seq_lens.shape[0] != S:
+        raise ValueError("block_table and seq_lens need one row per sequence")
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _bf16(out, "out", 3)
+    if tuple(out.shape) != (S, Hq, D):
+        raise ValueError("out must be [S][Hq][D]")
+    need = decode_workspace_bytes(S, Hq, Hkv, D, max_seq_len, total_kv_tokens) if S > 0 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
+    st = lib().pkv_paged_gqa_decode(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                   block_table.data_ptr(), block_table.shape[1], seq_lens.data_ptr(), max_seq_len,
+                                   total_kv_tokens, S, Hq, Hkv, D, B, NB, float(scale), workspace.data_ptr(),
+                                   workspace.numel(), _stream())
+    _check(st, "paged_gqa_decode")
+    return out
+
+
+def paged_gqa_prefill(q, cu_q_lens, k_pool, v_pool, block_table, seq_lens, scale: float, *, max_q_len: int,
+                      max_seq_len: int, out=None):
+    """Causal attention of packed chunk rows ``q [T][Hq][D]`` (see
+    ``pkv_paged_gqa_prefill``) -> ``out [T][Hq][D]`` bf16."""
+    NB, Hkv, B, D = _pool_shape(k_pool, v_pool)
+    _bf16(q, "q", 3)
+    T, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError("q head_dim differs from the pools'")
+    _i32(cu_q_lens, "cu_q_lens", 1)
+    _i32(block_table, "block_table", 2)
+    _i32(seq_lens, "seq_lens", 1)
+    S = seq_lens.shape[0]
+    if cu_q_lens.shape[0] != S + 1 or block_table.shape[0] != S:
+        raise ValueError("cu_q_lens must have num_seqs+1 entries and block_table num_seqs rows")
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _bf16(out, "out", 3)
+    if tuple(out.shape) != (T, Hq, D):
+        raise ValueError("out must be [T][Hq][D]")
+    st = lib().pkv_paged_gqa_prefill(out.data_ptr(), q.data_ptr(), cu_q_lens.data_ptr(), T, max_q_len,
+                                    k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(),
+                                    block_table.shape[1], seq_lens.data_ptr(), max_seq_len, S, Hq, Hkv, D, B, NB,
+                                    float(scale), _stream())
+    _check(st, "paged_gqa_prefill")
+    return out

@@ -1,0 +1,145 @@
+// C ABI of libpkv.so: argument validation, then the launches.  Nothing here
+// touches device memory or synchronises; a rejected call launches nothing.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/pkv.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+
+int device_cu_count() {
+    static std::mutex mu;
+    static std::vector<int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
+
+namespace {
+
+constexpr int32_t kMaxDecodeSeqs = 8192;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool pow2_in(int32_t x, int32_t lo, int32_t hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
+
+// Shape rules shared by the attention calls.
+int32_t check_heads(int32_t hq, int32_t hkv, int32_t d, int32_t bs) {
+    if (hq <= 0 || hkv <= 0 || hq % hkv != 0) return PKV_ERR_BAD_SHAPE;
+    const int32_t g = hq / hkv;
+    if (g != 1 && g != 2 && g != 4 && g != 8) return PKV_ERR_BAD_SHAPE;
+    if (d != 64 && d != 128) return PKV_ERR_BAD_SHAPE;
+    if (!pow2_in(bs, 16, 256)) return PKV_ERR_BAD_SHAPE;
+    return PKV_OK;
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" {
+
+int32_t pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_status_string(int32_t status) {
+    switch (status) {
+        case PKV_OK: return "ok";
+        case PKV_ERR_NULL_POINTER: return "a required pointer is NULL";
+        case PKV_ERR_BAD_SHAPE: return "sizes negative, inconsistent or unsupported";
+        case PKV_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
+        case PKV_ERR_WORKSPACE: return "decode workspace missing or too small";
+        case PKV_ERR_HIP: return "a kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int32_t pkv_kv_append(uint16_t* k_pool, uint16_t* v_pool, const uint16_t* k_new, const uint16_t* v_new,
+                      const int32_t* cu_new_lens, const int32_t* ctx_lens, const int32_t* block_table,
+                      int32_t max_blocks_per_seq, int32_t num_seqs, int32_t total_new_tokens, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks, void* stream) {
+    if (num_seqs < 0 || total_new_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0 || max_blocks_per_seq < 0)
+        return PKV_ERR_BAD_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return PKV_ERR_BAD_SHAPE;
+    if (!pow2_in(block_size, 16, 256)) return PKV_ERR_BAD_SHAPE;
+    if (total_new_tokens > 0 && (num_seqs == 0 || num_blocks == 0 || max_blocks_per_seq == 0))
+        return PKV_ERR_BAD_SHAPE;
+    if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PKV_ERR_BAD_SHAPE;
+    if (total_new_tokens == 0) return PKV_OK;
+    if (!k_pool || !v_pool || !k_new || !v_new || !cu_new_lens || !ctx_lens || !block_table)
+        return PKV_ERR_NULL_POINTER;
+    if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new))
+        return PKV_ERR_MISALIGNED;
+    AppendArgs a{k_pool, v_pool, k_new, v_new, cu_new_lens, ctx_lens, block_table, max_blocks_per_seq,
+                 num_seqs, total_new_tokens, num_kv_heads, head_dim, block_size, num_blocks};
+    return hip_status(launch_kv_append(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_seq_len, int64_t total_kv_tokens) {
+    if (num_seqs < 0 || num_seqs > kMaxDecodeSeqs || max_seq_len < 0) return 0;
+    if (check_heads(num_q_heads, num_kv_heads, head_dim, 16) != PKV_OK) return 0;
+    return plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, total_kv_tokens).bytes;
+}
+
+int32_t pkv_paged_gqa_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                             const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                             int32_t max_seq_len, int64_t total_kv_tokens, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                             float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    int32_t st = check_heads(num_q_heads, num_kv_heads, head_dim, block_size);
+    if (st != PKV_OK) return st;
+    if (num_seqs < 0 || num_seqs > kMaxDecodeSeqs || max_seq_len < 0 || num_blocks < 0 || max_blocks_per_seq < 0)
+        return PKV_ERR_BAD_SHAPE;
+    if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size) return PKV_ERR_BAD_SHAPE;
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !q || !block_table || !seq_lens) return PKV_ERR_NULL_POINTER;
+    if (max_seq_len > 0 && (!k_pool || !v_pool)) return PKV_ERR_NULL_POINTER;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(workspace))
+        return PKV_ERR_MISALIGNED;
+    const DecodePlan pl = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, total_kv_tokens);
+    if (!workspace || workspace_bytes < pl.bytes) return PKV_ERR_WORKSPACE;
+    const int64_t bound = total_kv_tokens > 0 ? total_kv_tokens : (int64_t)num_seqs * max_seq_len;
+    DecodeArgs a{out, q, k_pool, v_pool, block_table, max_blocks_per_seq, seq_lens, max_seq_len, bound,
+                 num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, workspace,
+                 workspace_bytes};
+    return hip_status(launch_decode(a, pl, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pkv_paged_gqa_prefill(uint16_t* out, const uint16_t* q, const int32_t* cu_q_lens, int32_t total_q_tokens,
+                              int32_t max_q_len, const uint16_t* k_pool, const uint16_t* v_pool,
+                              const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                              int32_t max_seq_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, void* stream) {
+    int32_t st = check_heads(num_q_heads, num_kv_heads, head_dim, block_size);
+    if (st != PKV_OK) return st;
+    if (num_seqs < 0 || total_q_tokens < 0 || max_q_len < 0 || max_seq_len < 0 || num_blocks < 0 ||
+        max_blocks_per_seq < 0)
+        return PKV_ERR_BAD_SHAPE;
+    if (max_q_len > max_seq_len || (int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size)
+        return PKV_ERR_BAD_SHAPE;
+    if (total_q_tokens > 0 && (num_seqs == 0 || max_q_len == 0)) return PKV_ERR_BAD_SHAPE;
+    if ((int64_t)max_q_len * num_seqs < total_q_tokens) return PKV_ERR_BAD_SHAPE;
+    if ((int64_t)((max_q_len + 127) / 128) * num_seqs * num_q_heads > INT32_MAX) return PKV_ERR_BAD_SHAPE;
+    if (num_seqs == 0 || total_q_tokens == 0) return PKV_OK;
+    if (!out || !q || !cu_q_lens || !k_pool || !v_pool || !block_table || !seq_lens) return PKV_ERR_NULL_POINTER;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return PKV_ERR_MISALIGNED;
+    PrefillArgs a{out, q, cu_q_lens, total_q_tokens, max_q_len, k_pool, v_pool, block_table, max_blocks_per_seq,
+                  seq_lens, max_seq_len, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                  scale};
+    return hip_status(launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

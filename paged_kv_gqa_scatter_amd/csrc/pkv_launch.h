@@ -1,0 +1,90 @@
+// Host-side launch interface between the C ABI (pkv_api.hip) and the kernels.
+// Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct AppendArgs {
+    uint16_t* k_pool;
+    uint16_t* v_pool;
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    const int32_t* cu_new_lens;
+    const int32_t* ctx_lens;
+    const int32_t* block_table;
+    int32_t max_blocks_per_seq;
+    int32_t num_seqs;
+    int32_t total_new_tokens;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+    int32_t num_blocks;
+};
+
+struct DecodeArgs {
+    uint16_t* out;
+    const uint16_t* q;
+    const uint16_t* k_pool;
+    const uint16_t* v_pool;
+    const int32_t* block_table;
+    int32_t max_blocks_per_seq;
+    const int32_t* seq_lens;
+    int32_t max_seq_len;
+    int64_t total_kv_tokens;  // host bound on sum(seq_lens), > 0
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+    int32_t num_blocks;
+    float scale;
+    void* workspace;
+    size_t workspace_bytes;
+};
+
+struct PrefillArgs {
+    uint16_t* out;
+    const uint16_t* q;
+    const int32_t* cu_q_lens;
+    int32_t total_q_tokens;
+    int32_t max_q_len;
+    const uint16_t* k_pool;
+    const uint16_t* v_pool;
+    const int32_t* block_table;
+    int32_t max_blocks_per_seq;
+    const int32_t* seq_lens;
+    int32_t max_seq_len;
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+    int32_t num_blocks;
+    float scale;
+};
+
+// Decode split plan: keys per split and workspace layout, a pure function of
+// host-known shapes so that the size query and the launch always agree.
+struct DecodePlan {
+    int32_t chunk;            // keys per split (multiple of 64)
+    int64_t max_partials;     // (sequence, split) slots the workspace holds
+    size_t prefix_offset;     // int32 [num_seqs + 1] split prefix
+    size_t lse_offset;        // float [max_partials][num_q_heads]
+    size_t o_offset;          // float [max_partials][num_q_heads][head_dim]
+    size_t bytes;
+};
+DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t max_seq_len, int64_t total_kv_tokens);
+
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace pkv

@@ -1,0 +1,157 @@
+"""Run a seeded workload (``workloads.Case``) through the HIP library.
+
+Plumbing only: it copies the generated inputs to the GPU, creates the pools
+filled with the NaN sentinel, and calls ``kv_append`` / ``paged_gqa_decode`` /
+``paged_gqa_prefill`` in the order the case lists them.  All arithmetic
+happens in the library's kernels.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from . import kv_append, paged_gqa_decode, paged_gqa_prefill, decode_workspace_bytes
+from .workloads import NAN_SENTINEL, AppendBatch, Case, DecodeBatch, PrefillBatch
+
+
+def _bits(a: np.ndarray, device) -> torch.Tensor:
+    """uint16 bf16 bits -> a CUDA bf16 tensor with the same bits."""
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def _i32(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+
+@dataclass
+class DevAppend:
+    k_new: torch.Tensor
+    v_new: torch.Tensor
+    cu_new_lens: torch.Tensor
+    ctx_lens: torch.Tensor
+    block_table: torch.Tensor
+
+
+@dataclass
+class DevDecode:
+    q: torch.Tensor
+    seq_lens: torch.Tensor
+    block_table: torch.Tensor
+    max_seq_len: int
+    total_kv_tokens: int
+    out: torch.Tensor
+    workspace: torch.Tensor
+
+
+@dataclass
+class DevPrefill:
+    q: torch.Tensor
+    cu_q_lens: torch.Tensor
+    seq_lens: torch.Tensor
+    block_table: torch.Tensor
+    max_q_len: int
+    max_seq_len: int
+    out: torch.Tensor
+
+
+class DeviceCase:
+    """A case resident on one GPU: pools, and every batch's inputs and outputs
+    preallocated, so that running a step allocates nothing."""
+
+    def __init__(self, case: Case, device: str = "cuda", pools: int = 1):
+        self.case = case
+        self.device = torch.device(device)
+        shape = (case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim)
+        self.pools = []
+        for _ in range(pools):  # several copies let a timing loop rotate past the caches
+            k = torch.full(shape, NAN_SENTINEL, dtype=torch.int16, device=self.device).view(torch.bfloat16)
+            v = torch.full(shape, NAN_SENTINEL, dtype=torch.int16, device=self.device).view(torch.bfloat16)
+            self.pools.append((k, v))
+        self.fills = [self._append(b) for b in case.fills]
+        self.steps = []
+        for st in case.steps:
+            self.steps.append({
+                "append": self._append(st.append) if st.append is not None else None,
+                "decode": self._decode(st.decode) if st.decode is not None else None,
+                "prefill": self._prefill(st.prefill) if st.prefill is not None else None,
+            })
+
+    @property
+    def k_pool(self):
+        return self.pools[0][0]
+
+    @property
+    def v_pool(self):
+        return self.pools[0][1]
+
+    def _append(self, b: AppendBatch) -> DevAppend:
+        d = self.device
+        return DevAppend(_bits(b.k_new, d), _bits(b.v_new, d), _i32(b.cu_new_lens, d), _i32(b.ctx_lens, d),
+                         _i32(b.block_table, d))
+
+    def _decode(self, b: DecodeBatch) -> DevDecode:
+        d = self.device
+        c = self.case
+        S = b.seq_lens.shape[0]
+        max_len = int(b.seq_lens.max()) if S else 0
+        total = int(b.seq_lens.astype(np.int64).sum())
+        ws = decode_workspace_bytes(S, c.num_q_heads, c.num_kv_heads, c.head_dim, max_len, total) if S else 16
+        return DevDecode(_bits(b.q, d), _i32(b.seq_lens, d), _i32(b.block_table, d), max_len, total,
+                         torch.empty((S, c.num_q_heads, c.head_dim), dtype=torch.bfloat16, device=d),
+                         torch.empty(max(ws, 16), dtype=torch.uint8, device=d))
+
+    def _prefill(self, b: PrefillBatch) -> DevPrefill:
+        d = self.device
+        c = self.case
+        T = int(b.cu_q_lens[-1])
+        return DevPrefill(_bits(b.q, d), _i32(b.cu_q_lens, d), _i32(b.seq_lens, d), _i32(b.block_table, d),
+                          b.max_q_len, int(b.seq_lens.max()) if b.seq_lens.size else 0,
+                          torch.empty((T, c.num_q_heads, c.head_dim), dtype=torch.bfloat16, device=d))
+
+    # ------------------------------------------------------------------ calls
+    def append(self, a: DevAppend, pool: int = 0):
+        k, v = self.pools[pool]
+        kv_append(k, v, a.k_new, a.v_new, a.cu_new_lens, a.ctx_lens, a.block_table)
+
+    def decode(self, dd: DevDecode, pool: int = 0):
+        k, v = self.pools[pool]
+        return paged_gqa_decode(dd.q, k, v, dd.block_table, dd.seq_lens, float(self.case.scale),
+                                max_seq_len=dd.max_seq_len, total_kv_tokens=dd.total_kv_tokens, out=dd.out,
+                                workspace=dd.workspace)
+
+    def prefill(self, pp: DevPrefill, pool: int = 0):
+        k, v = self.pools[pool]
+        return paged_gqa_prefill(pp.q, pp.cu_q_lens, k, v, pp.block_table, pp.seq_lens, float(self.case.scale),
+                                 max_q_len=pp.max_q_len, max_seq_len=pp.max_seq_len, out=pp.out)
+
+    def run_fills(self, pool: Optional[int] = None):
+        for p in (range(len(self.pools)) if pool is None else [pool]):
+            for f in self.fills:
+                self.append(f, p)
+
+    def run_step(self, i: int, pool: int = 0) -> Dict[str, torch.Tensor]:
+        st = self.steps[i]
+        res = {}
+        if st["append"] is not None:
+            self.append(st["append"], pool)
+        if st["decode"] is not None:
+            res["decode"] = self.decode(st["decode"], pool)
+        if st["prefill"] is not None:
+            res["prefill"] = self.prefill(st["prefill"], pool)
+        return res
+
+    def run_all(self) -> list:
+        """Fills, then every step in order; returns each step's outputs as fp64 numpy."""
+        self.run_fills(0)
+        outs = []
+        for i in range(len(self.steps)):
+            r = self.run_step(i)
+            outs.append({k: v.float().cpu().numpy().astype(np.float64) for k, v in r.items()})
+        return outs
+
+    def pools_numpy(self, pool: int = 0):
+        k, v = self.pools[pool]
+        return (k.view(torch.int16).cpu().numpy().view(np.uint16), v.view(torch.int16).cpu().numpy().view(np.uint16))

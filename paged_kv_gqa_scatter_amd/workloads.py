@@ -132,7 +132,8 @@ def _ceil_div(a: int, b: int) -> int:
 
 def build_case(name: str, rng: np.random.Generator, *, hq: int, hkv: int, d: int, bs: int,
                ctx_lens, new_lens, kinds, spare: float = 0.25, num_blocks: Optional[int] = None,
-               shared_prefix: int = 0, shared_seqs=None, scale: Optional[float] = None) -> Case:
+               shared_prefix: int = 0, shared_seqs=None, scale: Optional[float] = None,
+               placement_seed: Optional[int] = None) -> Case:
     """One batch of sequences: ``ctx_lens[s]`` tokens already cached (written
     by the fills), then a step that appends ``new_lens[s]`` tokens and runs
     decode (``kinds[s] == 'd'``, needs new_len 1) or chunked prefill
@@ -142,6 +143,10 @@ def build_case(name: str, rng: np.random.Generator, *, hq: int, hkv: int, d: int
     ``shared_prefix`` tokens (a whole number of blocks) are aliased: the
     sequences listed in ``shared_seqs`` all map their first blocks to the same
     physical blocks, which are written once by a fill of their own.
+
+    ``placement_seed`` replaces the drawn block permutation by one from another
+    generator (the draw still happens, so the samples do not change): the same
+    data at a different physical placement.
     """
     ctx_lens = np.asarray(ctx_lens, dtype=np.int64)
     new_lens = np.asarray(new_lens, dtype=np.int64)
@@ -167,6 +172,8 @@ def build_case(name: str, rng: np.random.Generator, *, hq: int, hkv: int, d: int
 
     # (2) physical placement
     perm = rng.permutation(num_blocks).astype(np.int32)
+    if placement_seed is not None:
+        perm = np.random.default_rng(placement_seed).permutation(num_blocks).astype(np.int32)
     table = np.full((S, mbs), -1, dtype=np.int32)
     nxt = n_pref_blocks
     pref_ids = perm[:n_pref_blocks]

@@ -1,0 +1,86 @@
+"""Run a seeded workload through the CPU oracle (host pools, fp64 outputs),
+and compare GPU outputs against it with the acceptance tolerance."""
+from __future__ import annotations
+
+import numpy as np
+
+# Acceptance bar for attention outputs with bf16 inputs/outputs, over the whole
+# output of a call: relative L2 error <= 1e-2, and every element within 1e-2
+# absolute -- except where bf16 itself cannot hold the exact value that
+# closely: bf16 keeps 8 significant bits, so for |o| >= 2 the spacing of
+# representable outputs exceeds 1e-2 (e.g. the exact -4.11244 lies between
+# -4.125 and -4.09375, and its correctly rounded output -4.125 is 0.0126 away).
+# There an element passes if it is one of the two bf16 values that bracket the
+# exact result, i.e. its error is below one bf16 ulp of the reference.
+TOL_MAX_ABS = 1e-2
+TOL_REL_L2 = 1e-2
+
+
+def bf16_ulp(x):
+    """Spacing of bf16 numbers in the binade of |x| (normal range)."""
+    ax = np.maximum(np.abs(np.asarray(x, np.float64)), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(ax)) - 7)
+
+
+def oracle_pools(case, orc, upto_step=None):
+    """Host pools after the fills and the appends of steps [0, upto_step)."""
+    K = case.empty_pool()
+    V = case.empty_pool()
+    for f in case.fills:
+        orc.kv_append(K, V, f.k_new, f.v_new, f.cu_new_lens, f.ctx_lens, f.block_table)
+    n = len(case.steps) if upto_step is None else upto_step
+    for st in case.steps[:n]:
+        a = st.append
+        orc.kv_append(K, V, a.k_new, a.v_new, a.cu_new_lens, a.ctx_lens, a.block_table)
+    return K, V
+
+
+def oracle_outputs(case, orc):
+    """Every output row of every step, in order (appends applied first)."""
+    K = case.empty_pool()
+    V = case.empty_pool()
+    for f in case.fills:
+        orc.kv_append(K, V, f.k_new, f.v_new, f.cu_new_lens, f.ctx_lens, f.block_table)
+    outs = []
+    for st in case.steps:
+        a = st.append
+        orc.kv_append(K, V, a.k_new, a.v_new, a.cu_new_lens, a.ctx_lens, a.block_table)
+        r = {}
+        if st.decode is not None:
+            d = st.decode
+            r["decode"] = orc.decode(d.q, K, V, d.block_table, d.seq_lens, case.scale)
+        if st.prefill is not None:
+            p = st.prefill
+            r["prefill"] = orc.attention(p.q, p.cu_q_lens, K, V, p.block_table, p.seq_lens, case.num_q_heads,
+                                         case.scale)
+        outs.append(r)
+    return outs, (K, V)
+
+
+def compare(gpu: np.ndarray, ref: np.ndarray, what: str):
+    """Max abs error and relative L2 error over the whole tensor."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert gpu.shape == ref.shape, f"{what}: shape {gpu.shape} vs {ref.shape}"
+    assert np.isfinite(gpu).all(), f"{what}: non-finite GPU output"
+    diff = gpu - ref
+    mx = float(np.abs(diff).max()) if diff.size else 0.0
+    nref = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(diff)) / nref if nref > 0 else float(np.linalg.norm(diff))
+    where = ""
+    if diff.size:
+        i = np.unravel_index(int(np.abs(diff).argmax()), diff.shape)
+        where = f"  worst at {tuple(int(x) for x in i)}: gpu {gpu[i]:.6g} ref {ref[i]:.6g}"
+    ad = np.abs(diff)
+    within_abs = ad <= TOL_MAX_ABS
+    within_ulp = ad < bf16_ulp(ref)
+    n_ulp = int(np.count_nonzero(~within_abs & within_ulp))
+    print(f"  {what}: max|err| {mx:.3e}  rel-L2 {rel:.3e}  ({gpu.size} values){where}"
+          + (f"  [{n_ulp} beyond 1e-2 but within one bf16 ulp]" if n_ulp else ""), flush=True)
+    bad = ~(within_abs | within_ulp)
+    if bad.any():
+        j = np.unravel_index(int(np.argmax(np.where(bad, ad, -1))), ad.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} elements off by more than max(1e-2, one bf16 ulp); "
+                             f"e.g. at {tuple(int(x) for x in j)}: gpu {gpu[j]:.6g} ref {ref[j]:.6g}")
+    assert rel <= TOL_REL_L2, f"{what}: rel-L2 {rel} > {TOL_REL_L2}"
+    return mx, rel

@@ -1,0 +1,120 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every symbol the
+header declares, and rejects bad arguments with the documented status codes
+before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_gqa_scatter_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pkv.LIB_PATH):
+        from paged_kv_gqa_scatter_amd import build
+        build.build()
+    return pkv.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(pkv_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_three_operations():
+    names = declared_functions()
+    for n in ("pkv_kv_append", "pkv_paged_gqa_decode", "pkv_paged_gqa_prefill"):
+        assert n in names
+    assert set(names) == set(pkv.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.pkv_abi_version() == 1
+    for code in range(6):
+        assert lib.pkv_status_string(code)
+    assert lib.pkv_status_string(99) == b"unknown status"
+
+
+A16 = 1 << 12  # any 16-byte aligned non-null address: these calls must be rejected before touching it
+
+
+def append_args(**kw):
+    a = dict(k_pool=A16, v_pool=A16, k_new=A16, v_new=A16, cu=A16, ctx=A16, table=A16, mbs=4, S=2, T=3, hkv=8,
+             d=128, bs=256, nb=10, stream=None)
+    a.update(kw)
+    return (a["k_pool"], a["v_pool"], a["k_new"], a["v_new"], a["cu"], a["ctx"], a["table"], a["mbs"], a["S"],
+            a["T"], a["hkv"], a["d"], a["bs"], a["nb"], a["stream"])
+
+
+def test_append_rejects(lib):
+    f = lib.pkv_kv_append
+    assert f(*append_args(d=96)) == 2
+    assert f(*append_args(bs=48)) == 2
+    assert f(*append_args(bs=512)) == 2
+    assert f(*append_args(bs=8)) == 2
+    assert f(*append_args(S=0)) == 2
+    assert f(*append_args(T=-1)) == 2
+    assert f(*append_args(k_new=None)) == 1
+    assert f(*append_args(table=None)) == 1
+    assert f(*append_args(v_pool=A16 + 2)) == 3
+    assert f(*append_args(T=0, k_new=None)) == 0  # nothing to do, nothing touched
+
+
+def decode_args(**kw):
+    a = dict(out=A16, q=A16, kp=A16, vp=A16, table=A16, mbs=9, lens=A16, maxlen=2049, total=0, S=8, hq=32, hkv=8,
+             d=128, bs=256, nb=50, scale=0.088, ws=A16, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return tuple(a[k] for k in ("out", "q", "kp", "vp", "table", "mbs", "lens", "maxlen", "total", "S", "hq", "hkv",
+                                "d", "bs", "nb", "scale", "ws", "wsb", "stream"))
+
+
+def test_decode_rejects(lib):
+    f = lib.pkv_paged_gqa_decode
+    assert f(*decode_args(hq=30)) == 2          # Hq % Hkv
+    assert f(*decode_args(hq=128, hkv=8)) == 2  # group of 16 unsupported
+    assert f(*decode_args(d=256)) == 2
+    assert f(*decode_args(maxlen=9 * 256 + 1)) == 2  # longer than the table can hold
+    assert f(*decode_args(S=9000)) == 2
+    assert f(*decode_args(q=None)) == 1
+    assert f(*decode_args(out=A16 + 8)) == 3
+    assert f(*decode_args(ws=None)) == 4
+    assert f(*decode_args(wsb=16)) == 4
+    assert f(*decode_args(S=0)) == 0
+
+
+def test_decode_workspace_bytes(lib):
+    f = lib.pkv_decode_workspace_bytes
+    assert f(8, 32, 8, 96, 2049, 0) == 0
+    small = f(8, 32, 8, 128, 2049, 10248)
+    big = f(8, 32, 8, 128, 2049, 0)
+    assert 0 < small <= big
+    assert f(272, 32, 8, 128, 32769, 1_830_000) < f(272, 32, 8, 128, 32769, 0)
+
+
+def prefill_args(**kw):
+    a = dict(out=A16, q=A16, cu=A16, T=1000, maxq=512, kp=A16, vp=A16, table=A16, mbs=8, lens=A16, maxlen=1536,
+             S=2, hq=32, hkv=8, d=128, bs=256, nb=20, scale=0.088, stream=None)
+    a.update(kw)
+    return tuple(a[k] for k in ("out", "q", "cu", "T", "maxq", "kp", "vp", "table", "mbs", "lens", "maxlen", "S", "hq",
+                                "hkv", "d", "bs", "nb", "scale", "stream"))
+
+
+def test_prefill_rejects(lib):
+    f = lib.pkv_paged_gqa_prefill
+    assert f(*prefill_args(maxq=2000)) == 2        # chunk longer than the sequence bound
+    assert f(*prefill_args(T=2000)) == 2           # more rows than num_seqs * max_q_len
+    assert f(*prefill_args(mbs=2)) == 2            # table too short for max_seq_len
+    assert f(*prefill_args(hkv=3)) == 2
+    assert f(*prefill_args(cu=None)) == 1
+    assert f(*prefill_args(q=A16 + 4)) == 3
+    assert f(*prefill_args(T=0)) == 0

@@ -1,0 +1,276 @@
+"""HIP path vs the CPU oracle on the same seeded inputs (needs an MI355X).
+
+kv_append must match bit for bit over the whole pools (never-written slots
+keep the NaN sentinel).  Attention outputs must satisfy max|err| <= 1e-2 and
+relative L2 <= 1e-2 over each call's output (bf16 in/out, fp32 accumulation).
+Full-size workloads are checked on every output where the oracle is cheap
+enough, otherwise on sampled rows the oracle computes one by one.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from case_oracle import compare, oracle_outputs, oracle_pools
+from paged_kv_gqa_scatter_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def _dev():
+    from paged_kv_gqa_scatter_amd.runner import DeviceCase
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return DeviceCase
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+# ---------------------------------------------------------------- kv_append
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_append_bitexact(orc, cfg):
+    case = W.CONFIGS[cfg]()
+    _say(f"case {case.name}: kv_append bit-exact over the pools")
+    dc = _dev()(case)
+    dc.run_fills()
+    for i in range(len(dc.steps)):
+        dc.append(dc.steps[i]["append"])
+    torch.cuda.synchronize()
+    gk, gv = dc.pools_numpy()
+    K, V = oracle_pools(case, orc)
+    assert np.array_equal(gk, K), "K pool differs"
+    assert np.array_equal(gv, V), "V pool differs"
+    assert (gk == W.NAN_SENTINEL).any(), "spare slots should keep the sentinel"
+
+
+def test_append_mid_block_and_block16(orc):
+    # chunks that start mid-block (ctx % B != 0), block size 16, D 64, several sequences
+    rng = np.random.default_rng(77)
+    case = W.build_case("append_mid_block", rng, hq=8, hkv=2, d=64, bs=16, ctx_lens=[5, 17, 0, 31],
+                        new_lens=[40, 1, 16, 3], kinds="pppp")
+    _say(f"case {case.name}")
+    dc = _dev()(case)
+    dc.run_fills()
+    dc.append(dc.steps[0]["append"])
+    torch.cuda.synchronize()
+    gk, gv = dc.pools_numpy()
+    K, V = oracle_pools(case, orc)
+    assert np.array_equal(gk, K) and np.array_equal(gv, V)
+
+
+# ---------------------------------------------------------------- whole workloads
+
+def test_config1_tiny_prefill_then_decodes(orc):
+    case = W.config1_tiny()
+    _say(f"case {case.name}")
+    outs = _dev()(case).run_all()
+    ref, _ = oracle_outputs(case, orc)
+    compare(outs[0]["prefill"], ref[0]["prefill"], "prefill 300 rows")
+    for t in range(1, 9):
+        compare(outs[t]["decode"], ref[t]["decode"], f"decode step {t}")
+
+
+def test_config1_block_size_16_vs_256(orc):
+    a = W.config1_tiny(block_size=16)
+    b = W.config1_tiny(block_size=256)
+    _say("case tiny: block size 16 vs 256")
+    oa = _dev()(a).run_all()
+    ob = _dev()(b).run_all()
+    ref, _ = oracle_outputs(b, orc)
+    for t in range(9):
+        k = "prefill" if t == 0 else "decode"
+        compare(ob[t][k], ref[t][k], f"B=256 step {t}")
+        compare(oa[t][k], ob[t][k], f"B=16 vs B=256 step {t}")
+
+
+def test_config2_decode(orc):
+    case = W.config2_decode()
+    _say(f"case {case.name}")
+    outs = _dev()(case).run_all()
+    ref, _ = oracle_outputs(case, orc)
+    compare(outs[0]["decode"], ref[0]["decode"], "decode 8 seqs")
+
+
+def test_config2_block_permutation_invariance(orc):
+    a = W.config2_decode()
+    rng = np.random.default_rng(2)  # same draws as config 2, then another placement
+    ctx = rng.integers(512, 2048, size=8, endpoint=True)
+    b = W.build_case("decode_replaced", rng, hq=32, hkv=8, d=128, bs=256, ctx_lens=ctx,
+                     new_lens=np.ones(8, np.int64), kinds="d" * 8, placement_seed=1234)
+    assert not np.array_equal(a.steps[0].decode.block_table, b.steps[0].decode.block_table)
+    _say("case decode: same data, different block placement")
+    oa = _dev()(a).run_all()[0]["decode"]
+    ob = _dev()(b).run_all()[0]["decode"]
+    compare(oa, ob, "placement A vs B")
+    print(f"  bit-identical: {np.array_equal(oa, ob)}", flush=True)
+
+
+def _prefill_sample_items(batch, rng, n_random=384):
+    """(seq, row, head) items: tile edges, first/last rows, and random rows."""
+    items = []
+    S = batch.seq_lens.shape[0]
+    Hq = batch.q.shape[1]
+    for s in range(S):
+        n = int(batch.cu_q_lens[s + 1] - batch.cu_q_lens[s])
+        for r in sorted({0, 1, 127, 128, 129, n // 2, n - 129, n - 128, n - 2, n - 1}):
+            if 0 <= r < n:
+                for h in (0, 3, 4, Hq - 1):
+                    items.append((s, r, h))
+    for _ in range(n_random):
+        s = int(rng.integers(S))
+        n = int(batch.cu_q_lens[s + 1] - batch.cu_q_lens[s])
+        items.append((s, int(rng.integers(n)), int(rng.integers(Hq))))
+    return np.array(items, np.int32)
+
+
+def test_config3_prefill_sampled(orc):
+    case = W.config3_prefill()
+    _say(f"case {case.name}: sampled rows")
+    outs = _dev()(case).run_all()
+    K, V = oracle_pools(case, orc)
+    p = case.steps[0].prefill
+    items = _prefill_sample_items(p, np.random.default_rng(33))
+    ref = orc.attention_rows(items, p.q, p.cu_q_lens, K, V, p.block_table, p.seq_lens, case.num_q_heads, case.scale)
+    rows = p.cu_q_lens[items[:, 0]] + items[:, 1]
+    gpu = outs[0]["prefill"][rows, items[:, 2]]
+    compare(gpu, ref, f"prefill {len(items)} sampled rows")
+
+
+def test_prefill_reduced_full(orc):
+    # several 128-row tiles with ragged tails, GQA 4, full comparison
+    rng = np.random.default_rng(303)
+    case = W.build_case("prefill_reduced", rng, hq=32, hkv=8, d=128, bs=256, ctx_lens=[0, 0, 0],
+                        new_lens=[300, 129, 517], kinds="ppp")
+    _say(f"case {case.name}")
+    outs = _dev()(case).run_all()
+    ref, _ = oracle_outputs(case, orc)
+    compare(outs[0]["prefill"], ref[0]["prefill"], "prefill 3 prompts")
+
+
+def test_config4_mixed(orc):
+    case = W.config4_mixed()
+    _say(f"case {case.name}")
+    outs = _dev()(case).run_all()
+    ref, _ = oracle_outputs(case, orc)
+    compare(outs[0]["decode"], ref[0]["decode"], "decode 64 seqs")
+    compare(outs[0]["prefill"], ref[0]["prefill"], "2 chunks of 512 on 1024 cached")
+
+
+@pytest.mark.timeout(900)
+def test_config5_prefix_long_sampled(orc):
+    case = W.config5_prefix_long()
+    _say(f"case {case.name}: sampled sequences")
+    dc = _dev()(case)
+    out = dc.run_all()[0]["decode"]
+    gk, gv = dc.pools_numpy()
+    del dc
+    torch.cuda.empty_cache()
+    K, V = oracle_pools(case, orc)
+    assert np.array_equal(gk, K) and np.array_equal(gv, V), "pools differ"
+    del gk, gv
+    d = case.steps[0].decode
+    S = d.seq_lens.shape[0]
+    pick = sorted(set(np.random.default_rng(55).choice(256, 12, replace=False).tolist()) | {0, 255, 256, 263, S - 1})
+    items = np.array([(s, 0, h) for s in pick for h in range(case.num_q_heads)], np.int32)
+    cu = np.arange(S + 1, dtype=np.int32)
+    ref = orc.attention_rows(items, d.q, cu, K, V, d.block_table, d.seq_lens, case.num_q_heads, case.scale)
+    gpu = out[items[:, 0], items[:, 2]]
+    compare(gpu, ref, f"decode {len(pick)} sequences x all heads")
+
+
+# ---------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("d,bs,hq,hkv", [(128, 256, 32, 8), (64, 16, 4, 1), (128, 16, 16, 2), (64, 256, 8, 8)])
+def test_decode_edge_lengths(orc, d, bs, hq, hkv):
+    # lengths at block edges (the off-by-one lesson of exact multiples), a
+    # single key, an empty sequence, and one long enough for many splits
+    lens = [1, bs - 1, bs, bs + 1, 2 * bs, 512, 8192, 32769, 0]
+    rng = np.random.default_rng(1000 + d + bs)
+    ctx = [max(L - 1, 0) for L in lens]
+    new = [1 if L > 0 else 0 for L in lens]
+    # the empty sequence appends nothing: give it new_len 0 in the append and seq_len 0 in the decode
+    case = W.build_case(f"decode_edges_d{d}_b{bs}", rng, hq=hq, hkv=hkv, d=d, bs=bs, ctx_lens=ctx[:-1],
+                        new_lens=new[:-1], kinds="d" * (len(lens) - 1))
+    dec = case.steps[0].decode
+    dec.seq_lens = np.append(dec.seq_lens, 0).astype(np.int32)
+    dec.block_table = np.vstack([dec.block_table, np.full((1, dec.block_table.shape[1]), -1, np.int32)])
+    dec.q = np.concatenate([dec.q, W.bf16_normal(rng, (1, hq, d))])
+    _say(f"case {case.name}: lens {lens}")
+    out = _dev()(case).run_all()[0]["decode"]
+    ref, _ = oracle_outputs(case, orc)
+    compare(out, ref[0]["decode"], "decode edge lengths")
+    assert np.array_equal(out[-1], np.zeros_like(out[-1])), "empty sequence must give zeros"
+
+
+@pytest.mark.parametrize("ctx", [0, 1000])
+def test_prefill_edge_qlens(orc, ctx):
+    qlens = [1, 127, 128, 129, 255, 256, 257]
+    rng = np.random.default_rng(2000 + ctx)
+    case = W.build_case(f"prefill_edges_ctx{ctx}", rng, hq=8, hkv=2, d=128, bs=256, ctx_lens=[ctx] * len(qlens),
+                        new_lens=qlens, kinds="p" * len(qlens))
+    _say(f"case {case.name}: q_lens {qlens}")
+    out = _dev()(case).run_all()[0]["prefill"]
+    ref, _ = oracle_outputs(case, orc)
+    compare(out, ref[0]["prefill"], "prefill edge q_lens")
+
+
+def test_prefill_d64_block16_chunked(orc):
+    rng = np.random.default_rng(404)
+    case = W.build_case("prefill_d64_b16", rng, hq=4, hkv=1, d=64, bs=16, ctx_lens=[0, 37, 300],
+                        new_lens=[300, 91, 8], kinds="ppp")
+    _say(f"case {case.name}")
+    out = _dev()(case).run_all()[0]["prefill"]
+    ref, _ = oracle_outputs(case, orc)
+    compare(out, ref[0]["prefill"], "prefill d64 b16")
+
+
+def test_decode_equals_last_prefill_rows(orc):
+    # prefill of all 308 tiny-case rows: rows 300..307 are the 8 decode steps' rows
+    tiny = W.config1_tiny()
+    outs = _dev()(tiny).run_all()
+    dec = [outs[t]["decode"] for t in range(1, 9)]
+    rng = np.random.default_rng(1)
+    rng.permutation(32)
+    k_all = W.bf16_normal(rng, (308, 1, 64))
+    v_all = W.bf16_normal(rng, (308, 1, 64))
+    q_all = W.bf16_normal(rng, (308, 4, 64))
+    full = W.Case("tiny_full_prefill", 4, 1, 64, 16, 32, tiny.max_blocks_per_seq, tiny.scale, [], [W.Step(
+        append=W.AppendBatch(k_all, v_all, np.array([0, 308], np.int32), np.zeros(1, np.int32),
+                             tiny.steps[0].append.block_table),
+        prefill=W.PrefillBatch(q_all, np.array([0, 308], np.int32), np.array([308], np.int32),
+                               tiny.steps[0].append.block_table))])
+    pf = _dev()(full).run_all()[0]["prefill"]
+    for t in range(8):
+        compare(dec[t][0], pf[300 + t], f"decode step {t + 1} vs prefill row {300 + t}")
+
+
+def test_chunked_equals_unchunked(orc):
+    # a 512-row chunk on 1024 cached tokens vs the same rows of a 1536-row prefill
+    rng = np.random.default_rng(4)
+    whole = W.build_case("whole_1536", rng, hq=32, hkv=8, d=128, bs=256, ctx_lens=[0], new_lens=[1536], kinds="p")
+    st = whole.steps[0]
+    chunk = W.Case("chunk_512_on_1024", 32, 8, 128, 256, whole.num_blocks, whole.max_blocks_per_seq, whole.scale,
+                   [W.AppendBatch(st.append.k_new[:1024], st.append.v_new[:1024], np.array([0, 1024], np.int32),
+                                  np.zeros(1, np.int32), st.append.block_table)],
+                   [W.Step(append=W.AppendBatch(st.append.k_new[1024:], st.append.v_new[1024:],
+                                                np.array([0, 512], np.int32), np.array([1024], np.int32),
+                                                st.append.block_table),
+                           prefill=W.PrefillBatch(st.prefill.q[1024:], np.array([0, 512], np.int32),
+                                                  np.array([1536], np.int32), st.prefill.block_table))])
+    _say("case chunked vs unchunked")
+    a = _dev()(whole).run_all()[0]["prefill"][1024:]
+    b = _dev()(chunk).run_all()[0]["prefill"]
+    compare(b, a, "chunk vs whole rows 1024..1535")
