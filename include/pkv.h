@@ -125,7 +125,8 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *   workspace        device scratch of workspace_bytes >=
  *                    pkv_decode_workspace_bytes(...) with the same shapes and
  *                    total_kv_tokens; it needs no initialisation, and calls
- *                    that share it must be ordered
+ *                    that share it must be ordered (same stream or
+ *                    synchronised)
  *
  * Long sequences are split into chunks of keys whose partial results are
  * merged with a log-sum-exp combine.  A sequence with seq_len 0 yields zeros.

@@ -6,20 +6,41 @@
 // point here, because decode is bound by HBM bandwidth ("从零搭建AI工程能力"
 // section 3.3).  The design on gfx950:
 //
-//  * Work item = (sequence, KV head, split of `chunk` keys), one wavefront
-//    each.  A persistent grid walks the items; each workgroup first derives
-//    the per-sequence split counts from seq_lens into LDS (no host sync).
-//  * Lane layout: D/8 lanes cover one key row with 16-byte loads, so a wave
-//    load reads 64/(D/8) consecutive rows of one contiguous (block, head) tile:
-//    fully coalesced, block-gathered through the table.  The K row is held in
-//    registers and used for all G query heads of the group (bf16 dot2 with
-//    fp32 accumulation), then reduced across its D/8 lanes with xor shuffles.
-//  * Online softmax in the exp2 domain (scale * log2 e folded into the scores),
-//    running max / sum per head; rows past the sequence end are excluded by a
+//  * Work item = (sequence, KV head, chunk of `chunk` keys), one workgroup of
+//    4 waves.  Each wave takes every 4th step of 64 keys of the chunk; the
+//    waves' partial softmax states are merged through LDS.  Short batches use
+//    a direct grid over (chunk, sequence, KV head) whose empty items exit at
+//    once; long, uneven batches use a persistent grid over a compact item list
+//    that each workgroup derives from seq_lens (a block scan in LDS).  Either
+//    way nothing is read back to the host, and the KV head sits in the low
+//    bits of the workgroup index, so items of one KV head run on one XCD
+//    (workgroups are dealt round-robin over the 8 XCDs) and K/V rows shared
+//    between sequences (a common prefix) are re-read from that XCD's L2.
+//  * Within a step all K and V loads are issued before any is used: D/8 lanes
+//    cover one row with 16-byte loads, a wave load reads 64/(D/8) consecutive
+//    rows of one contiguous (block, head) tile, and D/8 such loads cover the 64
+//    keys -- 32 KB in flight per wave.  Each K row, once in registers, serves
+//    all G query heads of the group.
+//  * Scores: each lane dots its 8 dims of each of its keys with the G query
+//    heads (bf16 dot2, fp32 accumulate).  The D/8 partial sums are folded
+//    across the row's lanes with DPP moves in a transposing order: at every
+//    fold a lane keeps half of its values and adds its partner's copy of that
+//    half, so after log2(D/8) folds each lane holds the complete G scores of
+//    exactly one key.  The softmax then costs G exponentials per lane.
+//  * Online softmax in the exp2 domain (scale * log2 e folded in); the step
+//    max is a wave reduction; rows past the sequence end are excluded by a
 //    select, never multiplied by zero (unwritten slots may hold NaN).
-//  * Splits of a sequence write a normalised partial and its log-sum-exp; a
-//    second kernel merges them (out = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M)).
-//    A sequence with a single split is written directly.
+//  * P V: each lane needs the weights of the keys whose V rows it holds; they
+//    are broadcast inside each group of D/8 lanes (DPP row broadcast or an LDS
+//    swizzle) and accumulated into G x 8 fp32 outputs per lane.
+//  * Chunks of a sequence write a normalised partial and its log2-sum-exp; a
+//    second kernel merges them in one pass with a running maximum
+//    (out = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M)).  The hand-off goes
+//    through a kernel boundary on purpose: the L2 is per XCD, so a device-scope
+//    fence inside the kernel would write back and invalidate an XCD's whole
+//    L2 under every other workgroup's streaming loads.  A sequence with one
+//    chunk is written directly (and the merge kernel is not launched when no
+//    sequence can have two); a sequence with no keys gets zeros.
 #include <math.h>
 
 #include "pkv_device.h"
@@ -28,36 +49,37 @@
 namespace pkv {
 namespace {
 
-constexpr int kDecodeThreads = 256;  // 4 waves, each an independent work item
-constexpr int kDecodeLoads = 4;      // wave-wide row loads per K (and V) per iteration
-constexpr int kTargetItems = 8192;   // aim for about this many (split, KV head) items
+constexpr int kDecodeThreads = 256;  // 4 waves share one work item
+constexpr int kDecodeWaves = kDecodeThreads / kWave;
+constexpr int kStepKeys = 64;        // keys whose K/V loads are in flight together
+constexpr int kXcds = 8;
 
 struct DecodeKernelArgs {
     DecodeArgs a;
-    int32_t chunk;
+    int32_t chunk;       // keys per work item (multiple of 4 * 64)
     int32_t log2_block;
+    int32_t max_chunks;  // chunks of the longest sequence
+    int32_t persistent;  // 1: persistent grid over the compact item list
     int64_t max_partials;
-    int32_t* prefix;  // [num_seqs + 1]
-    float* lse;       // [max_partials][Hq]
-    float* part;      // [max_partials][Hq][D]
+    float* lse;         // [max_partials][Hq]
+    float* part;        // [max_partials][Hq][D]
     float qk_scale_log2;
 };
 
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
-__device__ __forceinline__ int num_splits(int L, int chunk) { return L > 0 ? (L + chunk - 1) / chunk : 0; }
+__device__ __forceinline__ int num_chunks(int L, int chunk) { return L > 0 ? (L + chunk - 1) / chunk : 0; }
 
-// Exclusive prefix of split counts over all sequences into s_prefix[0..S];
-// every thread of the (256-thread) block takes part.
-__device__ void split_prefix(const DecodeKernelArgs& p, int32_t* s_prefix, int32_t* s_wave) {
+// Exclusive prefix of chunk counts over all sequences into s_prefix[0..S];
+// every thread of the block takes part.
+__device__ void chunk_prefix(const DecodeKernelArgs& p, int32_t* s_prefix, int32_t* s_wave) {
     const int S = p.a.num_seqs;
     const int cap = p.a.max_blocks_per_seq << p.log2_block;
     const int tid = threadIdx.x;
     const int per = (S + kDecodeThreads - 1) / kDecodeThreads;
     const int lo = min(S, tid * per), hi = min(S, lo + per);
     int sum = 0;
-    for (int i = lo; i < hi; ++i) sum += num_splits(clamp_len(p.a.seq_lens[i], cap), p.chunk);
-    // inclusive scan: within the wave, then across the 4 waves
+    for (int i = lo; i < hi; ++i) sum += num_chunks(clamp_len(p.a.seq_lens[i], cap), p.chunk);
     const int lane = tid & 63, wave = tid >> 6;
     int incl = sum;
 #pragma unroll
@@ -73,31 +95,226 @@ __device__ void split_prefix(const DecodeKernelArgs& p, int32_t* s_prefix, int32
     int run = incl - sum;
     for (int i = lo; i < hi; ++i) {
         s_prefix[i] = run;
-        run += num_splits(clamp_len(p.a.seq_lens[i], cap), p.chunk);
+        run += num_chunks(clamp_len(p.a.seq_lens[i], cap), p.chunk);
     }
     if (tid == kDecodeThreads - 1) s_prefix[S] = incl;
     __syncthreads();
 }
 
+// One fold of the transposing reduction over the lanes of a key row: lanes
+// whose `upper` bit is set keep the upper half of v[0..N) and the others the
+// lower half; each adds its partner's copy of the half it keeps.  kCtrl must
+// pair every lane with one whose `upper` bit differs and whose bits above it
+// agree.
+template <int N, int kCtrl>
+__device__ __forceinline__ void fold(float* v, bool upper) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+        const float keep = upper ? v[N / 2 + i] : v[i];
+        const float send = upper ? v[i] : v[N / 2 + i];
+        v[i] = keep + dpp<kCtrl>(send);
+    }
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp<kDppXor1>(x));
+    x = fmaxf(x, dpp<kDppXor2>(x));
+    x = fmaxf(x, dpp<kDppHalfMirror>(x));
+    x = fmaxf(x, dpp<kDppMirror>(x));
+    x = fmaxf(x, __shfl_xor(x, 16, kWave));
+    return fmaxf(x, __shfl_xor(x, 32, kWave));
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp<kDppXor1>(x);
+    x += dpp<kDppXor2>(x);
+    x += dpp<kDppHalfMirror>(x);
+    x += dpp<kDppMirror>(x);
+    x += __shfl_xor(x, 16, kWave);
+    return x + __shfl_xor(x, 32, kWave);
+}
+
+// Broadcast lane u of each group of kLanes lanes (16: DPP row broadcast;
+// 8: LDS swizzle in broadcast mode).
+template <int kLanes, int u>
+__device__ __forceinline__ float group_bcast(float x) {
+    if constexpr (kLanes == 16) {
+        return dpp<kDppRowBcast0 + u>(x);
+    } else {
+        static_assert(kLanes == 8, "groups of 8 or 16 lanes");
+        return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x18 | (u << 5)));
+    }
+}
+
+template <int kLanes, int G, int u>
+__device__ __forceinline__ void pv_accumulate(float (&o)[G][8], const float (&pk)[G], const u32x4& v) {
+    float pu[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) pu[h] = group_bcast<kLanes, u>(pk[h]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float vi = (i & 1) ? bf16_hi(v[i >> 1]) : bf16_lo(v[i >> 1]);
+#pragma unroll
+        for (int h = 0; h < G; ++h) o[h][i] += pu[h] * vi;
+    }
+}
+
+template <int kLanes, int G, int u>
+struct PvAll {
+    static __device__ __forceinline__ void run(float (&o)[G][8], const float (&pk)[G], const u32x4* vr) {
+        PvAll<kLanes, G, u - 1>::run(o, pk, vr);
+        pv_accumulate<kLanes, G, u - 1>(o, pk, vr[u - 1]);
+    }
+};
+template <int kLanes, int G>
+struct PvAll<kLanes, G, 0> {
+    static __device__ __forceinline__ void run(float (&)[G][8], const float (&)[G], const u32x4*) {}
+};
+
+// LDS of one workgroup: the waves' softmax states, then the item's merge.
 template <int D, int G>
-__device__ __forceinline__ void decode_item(const DecodeKernelArgs& p, int s, int g, int c, int nsplit,
-                                            int64_t pidx, int lane) {
-    constexpr int kLanesPerKey = D / 8;
-    constexpr int kKeysPerLoad = kWave / kLanesPerKey;
-    constexpr int kKeysPerIter = kDecodeLoads * kKeysPerLoad;
+struct DecodeShared {
+    float o[kDecodeWaves][G][D];
+    float m[kDecodeWaves][G];
+    float l[kDecodeWaves][G];
+    int32_t wave_sum[kDecodeWaves];
+};
+
+// Steps base = k_begin + wave*64, + 4*64, ... below k_end of sequence s, KV
+// head g; leaves per-lane running max m (wave-uniform), sum l (per key lane)
+// and o (per row of a wave load).
+template <int D, int G>
+__device__ __forceinline__ void wave_steps(const DecodeKernelArgs& p, int s, int g, int k_begin, int k_end,
+                                           int lane, int wave, float (&m)[G], float (&l)[G], float (&o)[G][8]) {
+    constexpr int kLanesPerKey = D / 8;                 // lanes per key row (16 B each)
+    constexpr int kKeysPerLoad = kWave / kLanesPerKey;  // rows per wave load
+    constexpr int kLoads = kStepKeys / kKeysPerLoad;    // wave loads per step (= kLanesPerKey)
+    static_assert(kLoads == kLanesPerKey, "one key per lane after the fold");
     const DecodeArgs& a = p.a;
-    const int kq = lane / kLanesPerKey;  // which row of a wave load
-    const int dl = lane % kLanesPerKey;  // which 8 dims of that row
+    const int kq = lane / kLanesPerKey;
+    const int dl = lane % kLanesPerKey;
     const int B = 1 << p.log2_block;
-    const int L = clamp_len(a.seq_lens[s], a.max_blocks_per_seq << p.log2_block);
-    const int k0 = c * p.chunk;
-    const int k1 = min(k0 + p.chunk, L);
     const int Hq = a.num_q_heads;
-    const int64_t head_stride = (int64_t)B * D;  // elements of one (block, head) tile
+    const int64_t tile = (int64_t)B * D;  // elements of one (block, head) tile
+    const int32_t* table = a.block_table + (int64_t)s * a.max_blocks_per_seq;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
 
     u32x4 qv[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) qv[h] = load16(a.q + ((int64_t)s * Hq + g * G + h) * D + dl * 8);
+
+    for (int base = k_begin + wave * kStepKeys; base < k_end; base += kDecodeWaves * kStepKeys) {
+        // ---- issue every K and V load of the step
+        u32x4 kr[kLoads], vr[kLoads];
+        const int blk_step = table[base >> p.log2_block];  // the whole step when B >= 64
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+            const int j = base + u * kKeysPerLoad + kq;
+            int blk = B >= kStepKeys ? blk_step : (j < k_end ? table[j >> p.log2_block] : -1);
+            const bool ok = j < k_end && (unsigned)blk < (unsigned)a.num_blocks;
+            blk = ok ? blk : 0;  // masked lanes keep an in-bounds address
+            const int64_t off = ((int64_t)blk * a.num_kv_heads + g) * tile + (int64_t)(j & (B - 1)) * D + dl * 8;
+            kr[u] = ok ? load16(a.k_pool + off) : zero;
+            vr[u] = ok ? load16(a.v_pool + off) : zero;
+        }
+        // ---- partial dots: sc[u * G + h] over this lane's 8 dims
+        float sc[kLoads * G];
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u)
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float acc = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = dot2_bf16(qv[h][i], kr[u][i], acc);
+                sc[u * G + h] = acc;
+            }
+        // ---- transposing fold: afterwards sc[0..G) are the scores of key u = dl
+        if constexpr (kLanesPerKey == 16) {
+            fold<16 * G, kDppMirror>(sc, dl & 8);
+            fold<8 * G, kDppHalfMirror>(sc, dl & 4);
+            fold<4 * G, kDppXor2>(sc, dl & 2);
+            fold<2 * G, kDppXor1>(sc, dl & 1);
+        } else {
+            fold<8 * G, kDppHalfMirror>(sc, dl & 4);
+            fold<4 * G, kDppXor2>(sc, dl & 2);
+            fold<2 * G, kDppXor1>(sc, dl & 1);
+        }
+        const int key = base + dl * kKeysPerLoad + kq;
+        bool valid = key < k_end;
+        if (valid) valid = (unsigned)(B >= kStepKeys ? blk_step : table[key >> p.log2_block]) < (unsigned)a.num_blocks;
+        // ---- online softmax (exp2 domain); one key per lane
+        float pk[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float z = valid ? sc[h] * p.qk_scale_log2 : -INFINITY;
+            const float m_new = fmaxf(m[h], wave_max(z));
+            const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m[h] - m_new);
+            pk[h] = valid ? fast_exp2(z - m_new) : 0.f;
+            l[h] = l[h] * alpha + pk[h];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[h][i] *= alpha;
+            m[h] = m_new;
+        }
+        // ---- P V over the step's keys
+        PvAll<kLanesPerKey, G, kLoads>::run(o, pk, vr);
+    }
+}
+
+// Merge kernel: one workgroup per (sequence, KV head) merges that sequence's
+// chunk partials into the bf16 output, one pass with a running maximum so all
+// loads are independent.  Sequences with fewer than two chunks were finished
+// by the split kernel.
+template <int D, int G>
+constexpr int elems_per_thread() { return (G * D + kDecodeThreads - 1) / kDecodeThreads; }
+
+template <int D, int G>
+__global__ __launch_bounds__(kDecodeThreads) void decode_merge_kernel(DecodeKernelArgs p, const int32_t* prefix) {
+    constexpr int kElems = elems_per_thread<D, G>();  // outputs per thread
+    const int Hkv = p.a.num_kv_heads, Hq = p.a.num_q_heads;
+    const int g = blockIdx.x % Hkv, s = blockIdx.x / Hkv;
+    const int cap = p.a.max_blocks_per_seq << p.log2_block;
+    const int n = num_chunks(clamp_len(p.a.seq_lens[s], cap), p.chunk);
+    if (n < 2) return;
+    const int64_t base = p.persistent ? (int64_t)prefix[s] : (int64_t)s * p.max_chunks;
+    if (base + n > p.max_partials) return;  // precondition broken: no partials to merge
+    const int e0 = threadIdx.x * kElems;
+    if (e0 >= G * D) return;
+    const int h = e0 / D, d0 = e0 % D;
+    const int qh = g * G + h;
+    float mx = -INFINITY, den = 0.f, num[kElems];
+#pragma unroll
+    for (int k = 0; k < kElems; ++k) num[k] = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < n; ++i) {
+        const float li = p.lse[(base + i) * Hq + qh];
+        const float* src = p.part + ((base + i) * Hq + qh) * D + d0;
+        const float m_new = fmaxf(mx, li);
+        const float a_old = fast_exp2(mx - m_new);  // 0 on the first partial
+        const float w = fast_exp2(li - m_new);
+        den = den * a_old + w;
+#pragma unroll
+        for (int k = 0; k < kElems; ++k) num[k] = num[k] * a_old + w * src[k];
+        mx = m_new;
+    }
+    const float inv = 1.f / den;
+    uint16_t* dst = p.a.out + ((int64_t)s * Hq + qh) * D + d0;
+#pragma unroll
+    for (int k = 0; k < kElems; ++k) dst[k] = __builtin_bit_cast(uint16_t, (__bf16)(num[k] * inv));
+}
+
+// One work item: chunk c of sequence s, KV head g; `slot` is its partial slot
+// and `base` the slot of the sequence's first chunk.
+template <int D, int G>
+__device__ void decode_item(const DecodeKernelArgs& p, DecodeShared<D, G>& sh, int s, int g, int c, int nchunks,
+                            int64_t slot) {
+    constexpr int kLanesPerKey = D / 8;
+    const DecodeArgs& a = p.a;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kq = lane / kLanesPerKey, dl = lane % kLanesPerKey;
+    const int L = clamp_len(a.seq_lens[s], a.max_blocks_per_seq << p.log2_block);
+    const int k0 = c * p.chunk;
+    const int k1 = min(k0 + p.chunk, L);
+    const int Hq = a.num_q_heads;
 
     float m[G], l[G], o[G][8];
 #pragma unroll
@@ -107,175 +324,146 @@ __device__ __forceinline__ void decode_item(const DecodeKernelArgs& p, int s, in
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[h][i] = 0.f;
     }
-    const int32_t* table = a.block_table + (int64_t)s * a.max_blocks_per_seq;
+    wave_steps<D, G>(p, s, g, k0, k1, lane, wave, m, l, o);
 
-    for (int base = k0; base < k1; base += kKeysPerIter) {
-        u32x4 kr[kDecodeLoads], vr[kDecodeLoads];
-        bool valid[kDecodeLoads];
-#pragma unroll
-        for (int u = 0; u < kDecodeLoads; ++u) {
-            const int j = base + u * kKeysPerLoad + kq;
-            int blk = j < k1 ? table[j >> p.log2_block] : -1;
-            valid[u] = (unsigned)blk < (unsigned)a.num_blocks;
-            blk = valid[u] ? blk : 0;  // masked lanes keep an in-bounds address
-            const int64_t off = ((int64_t)blk * a.num_kv_heads + g) * head_stride + (int64_t)(j & (B - 1)) * D + dl * 8;
-            const u32x4 zero = {0u, 0u, 0u, 0u};
-            kr[u] = valid[u] ? load16(a.k_pool + off) : zero;
-            vr[u] = valid[u] ? load16(a.v_pool + off) : zero;
-        }
-        float sc[kDecodeLoads][G];
-#pragma unroll
-        for (int u = 0; u < kDecodeLoads; ++u)
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float acc = 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc = dot2_bf16(qv[h][i], kr[u][i], acc);
-                sc[u][h] = group_sum<kLanesPerKey>(acc);
-            }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float mt = -INFINITY;
-#pragma unroll
-            for (int u = 0; u < kDecodeLoads; ++u) {
-                sc[u][h] = valid[u] ? sc[u][h] * p.qk_scale_log2 : -INFINITY;
-                mt = fmaxf(mt, sc[u][h]);
-            }
-#pragma unroll
-            for (int off = kLanesPerKey; off < kWave; off <<= 1) mt = fmaxf(mt, __shfl_xor(mt, off, kWave));
-            const float m_new = fmaxf(m[h], mt);
-            const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m[h] - m_new);
-            float pu[kDecodeLoads];
-            float psum = 0.f;
-#pragma unroll
-            for (int u = 0; u < kDecodeLoads; ++u) {
-                pu[u] = valid[u] ? fast_exp2(sc[u][h] - m_new) : 0.f;
-                psum += pu[u];
-            }
-            l[h] = l[h] * alpha + psum;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float acc = o[h][i] * alpha;
-#pragma unroll
-                for (int u = 0; u < kDecodeLoads; ++u) {
-                    const uint32_t w = vr[u][i >> 1];
-                    acc += pu[u] * ((i & 1) ? bf16_hi(w) : bf16_lo(w));
-                }
-                o[h][i] = acc;
-            }
-            m[h] = m_new;
-        }
-    }
-
-    // sum the per-row partials over the rows of a wave load (same max everywhere)
+    // ---- wave totals: l over every key lane, o over the rows of a wave load
 #pragma unroll
     for (int h = 0; h < G; ++h) {
+        l[h] = wave_sum(l[h]);
 #pragma unroll
-        for (int off = kLanesPerKey; off < kWave; off <<= 1) {
-            l[h] += __shfl_xor(l[h], off, kWave);
+        for (int off = kLanesPerKey; off < kWave; off <<= 1)
 #pragma unroll
             for (int i = 0; i < 8; ++i) o[h][i] += __shfl_xor(o[h][i], off, kWave);
-        }
     }
-    if (kq != 0) return;
+    if (kq == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const int qh = g * G + h;
-        const float inv = 1.f / l[h];
-        if (nsplit == 1) {
-            u32x4 packed;
+        for (int h = 0; h < G; ++h) {
+            *reinterpret_cast<f32x4*>(&sh.o[wave][h][dl * 8]) = f32x4{o[h][0], o[h][1], o[h][2], o[h][3]};
+            *reinterpret_cast<f32x4*>(&sh.o[wave][h][dl * 8 + 4]) = f32x4{o[h][4], o[h][5], o[h][6], o[h][7]};
+        }
+    }
+    if (lane == 0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) packed[i] = pack_bf16x2(o[h][2 * i] * inv, o[h][2 * i + 1] * inv);
-            store16(a.out + ((int64_t)s * Hq + qh) * D + dl * 8, packed);
-        } else if (pidx < p.max_partials) {
-            float* dst = p.part + (pidx * Hq + qh) * D + dl * 8;
-            f32x4 lo4 = {o[h][0] * inv, o[h][1] * inv, o[h][2] * inv, o[h][3] * inv};
-            f32x4 hi4 = {o[h][4] * inv, o[h][5] * inv, o[h][6] * inv, o[h][7] * inv};
-            *reinterpret_cast<f32x4*>(dst) = lo4;
-            *reinterpret_cast<f32x4*>(dst + 4) = hi4;
-            if (dl == 0) p.lse[pidx * Hq + qh] = m[h] + log2f(l[h]);
+        for (int h = 0; h < G; ++h) {
+            sh.m[wave][h] = m[h];
+            sh.l[wave][h] = l[h];
         }
     }
-}
+    __syncthreads();
 
-template <int D, int G>
-__global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(DecodeKernelArgs p) {
-    extern __shared__ int32_t s_prefix[];  // num_seqs + 1
-    __shared__ int32_t s_wave[kDecodeThreads / kWave];
-    split_prefix(p, s_prefix, s_wave);
-    const int S = p.a.num_seqs;
-    if (blockIdx.x == 0)
-        for (int i = threadIdx.x; i <= S; i += kDecodeThreads) p.prefix[i] = s_prefix[i];
-
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int Hkv = p.a.num_kv_heads;
-    const int64_t total_items = (int64_t)s_prefix[S] * Hkv;
-    const int64_t stride = (int64_t)gridDim.x * (kDecodeThreads / kWave);
-    for (int64_t item = (int64_t)blockIdx.x * (kDecodeThreads / kWave) + wave; item < total_items; item += stride) {
-        const int split = (int)(item / Hkv);
-        const int g = (int)(item - (int64_t)split * Hkv);
-        // the sequence owning this split: last s with s_prefix[s] <= split
-        int lo = 0, hi = S - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_prefix[mid] <= split) lo = mid; else hi = mid - 1;
-        }
-        const int nsplit = s_prefix[lo + 1] - s_prefix[lo];
-        decode_item<D, G>(p, lo, g, split - s_prefix[lo], nsplit, split, lane);
+    // ---- merge the 4 waves: thread -> kElems consecutive outputs of one head
+    constexpr int kElems = elems_per_thread<D, G>();
+    const int e0 = threadIdx.x * kElems;
+    const bool active = e0 < G * D;  // fewer outputs than threads when G * D < 256
+    const int h = active ? e0 / D : 0, d0 = active ? e0 % D : 0;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) mx = fmaxf(mx, sh.m[w][h]);
+    float den = 0.f, val[kElems];
+#pragma unroll
+    for (int k = 0; k < kElems; ++k) val[k] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+        const float sc = sh.m[w][h] == -INFINITY ? 0.f : fast_exp2(sh.m[w][h] - mx);  // a wave without keys adds 0
+        den += sh.l[w][h] * sc;
+#pragma unroll
+        for (int k = 0; k < kElems; ++k) val[k] += sh.o[w][h][d0 + k] * sc;
     }
-}
-
-// One thread per (sequence, query head, dim): merge the splits of a sequence.
-template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeKernelArgs p) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int Hq = p.a.num_q_heads;
-    const int d = (int)(idx % D);
-    const int64_t sh = idx / D;
-    const int h = (int)(sh % Hq);
-    const int s = (int)(sh / Hq);
-    if (s >= p.a.num_seqs) return;
-    const int base = p.prefix[s];
-    const int n = p.prefix[s + 1] - base;
-    uint16_t* dst = p.a.out + ((int64_t)s * Hq + h) * D + d;
-    if (n == 0) {  // no keys at all: the row is zero
-        *dst = 0;
+    const int qh = g * G + h;
+    const float inv = 1.f / den;
+    if (nchunks == 1) {
+        uint16_t* dst = a.out + ((int64_t)s * Hq + qh) * D + d0;
+        if (active)
+#pragma unroll
+            for (int k = 0; k < kElems; ++k) dst[k] = __builtin_bit_cast(uint16_t, (__bf16)(val[k] * inv));
+        __syncthreads();  // LDS is reused by the next item
         return;
     }
-    if (n == 1 || (int64_t)base + n > p.max_partials) return;
-    float mx = -INFINITY;
-    for (int i = 0; i < n; ++i) mx = fmaxf(mx, p.lse[(int64_t)(base + i) * Hq + h]);
-    float num = 0.f, den = 0.f;
-    for (int i = 0; i < n; ++i) {
-        const float w = fast_exp2(p.lse[(int64_t)(base + i) * Hq + h] - mx);
-        den += w;
-        num += w * p.part[((int64_t)(base + i) * Hq + h) * D + d];
+    if (active && slot < p.max_partials) {
+        float* dst = p.part + (slot * Hq + qh) * D + d0;
+#pragma unroll
+        for (int k = 0; k < kElems; ++k) dst[k] = val[k] * inv;
+        if (d0 == 0) p.lse[slot * Hq + qh] = mx + log2f(den);
     }
-    const __bf16 r = (__bf16)(num / den);
-    *dst = __builtin_bit_cast(uint16_t, r);
+    __syncthreads();  // LDS is reused by the next item
 }
 
 template <int D, int G>
-hipError_t launch_typed(const DecodeKernelArgs& kp, hipStream_t stream) {
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeKernelArgs p, int32_t* prefix_out) {
+    __shared__ DecodeShared<D, G> sh;
+    const int S = p.a.num_seqs;
+    const int Hq = p.a.num_q_heads;
+    const int Hkv = p.a.num_kv_heads;
+    const int cap = p.a.max_blocks_per_seq << p.log2_block;
+
+    if (!p.persistent) {
+        // direct grid: workgroup -> (chunk, sequence, KV head), KV head fastest
+        int idx = blockIdx.x;
+        const int g = idx % Hkv;
+        idx /= Hkv;
+        const int s = idx % S;
+        const int c = idx / S;
+        const int L = clamp_len(p.a.seq_lens[s], cap);
+        const int n = num_chunks(L, p.chunk);
+        if (L == 0 && c == 0)  // a sequence without keys: zero rows
+            for (int e = threadIdx.x; e < G * D; e += kDecodeThreads) p.a.out[((int64_t)s * Hq + g * G) * D + e] = 0;
+        if (c >= n) return;
+        decode_item<D, G>(p, sh, s, g, c, n, (int64_t)s * p.max_chunks + c);
+        return;
+    }
+
+    extern __shared__ int32_t s_prefix[];  // num_seqs + 1
+    chunk_prefix(p, s_prefix, sh.wave_sum);
+    if (blockIdx.x == 0) {  // the merge kernel's view of the list; sequences without keys: zero rows
+        for (int i = threadIdx.x; i <= S; i += kDecodeThreads) prefix_out[i] = s_prefix[i];
+        const int pieces = Hq * D / 8;
+        for (int64_t e = threadIdx.x; e < (int64_t)S * pieces; e += kDecodeThreads) {
+            const int s = (int)(e / pieces);
+            if (s_prefix[s + 1] == s_prefix[s]) store16(p.a.out + e * 8, u32x4{0u, 0u, 0u, 0u});
+        }
+    }
+    // item i = (chunk i / Hkv of the compact list, KV head i % Hkv); the grid is
+    // a multiple of 8 workgroups, so a workgroup only meets KV heads congruent
+    // to its XCD modulo 8
+    const int64_t total_items = (int64_t)s_prefix[S] * Hkv;
+    for (int64_t item = blockIdx.x; item < total_items; item += gridDim.x) {
+        const int chunk = (int)(item / Hkv);
+        const int g = (int)(item - (int64_t)chunk * Hkv);
+        int lo = 0, hi = S - 1;  // the sequence owning this chunk: last s with s_prefix[s] <= chunk
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_prefix[mid] <= chunk) lo = mid; else hi = mid - 1;
+        }
+        const int n = s_prefix[lo + 1] - s_prefix[lo];
+        decode_item<D, G>(p, sh, lo, g, chunk - s_prefix[lo], n, chunk);
+    }
+}
+
+template <int D, int G>
+hipError_t launch_typed(const DecodeKernelArgs& kp, int32_t* prefix, hipStream_t stream) {
     const DecodeArgs& a = kp.a;
-    const size_t lds = sizeof(int32_t) * (size_t)(a.num_seqs + 1);
-    // persistent grid: as many workgroups as can be resident, but no more than the work
-    int per_cu = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, G>, kDecodeThreads, lds);
-    if (e != hipSuccess) return e;
-    if (per_cu < 1) per_cu = 1;
-    const int64_t max_splits = (int64_t)a.num_seqs * ((a.max_seq_len + kp.chunk - 1) / kp.chunk);
-    const int64_t items = (max_splits < kp.max_partials ? max_splits : kp.max_partials) * a.num_kv_heads;
-    int64_t blocks = (items + 3) / 4;
-    const int64_t resident = (int64_t)per_cu * device_cu_count();
-    if (blocks > resident) blocks = resident;
-    if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3((unsigned)blocks), dim3(kDecodeThreads), lds, stream, kp);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t threads = (int64_t)a.num_seqs * a.num_q_heads * D;
-    hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, kp);
+    if (!kp.persistent) {
+        const int64_t blocks = (int64_t)kp.max_chunks * a.num_seqs * a.num_kv_heads;
+        hipLaunchKernelGGL((decode_kernel<D, G>), dim3((unsigned)blocks), dim3(kDecodeThreads), 0, stream, kp, prefix);
+    } else {
+        const size_t lds = sizeof(int32_t) * (size_t)(a.num_seqs + 1);
+        int per_cu = 0;
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, G>, kDecodeThreads, lds);
+        if (e != hipSuccess) return e;
+        if (per_cu < 1) per_cu = 1;
+        const int64_t direct = (int64_t)a.num_seqs * kp.max_chunks;
+        const int64_t items = (kp.max_partials < direct ? kp.max_partials : direct) * a.num_kv_heads;
+        int64_t blocks = (items + kXcds - 1) / kXcds * kXcds;
+        int64_t resident = (int64_t)per_cu * device_cu_count() / kXcds * kXcds;
+        if (resident < kXcds) resident = kXcds;
+        if (blocks > resident) blocks = resident;
+        hipLaunchKernelGGL((decode_kernel<D, G>), dim3((unsigned)blocks), dim3(kDecodeThreads), lds, stream, kp,
+                           prefix);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || kp.max_chunks < 2) return e;  // no sequence has two chunks: nothing to merge
+    hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3((unsigned)(a.num_seqs * a.num_kv_heads)),
+                       dim3(kDecodeThreads), 0, stream, kp, (const int32_t*)prefix);
     return hipGetLastError();
 }
 
@@ -293,13 +481,17 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
     const int64_t bound_tokens = (int64_t)num_seqs * max_seq_len;
     int64_t total = total_kv_tokens > 0 ? total_kv_tokens : bound_tokens;
     if (total > bound_tokens) total = bound_tokens;
+    // chunk: about 4 workgroups per CU-slot's worth of work, 256..8192 keys
     const int64_t key_heads = total * num_kv_heads;
-    int chunk = 64;
-    while (chunk < 2048 && (int64_t)chunk * 2 * kTargetItems <= key_heads) chunk *= 2;
+    int chunk = kDecodeWaves * kStepKeys;
+    while (chunk < 8192 && (int64_t)chunk * 2 * 4096 <= key_heads) chunk *= 2;
     pl.chunk = chunk;
-    const int64_t by_len = (int64_t)num_seqs * ((max_seq_len + chunk - 1) / chunk);
-    const int64_t by_total = (total + chunk - 1) / chunk + num_seqs;
-    pl.max_partials = by_len < by_total ? by_len : by_total;
+    pl.max_chunks = (max_seq_len + chunk - 1) / chunk;
+    const int64_t direct_items = (int64_t)num_seqs * pl.max_chunks;
+    const int64_t real_items = (total + chunk - 1) / chunk + num_seqs;  // bound on chunks actually present
+    // a direct grid when its empty workgroups are few (or the launch is small)
+    pl.persistent = (direct_items > 2 * real_items && direct_items * num_kv_heads > 4096) ? 1 : 0;
+    pl.max_partials = pl.persistent ? (direct_items < real_items ? direct_items : real_items) : direct_items;
     auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
     pl.prefix_offset = 0;
     pl.lse_offset = align(sizeof(int32_t) * (size_t)(num_seqs + 1));
@@ -314,26 +506,28 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     kp.a = a;
     kp.chunk = pl.chunk;
     kp.log2_block = ilog2(a.block_size);
+    kp.max_chunks = pl.max_chunks;
+    kp.persistent = pl.persistent;
     kp.max_partials = pl.max_partials;
     char* ws = static_cast<char*>(a.workspace);
-    kp.prefix = reinterpret_cast<int32_t*>(ws + pl.prefix_offset);
+    int32_t* prefix = reinterpret_cast<int32_t*>(ws + pl.prefix_offset);
     kp.lse = reinterpret_cast<float*>(ws + pl.lse_offset);
     kp.part = reinterpret_cast<float*>(ws + pl.o_offset);
     kp.qk_scale_log2 = a.scale * kLog2e;
     const int G = a.num_q_heads / a.num_kv_heads;
     if (a.head_dim == 128) {
         switch (G) {
-            case 1: return launch_typed<128, 1>(kp, stream);
-            case 2: return launch_typed<128, 2>(kp, stream);
-            case 4: return launch_typed<128, 4>(kp, stream);
-            default: return launch_typed<128, 8>(kp, stream);
+            case 1: return launch_typed<128, 1>(kp, prefix, stream);
+            case 2: return launch_typed<128, 2>(kp, prefix, stream);
+            case 4: return launch_typed<128, 4>(kp, prefix, stream);
+            default: return launch_typed<128, 8>(kp, prefix, stream);
         }
     }
     switch (G) {
-        case 1: return launch_typed<64, 1>(kp, stream);
-        case 2: return launch_typed<64, 2>(kp, stream);
-        case 4: return launch_typed<64, 4>(kp, stream);
-        default: return launch_typed<64, 8>(kp, stream);
+        case 1: return launch_typed<64, 1>(kp, prefix, stream);
+        case 2: return launch_typed<64, 2>(kp, prefix, stream);
+        case 4: return launch_typed<64, 4>(kp, prefix, stream);
+        default: return launch_typed<64, 8>(kp, prefix, stream);
     }
 }
 

@@ -14,10 +14,14 @@ namespace {
 
 constexpr int kAppendThreads = 256;
 
-// Sequence owning packed row t: the last s with cu[s] <= t (binary search over
-// the num_seqs + 1 prefix; every lane of a wave searches for nearby rows, so
-// the probes are mostly the same addresses and hit in cache).
-__device__ __forceinline__ int owner_seq(const int32_t* __restrict__ cu, int num_seqs, int t) {
+// Sequence owning packed row t: the last s with cu[s] <= t.  The first guess
+// assumes equal row counts per sequence (exact for a decode step or equal
+// chunks) and costs one round trip; otherwise a binary search over the
+// num_seqs + 1 prefix follows (lanes of a wave search for nearby rows, so the
+// probes mostly share addresses and hit in cache).
+__device__ __forceinline__ int owner_seq(const int32_t* __restrict__ cu, int num_seqs, int total, int t) {
+    const int guess = (int)((int64_t)t * num_seqs / total);
+    if (cu[guess] <= t && (guess + 1 == num_seqs || cu[guess + 1] > t)) return guess;
     int lo = 0, hi = num_seqs - 1;
     while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
@@ -37,18 +41,19 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendArgs a)
     const int g = (int)(row_head % a.num_kv_heads);
     const int t = (int)(row_head / a.num_kv_heads);
 
-    const int s = owner_seq(a.cu_new_lens, a.num_seqs, t);
+    // the row's data does not depend on where it goes: load it first
+    const int64_t src = ((int64_t)t * a.num_kv_heads + g) * D + piece * 8;
+    const u32x4 kv = load16(a.k_new + src);
+    const u32x4 vv = load16(a.v_new + src);
+
+    const int s = owner_seq(a.cu_new_lens, a.num_seqs, a.total_new_tokens, t);
     const int64_t pos = (int64_t)a.ctx_lens[s] + (t - a.cu_new_lens[s]);
     const int64_t lblock = pos / a.block_size;
     if (pos < 0 || lblock >= a.max_blocks_per_seq) return;  // precondition broken: skip
     const int blk = a.block_table[(int64_t)s * a.max_blocks_per_seq + lblock];
     if (blk < 0 || blk >= a.num_blocks) return;
     const int slot = (int)(pos & (a.block_size - 1));
-
-    const int64_t src = ((int64_t)t * a.num_kv_heads + g) * D + piece * 8;
     const int64_t dst = (((int64_t)blk * a.num_kv_heads + g) * a.block_size + slot) * D + piece * 8;
-    const u32x4 kv = load16(a.k_new + src);
-    const u32x4 vv = load16(a.v_new + src);
     store16(a.k_pool + dst, kv);
     store16(a.v_pool + dst, vv);
 }

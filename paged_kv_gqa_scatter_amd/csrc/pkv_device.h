@@ -37,6 +37,22 @@ __device__ __forceinline__ void store16(uint16_t* p, u32x4 v) { *reinterpret_cas
 // 2^x (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// DPP lane moves inside a row of 16 lanes (v_mov_b32_dpp).  Each control is
+// a permutation of the row: quad xor 1, quad xor 2, xor 7 within 8 lanes
+// (half-row mirror), xor 15 within 16 (row mirror), and broadcast of lane n.
+enum : int {
+    kDppXor1 = 0xB1,       // quad_perm [1,0,3,2]
+    kDppXor2 = 0x4E,       // quad_perm [2,3,0,1]
+    kDppHalfMirror = 0x141,
+    kDppMirror = 0x140,
+    kDppRowBcast0 = 0x150  // + n: row_newbcast:n
+};
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+
 // Lane-crossing reductions over groups of lanes.  `width` lanes with
 // consecutive ids form a group; the xor partner stays inside the group.
 template <int kWidth>

@@ -70,9 +70,12 @@ struct PrefillArgs {
 // Decode split plan: keys per split and workspace layout, a pure function of
 // host-known shapes so that the size query and the launch always agree.
 struct DecodePlan {
-    int32_t chunk;            // keys per split (multiple of 64)
+    int32_t chunk;            // keys per work item (multiple of 256)
+    int32_t max_chunks;       // chunks of the longest sequence
+    int32_t persistent;       // 1: persistent grid over a compact item list
+
     int64_t max_partials;     // (sequence, split) slots the workspace holds
-    size_t prefix_offset;     // int32 [num_seqs + 1] split prefix
+    size_t prefix_offset;     // int32 [num_seqs + 1] chunk prefix (persistent grid)
     size_t lse_offset;        // float [max_partials][num_q_heads]
     size_t o_offset;          // float [max_partials][num_q_heads][head_dim]
     size_t bytes;
