@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+PROFILES = os.path.join(ROOT, "profiles")
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 ROTATE_BYTES = 1 << 30
@@ -47,7 +48,64 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="for counter runs: a few untimed steps of each kernel plus a reference device copy, no JSON")
+    ap.add_argument("--copy-mib", type=int, default=256, help="size of the reference copy in --profile-pass")
     return ap.parse_args()
+
+
+def profile_pass(args):
+    """A short program for rocprofv3 counter passes: the decode step and the
+    prefill kernel a few times each, and one plain device-to-device copy of
+    --copy-mib MiB whose counter readings calibrate the byte counters."""
+    import torch
+    from paged_kv_gqa_scatter_amd import workloads as W
+    from paged_kv_gqa_scatter_amd.runner import DeviceCase
+
+    n = max(1, args.steps)
+    case = W.config2_decode()
+    n_rot = max(1, -(-ROTATE_BYTES // case.pool_bytes))  # as timed: every step reads HBM
+    dc = DeviceCase(case, pools=n_rot)
+    dc.run_fills()
+    for i in range(n):
+        dc.run_step(0, pool=i % n_rot)
+    pc = DeviceCase(W.config3_prefill())
+    pc.run_fills()
+    pc.append(pc.steps[0]["append"])
+    for _ in range(n):
+        pc.prefill(pc.steps[0]["prefill"])
+    src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"profile pass done: {n} decode steps, {n} prefills, copy of {args.copy_mib} MiB", flush=True)
+
+
+def library_source_hash() -> str:
+    """sha256 over the HIP library's sources: a counter record is valid only
+    for the kernels it was taken on."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "paged_kv_gqa_scatter_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def traffic_record(op: str):
+    """HBM bytes per launch of `op` from the committed rocprofv3 --pmc
+    summaries (lines `traffic-record: {json}` in profiles/*.md), or None when
+    no record matches the current sources."""
+    import glob
+    want = library_source_hash()
+    for f in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        for line in open(f, encoding="utf-8"):
+            if line.startswith("traffic-record:"):
+                rec = json.loads(line.split(":", 1)[1])
+                if rec.get("op") == op and rec.get("source_sha256") == want:
+                    return rec
+    return None
 
 
 def time_decode_workload(args):
@@ -148,6 +206,9 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench needs a GPU"
+    if args.profile_pass:
+        profile_pass(args)
+        return
 
     case, dec, kv_bytes, n_rot, step_ms, dec_ms = time_decode_workload(args)
     gbs = kv_bytes / (step_ms * 1e-3) / 1e9
@@ -169,19 +230,26 @@ def main():
                                "32q/8kv heads, d128, block 256",
                    "seqs": int(dec.seq_lens.shape[0]), "keys": int(dec.seq_lens.sum()),
                    "unique_kv_bytes": int(kv_bytes), "pool_copies_rotated": n_rot},
-        "roofline": {"bound": "hbm", "kernel": "paged_gqa_decode (split + combine)", "achieved": round(dec_gbs, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "ms": round(dec_ms, 5)},
+        "roofline": {"bound": "hbm", "kernel": "paged_gqa_decode (decode_kernel + decode_merge_kernel)",
+                     "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": int(kv_bytes),
+                     "ms": round(dec_ms, 5)},
     }
+    rec = traffic_record("paged_gqa_decode")
+    if rec is not None:
+        line["roofline"]["traffic"] = int(rec["hbm_bytes_per_launch"])
     if not args.no_prefill:
         pcase, flops, pms = time_prefill_workload(args)
         tfs = flops / (pms * 1e-3) / 1e12
         line["prefill"] = {
             "workload": "qwen3-8b one-layer causal prefill: 4 prompts U[1024,4096], 32q/8kv, d128, block 256",
             "value": round(tfs, 2), "unit": "TFLOP/s", "causal_flops": int(flops), "ms": round(pms, 5),
-            "roofline": {"bound": "mfma", "kernel": "paged_gqa_prefill", "achieved": round(tfs, 2),
+            "roofline": {"bound": "mfma", "kernel": "paged_gqa_prefill (prefill_kernel)", "achieved": round(tfs, 2),
                          "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
                          "traffic": None}}
+        prec = traffic_record("paged_gqa_prefill")
+        if prec is not None:
+            line["prefill"]["roofline"]["traffic"] = int(prec["hbm_bytes_per_launch"])
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, dec, kv_bytes, args.cpu_seconds)
     print(json.dumps(line), flush=True)

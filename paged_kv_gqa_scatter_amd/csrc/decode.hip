@@ -53,6 +53,7 @@ constexpr int kDecodeThreads = 256;  // 4 waves share one work item
 constexpr int kDecodeWaves = kDecodeThreads / kWave;
 constexpr int kStepKeys = 64;        // keys whose K/V loads are in flight together
 constexpr int kXcds = 8;
+constexpr float kRescaleSlack = 8.f;  // log2 of the largest weight a stale running max may give
 
 struct DecodeKernelArgs {
     DecodeArgs a;
@@ -116,13 +117,18 @@ __device__ __forceinline__ void fold(float* v, bool upper) {
     }
 }
 
+// Reductions over the 64 lanes, returned wave-uniform: DPP inside each row of
+// 16 lanes; then every lane of a row holds the row's result, and the row
+// broadcasts 15 and 31 fold rows 0..2 into row 3, whose last lane is read into
+// a scalar register.
 __device__ __forceinline__ float wave_max(float x) {
     x = fmaxf(x, dpp<kDppXor1>(x));
     x = fmaxf(x, dpp<kDppXor2>(x));
     x = fmaxf(x, dpp<kDppHalfMirror>(x));
     x = fmaxf(x, dpp<kDppMirror>(x));
-    x = fmaxf(x, __shfl_xor(x, 16, kWave));
-    return fmaxf(x, __shfl_xor(x, 32, kWave));
+    x = fmaxf(x, dpp_rows<kDppRowBcast15, 0xA>(x, x));
+    x = fmaxf(x, dpp_rows<kDppRowBcast31, 0xC>(x, x));
+    return readlane(x, 63);
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
@@ -130,8 +136,9 @@ __device__ __forceinline__ float wave_sum(float x) {
     x += dpp<kDppXor2>(x);
     x += dpp<kDppHalfMirror>(x);
     x += dpp<kDppMirror>(x);
-    x += __shfl_xor(x, 16, kWave);
-    return x + __shfl_xor(x, 32, kWave);
+    x += dpp_rows<kDppRowBcast15, 0xA>(0.f, x);
+    x += dpp_rows<kDppRowBcast31, 0xC>(0.f, x);
+    return readlane(x, 63);
 }
 
 // Broadcast lane u of each group of kLanes lanes (16: DPP row broadcast;
@@ -146,24 +153,31 @@ __device__ __forceinline__ float group_bcast(float x) {
     }
 }
 
-template <int kLanes, int G, int u>
-__device__ __forceinline__ void pv_accumulate(float (&o)[G][8], const float (&pk)[G], const u32x4& v) {
-    float pu[G];
+// P V for the key pair (2a, 2a+1) of a step: their bf16 weights (already
+// rounded, so the packing is exact) times their V rows, two keys per dot2.
+template <int kLanes, int G, int a>
+__device__ __forceinline__ void pv_pair(float (&o)[G][8], const float (&pk)[G], const u32x4& va, const u32x4& vb) {
+    uint32_t pp[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) pu[h] = group_bcast<kLanes, u>(pk[h]);
+    for (int h = 0; h < G; ++h)
+        pp[h] = pack_bf16x2(group_bcast<kLanes, 2 * a>(pk[h]), group_bcast<kLanes, 2 * a + 1>(pk[h]));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float vi = (i & 1) ? bf16_hi(v[i >> 1]) : bf16_lo(v[i >> 1]);
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = (va[i] & 0xFFFFu) | (vb[i] << 16);         // dim 2i of keys 2a, 2a+1
+        const uint32_t hi = (va[i] >> 16) | (vb[i] & 0xFFFF0000u);     // dim 2i+1
 #pragma unroll
-        for (int h = 0; h < G; ++h) o[h][i] += pu[h] * vi;
+        for (int h = 0; h < G; ++h) {
+            o[h][2 * i] = dot2_bf16(lo, pp[h], o[h][2 * i]);
+            o[h][2 * i + 1] = dot2_bf16(hi, pp[h], o[h][2 * i + 1]);
+        }
     }
 }
 
-template <int kLanes, int G, int u>
+template <int kLanes, int G, int a>
 struct PvAll {
     static __device__ __forceinline__ void run(float (&o)[G][8], const float (&pk)[G], const u32x4* vr) {
-        PvAll<kLanes, G, u - 1>::run(o, pk, vr);
-        pv_accumulate<kLanes, G, u - 1>(o, pk, vr[u - 1]);
+        PvAll<kLanes, G, a - 1>::run(o, pk, vr);
+        pv_pair<kLanes, G, a - 1>(o, pk, vr[2 * a - 2], vr[2 * a - 1]);
     }
 };
 template <int kLanes, int G>
@@ -172,20 +186,25 @@ struct PvAll<kLanes, G, 0> {
 };
 
 // LDS of one workgroup: the waves' softmax states, then the item's merge.
+// o keeps each wave's per-row partial sums (rows of a wave load are summed by
+// the merge, which is cheaper than cross-row lane exchanges).
 template <int D, int G>
 struct DecodeShared {
-    float o[kDecodeWaves][G][D];
+    static constexpr int kRows = kWave / (D / 8);  // keys per wave load
+    float o[kDecodeWaves][kRows][G][D];
     float m[kDecodeWaves][G];
     float l[kDecodeWaves][G];
     int32_t wave_sum[kDecodeWaves];
 };
 
 // Steps base = k_begin + wave*64, + 4*64, ... below k_end of sequence s, KV
-// head g; leaves per-lane running max m (wave-uniform), sum l (per key lane)
-// and o (per row of a wave load).
-template <int D, int G>
+// head g; leaves the running max m (wave-uniform), the per-key-lane sums l and
+// the per-row outputs o.  first_blk is the block id of this wave's first step,
+// loaded by the caller together with the sequence length.
+template <int D, int G, bool kWholeStep>
 __device__ __forceinline__ void wave_steps(const DecodeKernelArgs& p, int s, int g, int k_begin, int k_end,
-                                           int lane, int wave, float (&m)[G], float (&l)[G], float (&o)[G][8]) {
+                                           int first_blk, const u32x4 (&qv)[G], int lane, int wave, float (&m)[G],
+                                           float (&l)[G], float (&o)[G][8]) {
     constexpr int kLanesPerKey = D / 8;                 // lanes per key row (16 B each)
     constexpr int kKeysPerLoad = kWave / kLanesPerKey;  // rows per wave load
     constexpr int kLoads = kStepKeys / kKeysPerLoad;    // wave loads per step (= kLanesPerKey)
@@ -194,29 +213,40 @@ __device__ __forceinline__ void wave_steps(const DecodeKernelArgs& p, int s, int
     const int kq = lane / kLanesPerKey;
     const int dl = lane % kLanesPerKey;
     const int B = 1 << p.log2_block;
-    const int Hq = a.num_q_heads;
     const int64_t tile = (int64_t)B * D;  // elements of one (block, head) tile
     const int32_t* table = a.block_table + (int64_t)s * a.max_blocks_per_seq;
+    const int last_entry = a.max_blocks_per_seq - 1;
     const u32x4 zero = {0u, 0u, 0u, 0u};
-
-    u32x4 qv[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) qv[h] = load16(a.q + ((int64_t)s * Hq + g * G + h) * D + dl * 8);
+    int blk_step = first_blk;  // the whole step's block when kWholeStep (blocks of >= 64 keys)
 
     for (int base = k_begin + wave * kStepKeys; base < k_end; base += kDecodeWaves * kStepKeys) {
+        // ---- block ids of the step's rows first (one batch of loads when blocks
+        //      are smaller than a step), so that the K/V loads below go out back
+        //      to back with no wait between them
+        int blks[kLoads];
+        if constexpr (kWholeStep) {
+#pragma unroll
+            for (int u = 0; u < kLoads; ++u) blks[u] = blk_step;
+        } else {
+#pragma unroll
+            for (int u = 0; u < kLoads; ++u) {
+                const int j = base + u * kKeysPerLoad + kq;
+                blks[u] = table[min(j, k_end - 1) >> p.log2_block];
+            }
+        }
         // ---- issue every K and V load of the step
         u32x4 kr[kLoads], vr[kLoads];
-        const int blk_step = table[base >> p.log2_block];  // the whole step when B >= 64
 #pragma unroll
         for (int u = 0; u < kLoads; ++u) {
             const int j = base + u * kKeysPerLoad + kq;
-            int blk = B >= kStepKeys ? blk_step : (j < k_end ? table[j >> p.log2_block] : -1);
-            const bool ok = j < k_end && (unsigned)blk < (unsigned)a.num_blocks;
-            blk = ok ? blk : 0;  // masked lanes keep an in-bounds address
+            const bool ok = j < k_end && (unsigned)blks[u] < (unsigned)a.num_blocks;
+            const int blk = ok ? blks[u] : 0;  // masked lanes keep an in-bounds address
             const int64_t off = ((int64_t)blk * a.num_kv_heads + g) * tile + (int64_t)(j & (B - 1)) * D + dl * 8;
             kr[u] = ok ? load16(a.k_pool + off) : zero;
             vr[u] = ok ? load16(a.v_pool + off) : zero;
         }
+        const int cur_blk = blk_step;
+        blk_step = table[min((base + kDecodeWaves * kStepKeys) >> p.log2_block, last_entry)];  // next step's
         // ---- partial dots: sc[u * G + h] over this lane's 8 dims
         float sc[kLoads * G];
 #pragma unroll
@@ -241,22 +271,27 @@ __device__ __forceinline__ void wave_steps(const DecodeKernelArgs& p, int s, int
         }
         const int key = base + dl * kKeysPerLoad + kq;
         bool valid = key < k_end;
-        if (valid) valid = (unsigned)(B >= kStepKeys ? blk_step : table[key >> p.log2_block]) < (unsigned)a.num_blocks;
-        // ---- online softmax (exp2 domain); one key per lane
+        if (valid) valid = (unsigned)(kWholeStep ? cur_blk : table[key >> p.log2_block]) < (unsigned)a.num_blocks;
+        // ---- online softmax (exp2 domain), one key per lane; the running max
+        //      is wave-uniform and moves only when it would grow by > 2^8
         float pk[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             const float z = valid ? sc[h] * p.qk_scale_log2 : -INFINITY;
-            const float m_new = fmaxf(m[h], wave_max(z));
-            const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m[h] - m_new);
-            pk[h] = valid ? fast_exp2(z - m_new) : 0.f;
-            l[h] = l[h] * alpha + pk[h];
+            const float mx = wave_max(z);
+            if (mx > m[h] + kRescaleSlack) {
+                const float alpha = fast_exp2(m[h] - mx);  // 0 while m is -inf
+                l[h] *= alpha;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[h][i] *= alpha;
-            m[h] = m_new;
+                for (int i = 0; i < 8; ++i) o[h][i] *= alpha;
+                m[h] = mx;
+            }
+            // weights are rounded to bf16 for the dot2 P V; the sums take the same values
+            pk[h] = valid ? round_bf16(fast_exp2(z - m[h])) : 0.f;
+            l[h] += pk[h];
         }
-        // ---- P V over the step's keys
-        PvAll<kLanesPerKey, G, kLoads>::run(o, pk, vr);
+        // ---- P V over the step's keys, two keys per dot2
+        PvAll<kLanesPerKey, G, kLoads / 2>::run(o, pk, vr);
     }
 }
 
@@ -302,19 +337,41 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_merge_kernel(DecodeKern
     for (int k = 0; k < kElems; ++k) dst[k] = __builtin_bit_cast(uint16_t, (__bf16)(num[k] * inv));
 }
 
-// One work item: chunk c of sequence s, KV head g; `slot` is its partial slot
-// and `base` the slot of the sequence's first chunk.
+// What a work item needs before its first K/V load, fetched in one round
+// trip: the sequence length, the G query rows and this wave's first block id.
 template <int D, int G>
+struct ItemInputs {
+    int L_raw;
+    int first_blk;
+    u32x4 qv[G];
+};
+
+template <int D, int G>
+__device__ __forceinline__ ItemInputs<D, G> load_item_inputs(const DecodeKernelArgs& p, int s, int g, int c) {
+    const DecodeArgs& a = p.a;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int dl = lane % (D / 8);
+    ItemInputs<D, G> in;
+    in.L_raw = a.seq_lens[s];
+#pragma unroll
+    for (int h = 0; h < G; ++h) in.qv[h] = load16(a.q + ((int64_t)s * a.num_q_heads + g * G + h) * D + dl * 8);
+    in.first_blk = a.block_table[(int64_t)s * a.max_blocks_per_seq +
+                                 min((c * p.chunk + wave * kStepKeys) >> p.log2_block, a.max_blocks_per_seq - 1)];
+    return in;
+}
+
+// One work item: chunk c of sequence s, KV head g; `slot` is its partial slot.
+template <int D, int G, bool kWholeStep>
 __device__ void decode_item(const DecodeKernelArgs& p, DecodeShared<D, G>& sh, int s, int g, int c, int nchunks,
-                            int64_t slot) {
+                            int64_t slot, const ItemInputs<D, G>& in) {
     constexpr int kLanesPerKey = D / 8;
     const DecodeArgs& a = p.a;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int kq = lane / kLanesPerKey, dl = lane % kLanesPerKey;
-    const int L = clamp_len(a.seq_lens[s], a.max_blocks_per_seq << p.log2_block);
-    const int k0 = c * p.chunk;
-    const int k1 = min(k0 + p.chunk, L);
     const int Hq = a.num_q_heads;
+    const int k0 = c * p.chunk;
+    const int L = clamp_len(in.L_raw, a.max_blocks_per_seq << p.log2_block);
+    const int k1 = min(k0 + p.chunk, L);
 
     float m[G], l[G], o[G][8];
 #pragma unroll
@@ -324,23 +381,14 @@ __device__ void decode_item(const DecodeKernelArgs& p, DecodeShared<D, G>& sh, i
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[h][i] = 0.f;
     }
-    wave_steps<D, G>(p, s, g, k0, k1, lane, wave, m, l, o);
+    wave_steps<D, G, kWholeStep>(p, s, g, k0, k1, in.first_blk, in.qv, lane, wave, m, l, o);
 
-    // ---- wave totals: l over every key lane, o over the rows of a wave load
+    // ---- wave totals: l over every key lane; o per row, summed by the merge
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         l[h] = wave_sum(l[h]);
-#pragma unroll
-        for (int off = kLanesPerKey; off < kWave; off <<= 1)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o[h][i] += __shfl_xor(o[h][i], off, kWave);
-    }
-    if (kq == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            *reinterpret_cast<f32x4*>(&sh.o[wave][h][dl * 8]) = f32x4{o[h][0], o[h][1], o[h][2], o[h][3]};
-            *reinterpret_cast<f32x4*>(&sh.o[wave][h][dl * 8 + 4]) = f32x4{o[h][4], o[h][5], o[h][6], o[h][7]};
-        }
+        *reinterpret_cast<f32x4*>(&sh.o[wave][kq][h][dl * 8]) = f32x4{o[h][0], o[h][1], o[h][2], o[h][3]};
+        *reinterpret_cast<f32x4*>(&sh.o[wave][kq][h][dl * 8 + 4]) = f32x4{o[h][4], o[h][5], o[h][6], o[h][7]};
     }
     if (lane == 0) {
 #pragma unroll
@@ -367,7 +415,12 @@ __device__ void decode_item(const DecodeKernelArgs& p, DecodeShared<D, G>& sh, i
         const float sc = sh.m[w][h] == -INFINITY ? 0.f : fast_exp2(sh.m[w][h] - mx);  // a wave without keys adds 0
         den += sh.l[w][h] * sc;
 #pragma unroll
-        for (int k = 0; k < kElems; ++k) val[k] += sh.o[w][h][d0 + k] * sc;
+        for (int k = 0; k < kElems; ++k) {
+            float rows = 0.f;
+#pragma unroll
+            for (int r = 0; r < DecodeShared<D, G>::kRows; ++r) rows += sh.o[w][r][h][d0 + k];
+            val[k] += rows * sc;
+        }
     }
     const int qh = g * G + h;
     const float inv = 1.f / den;
@@ -388,7 +441,7 @@ __device__ void decode_item(const DecodeKernelArgs& p, DecodeShared<D, G>& sh, i
     __syncthreads();  // LDS is reused by the next item
 }
 
-template <int D, int G>
+template <int D, int G, bool kWholeStep>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeKernelArgs p, int32_t* prefix_out) {
     __shared__ DecodeShared<D, G> sh;
     const int S = p.a.num_seqs;
@@ -403,12 +456,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeKernelArgs
         idx /= Hkv;
         const int s = idx % S;
         const int c = idx / S;
-        const int L = clamp_len(p.a.seq_lens[s], cap);
+        const ItemInputs<D, G> in = load_item_inputs<D, G>(p, s, g, c);  // before the exit test: one round trip
+        const int L = clamp_len(in.L_raw, cap);
         const int n = num_chunks(L, p.chunk);
         if (L == 0 && c == 0)  // a sequence without keys: zero rows
             for (int e = threadIdx.x; e < G * D; e += kDecodeThreads) p.a.out[((int64_t)s * Hq + g * G) * D + e] = 0;
         if (c >= n) return;
-        decode_item<D, G>(p, sh, s, g, c, n, (int64_t)s * p.max_chunks + c);
+        decode_item<D, G, kWholeStep>(p, sh, s, g, c, n, (int64_t)s * p.max_chunks + c, in);
         return;
     }
 
@@ -435,20 +489,21 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeKernelArgs
             if (s_prefix[mid] <= chunk) lo = mid; else hi = mid - 1;
         }
         const int n = s_prefix[lo + 1] - s_prefix[lo];
-        decode_item<D, G>(p, sh, lo, g, chunk - s_prefix[lo], n, chunk);
+        const int c = chunk - s_prefix[lo];
+        decode_item<D, G, kWholeStep>(p, sh, lo, g, c, n, chunk, load_item_inputs<D, G>(p, lo, g, c));
     }
 }
 
-template <int D, int G>
-hipError_t launch_typed(const DecodeKernelArgs& kp, int32_t* prefix, hipStream_t stream) {
+template <int D, int G, bool kWholeStep>
+hipError_t launch_grid(const DecodeKernelArgs& kp, int32_t* prefix, hipStream_t stream) {
     const DecodeArgs& a = kp.a;
     if (!kp.persistent) {
         const int64_t blocks = (int64_t)kp.max_chunks * a.num_seqs * a.num_kv_heads;
-        hipLaunchKernelGGL((decode_kernel<D, G>), dim3((unsigned)blocks), dim3(kDecodeThreads), 0, stream, kp, prefix);
+        hipLaunchKernelGGL((decode_kernel<D, G, kWholeStep>), dim3((unsigned)blocks), dim3(kDecodeThreads), 0, stream, kp, prefix);
     } else {
         const size_t lds = sizeof(int32_t) * (size_t)(a.num_seqs + 1);
         int per_cu = 0;
-        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, G>, kDecodeThreads, lds);
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, G, kWholeStep>, kDecodeThreads, lds);
         if (e != hipSuccess) return e;
         if (per_cu < 1) per_cu = 1;
         const int64_t direct = (int64_t)a.num_seqs * kp.max_chunks;
@@ -457,7 +512,7 @@ hipError_t launch_typed(const DecodeKernelArgs& kp, int32_t* prefix, hipStream_t
         int64_t resident = (int64_t)per_cu * device_cu_count() / kXcds * kXcds;
         if (resident < kXcds) resident = kXcds;
         if (blocks > resident) blocks = resident;
-        hipLaunchKernelGGL((decode_kernel<D, G>), dim3((unsigned)blocks), dim3(kDecodeThreads), lds, stream, kp,
+        hipLaunchKernelGGL((decode_kernel<D, G, kWholeStep>), dim3((unsigned)blocks), dim3(kDecodeThreads), lds, stream, kp,
                            prefix);
     }
     hipError_t e = hipGetLastError();
@@ -465,6 +520,13 @@ hipError_t launch_typed(const DecodeKernelArgs& kp, int32_t* prefix, hipStream_t
     hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3((unsigned)(a.num_seqs * a.num_kv_heads)),
                        dim3(kDecodeThreads), 0, stream, kp, (const int32_t*)prefix);
     return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t launch_typed(const DecodeKernelArgs& kp, int32_t* prefix, hipStream_t stream) {
+    // a 64-key step lies in one block when blocks hold >= 64 keys
+    if ((1 << kp.log2_block) >= kStepKeys) return launch_grid<D, G, true>(kp, prefix, stream);
+    return launch_grid<D, G, false>(kp, prefix, stream);
 }
 
 int ilog2(int x) {

@@ -45,13 +45,42 @@ enum : int {
     kDppXor2 = 0x4E,       // quad_perm [2,3,0,1]
     kDppHalfMirror = 0x141,
     kDppMirror = 0x140,
-    kDppRowBcast0 = 0x150  // + n: row_newbcast:n
+    kDppRowRor8 = 0x128,     // xor 8 within 16
+    kDppRowBcast15 = 0x142,  // lane 15 of each row -> the next row (scans)
+    kDppRowBcast31 = 0x143,  // lane 31 -> rows 2 and 3 (scans)
+    kDppRowBcast0 = 0x150    // + n: row_newbcast:n
 };
 
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
 }
+
+// DPP move of v into the rows enabled by kRowMask; other rows get `old`.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_rows(float old, float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
+                                                                  kCtrl, kRowMask, 0xF, false));
+}
+
+// Combine every lane with lane ^ 32 (v_permlane32_swap: one VALU op, no LDS).
+__device__ __forceinline__ float max_with_lane_xor32(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+__device__ __forceinline__ float sum_with_lane_xor32(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
+}
+
+__device__ __forceinline__ float readlane(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Round to bf16 (nearest even) and back.
+__device__ __forceinline__ float round_bf16(float x) { return (float)(__bf16)x; }
 
 // Lane-crossing reductions over groups of lanes.  `width` lanes with
 // consecutive ids form a group; the xor partner stays inside the group.

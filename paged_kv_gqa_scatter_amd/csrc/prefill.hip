@@ -21,7 +21,7 @@
 //    LDS with global_load_lds_dwordx4 (no register staging), double-buffered:
 //    the loads of tile t+1 are in flight while tile t is computed.  The LDS
 //    tile is unpadded; 16-byte pieces are XOR-swizzled per row so that the
-//    K reads (16 rows, one piece) and the transposing V reads (4 rows, two
+//    K reads (16 rows, one piece) and the transposing V reads (4 rows, four
 //    pieces) hit distinct banks.  Rows past the last visible key load a copy
 //    of a visible row, so no unwritten (NaN) slot reaches the MFMA, and are
 //    excluded by the mask.
@@ -75,10 +75,14 @@ __device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
 }
 
 // Slot of 16-byte piece `piece` of LDS tile row `row` (D/8 pieces per row).
+// The XOR key maps the 16 rows a K read touches (same piece) to 16 different
+// slots, and gives each of the 4 consecutive rows a transposing V read
+// touches (4 pieces) its own group of 4 slots, so neither read has two lanes
+// on one bank.
 template <int D>
 __device__ __forceinline__ int swizzle(int row, int piece) {
     constexpr int kPieces = D / 8;
-    return piece ^ ((((row & 7) << 1) | ((row >> 3) & 1)) & (kPieces - 1));
+    return piece ^ ((((row & 3) << 2) | ((row >> 2) & 3)) & (kPieces - 1));
 }
 
 // Rows of a 64-key tile this wave moves into LDS: rows [16 w, 16 w + 16),
