@@ -10,7 +10,9 @@ last-level cache.
 
 The metric also names prefill: the Qwen3-8B causal prefill workload (4 prompts
 of 1024..4096 tokens) is timed in the same run and reported as causal TFLOP/s
-(4 * D * Hq flops per unmasked query/key pair) under ``prefill``.
+(4 * D * Hq flops per unmasked query/key pair) under ``prefill``.  Decode at a
+bandwidth-bound scale (3.24 GB of unique K/V, shared prefixes and 32K-token
+sequences) is reported under ``long_context_decode``.
 
 Kernel durations are measured with HIP events on the stream the kernels run
 on; ``roofline`` relates the decode call to HBM peak, ``prefill.roofline`` the
@@ -43,10 +45,11 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3000)
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long", action="store_true", help="skip the long-context decode measurement")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile-pass", action="store_true",
                     help="for counter runs: a few untimed steps of each kernel plus a reference device copy, no JSON")
@@ -174,6 +177,48 @@ def time_prefill_workload(args):
     return case, flops, ms
 
 
+def time_long_decode(args):
+    """Decode at a bandwidth-bound scale: 256 sequences sharing a 4096-token
+    prefix (aliased blocks) plus 0..2048 private tokens, and 16 sequences of
+    32768 cached tokens (3.24 GB of unique K/V, 7.5 GB logical).  Lengths and
+    placement follow the seeded recipe; K/V/q values are drawn on the device
+    (timing only, no parity claim)."""
+    import torch
+    from paged_kv_gqa_scatter_amd import workloads as W
+    from paged_kv_gqa_scatter_amd.runner import DeviceCase
+
+    case = W.config5_prefix_long(draw_values=False)
+    dec = case.steps[0].decode
+    uniq = W.decode_unique_kv_bytes(case, dec)
+    logical = W.decode_logical_kv_bytes(case, dec)
+    dc = DeviceCase(case)
+    dc.run_fills()
+    step = dc.steps[0]
+    dc.append(step["append"])
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        dc.decode(step["decode"])
+    torch.cuda.synchronize()
+    n = max(5, args.prefill_steps)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record(stream)
+        dc.decode(step["decode"])
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    del dc
+    torch.cuda.empty_cache()
+    gbs = uniq / (ms * 1e-3) / 1e9
+    return {"workload": "qwen3-8b decode, 256 seqs sharing a 4096-token prefix + U[0,2048] private, 16 seqs x 32768; "
+                        "32q/8kv, d128, block 256",
+            "ms": round(ms, 5), "unique_kv_bytes": int(uniq), "logical_kv_bytes": int(logical),
+            "value": round(gbs, 2), "unit": "GB/s", "logical_gbs": round(logical / (ms * 1e-3) / 1e9, 2),
+            "roofline": {"bound": "hbm", "kernel": "paged_gqa_decode (decode_kernel + decode_merge_kernel)",
+                         "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
 def cpu_baseline(case, dec, kv_bytes, seconds):
     """The fp64 oracle on the same decode step, repeated for about `seconds`."""
     import oracle
@@ -250,6 +295,8 @@ def main():
         prec = traffic_record("paged_gqa_prefill")
         if prec is not None:
             line["prefill"]["roofline"]["traffic"] = int(prec["hbm_bytes_per_launch"])
+    if not args.no_long:
+        line["long_context_decode"] = time_long_decode(args)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, dec, kv_bytes, args.cpu_seconds)
     print(json.dumps(line), flush=True)

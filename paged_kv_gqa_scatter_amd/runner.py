@@ -14,11 +14,21 @@ import numpy as np
 import torch
 
 from . import kv_append, paged_gqa_decode, paged_gqa_prefill, decode_workspace_bytes
-from .workloads import NAN_SENTINEL, AppendBatch, Case, DecodeBatch, PrefillBatch
+from .workloads import NAN_SENTINEL, AppendBatch, Case, DecodeBatch, Deferred, PrefillBatch
 
 
-def _bits(a: np.ndarray, device) -> torch.Tensor:
-    """uint16 bf16 bits -> a CUDA bf16 tensor with the same bits."""
+_device_gen = {}
+
+
+def _bits(a, device) -> torch.Tensor:
+    """uint16 bf16 bits -> a CUDA bf16 tensor with the same bits; a Deferred
+    array is drawn here as N(0,1) with torch's seeded device generator."""
+    if isinstance(a, Deferred):
+        gen = _device_gen.get(str(device))
+        if gen is None:
+            gen = _device_gen[str(device)] = torch.Generator(device=device)
+            gen.manual_seed(0x5EED)
+        return torch.randn(a.shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
 
 

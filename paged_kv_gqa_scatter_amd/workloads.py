@@ -56,6 +56,20 @@ def bf16_normal(rng: np.random.Generator, shape) -> np.ndarray:
     return out.reshape(shape)
 
 
+class Deferred:
+    """Stands for a bf16 N(0,1) array that is drawn later, on the device.
+    Slicing keeps track of the shape only."""
+
+    def __init__(self, shape):
+        self.shape = tuple(int(x) for x in shape)
+
+    def __getitem__(self, key):
+        if isinstance(key, slice):
+            n = len(range(*key.indices(self.shape[0])))
+            return Deferred((n,) + self.shape[1:])
+        raise TypeError("Deferred arrays only support row slices")
+
+
 @dataclass
 class AppendBatch:
     """New K/V rows for ``kv_append``: rows of sequence s go to positions
@@ -133,7 +147,7 @@ def _ceil_div(a: int, b: int) -> int:
 def build_case(name: str, rng: np.random.Generator, *, hq: int, hkv: int, d: int, bs: int,
                ctx_lens, new_lens, kinds, spare: float = 0.25, num_blocks: Optional[int] = None,
                shared_prefix: int = 0, shared_seqs=None, scale: Optional[float] = None,
-               placement_seed: Optional[int] = None) -> Case:
+               placement_seed: Optional[int] = None, draw_values: bool = True) -> Case:
     """One batch of sequences: ``ctx_lens[s]`` tokens already cached (written
     by the fills), then a step that appends ``new_lens[s]`` tokens and runs
     decode (``kinds[s] == 'd'``, needs new_len 1) or chunked prefill
@@ -147,6 +161,10 @@ def build_case(name: str, rng: np.random.Generator, *, hq: int, hkv: int, d: int
     ``placement_seed`` replaces the drawn block permutation by one from another
     generator (the draw still happens, so the samples do not change): the same
     data at a different physical placement.
+
+    ``draw_values=False`` skips steps (3)-(5): K/V/q arrays are left as None
+    (with their shapes recorded) for timing runs that draw N(0,1) values on the
+    device instead; lengths and placement are unchanged.
     """
     ctx_lens = np.asarray(ctx_lens, dtype=np.int64)
     new_lens = np.asarray(new_lens, dtype=np.int64)
@@ -192,11 +210,14 @@ def build_case(name: str, rng: np.random.Generator, *, hq: int, hkv: int, d: int
     n_fill = shared_prefix + int(fill_new.sum())
     n_step = int(new_lens.sum())
 
-    # (3) K rows, (4) V rows: fills first, then the step
-    k_all = bf16_normal(rng, (n_fill + n_step, hkv, d))
-    v_all = bf16_normal(rng, (n_fill + n_step, hkv, d))
-    # (5) q rows of the step
-    q_all = bf16_normal(rng, (n_step, hq, d))
+    # (3) K rows, (4) V rows: fills first, then the step; (5) q rows of the step
+    if draw_values:
+        k_all = bf16_normal(rng, (n_fill + n_step, hkv, d))
+        v_all = bf16_normal(rng, (n_fill + n_step, hkv, d))
+        q_all = bf16_normal(rng, (n_step, hq, d))
+    else:
+        k_all = v_all = Deferred((n_fill + n_step, hkv, d))
+        q_all = Deferred((n_step, hq, d))
 
     def cu(lens):
         return np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
@@ -219,12 +240,12 @@ def build_case(name: str, rng: np.random.Generator, *, hq: int, hkv: int, d: int
     step = Step()
     step.append = AppendBatch(k_all[n_fill:], v_all[n_fill:], cu(new_lens), ctx_lens.astype(np.int32),
                               table.copy())
+    keep = (lambda a: a) if not draw_values else np.ascontiguousarray
     if nd:
-        step.decode = DecodeBatch(np.ascontiguousarray(q_all[:nd]), final[:nd].astype(np.int32),
-                                  np.ascontiguousarray(table[:nd]))
+        step.decode = DecodeBatch(keep(q_all[:nd]), final[:nd].astype(np.int32), np.ascontiguousarray(table[:nd]))
     if nd < S:
-        step.prefill = PrefillBatch(np.ascontiguousarray(q_all[nd:]), cu(new_lens[nd:]),
-                                    final[nd:].astype(np.int32), np.ascontiguousarray(table[nd:]))
+        step.prefill = PrefillBatch(keep(q_all[nd:]), cu(new_lens[nd:]), final[nd:].astype(np.int32),
+                                    np.ascontiguousarray(table[nd:]))
     sc = np.float32(1.0 / math.sqrt(d)) if scale is None else np.float32(scale)
     return Case(name, hq, hkv, d, bs, int(num_blocks), int(mbs), sc, fills, [step])
 
@@ -297,7 +318,7 @@ def config4_mixed(seed: int = 4) -> Case:
 
 
 def config5_prefix_long(seed: int = 5, n_share: int = 256, n_long: int = 16, long_ctx: int = 32768,
-                        prefix: int = 4096, private_max: int = 2048) -> Case:
+                        prefix: int = 4096, private_max: int = 2048, draw_values: bool = True) -> Case:
     """Prefix-sharing long-context decode: 256 sequences whose first 4096
     tokens alias the same 16 physical blocks, plus 0..2048 private cached
     tokens each; and 16 sequences with 32768 cached tokens.  The step appends
@@ -308,7 +329,7 @@ def config5_prefix_long(seed: int = 5, n_share: int = 256, n_long: int = 16, lon
     S = n_share + n_long
     return build_case("qwen3_8b_prefix4096x256_plus_16x32k", rng, hq=32, hkv=8, d=128, bs=256,
                       ctx_lens=ctx, new_lens=np.ones(S, np.int64), kinds="d" * S,
-                      shared_prefix=prefix, shared_seqs=range(n_share))
+                      shared_prefix=prefix, shared_seqs=range(n_share), draw_values=draw_values)
 
 
 CONFIGS = {1: config1_tiny, 2: config2_decode, 3: config3_prefill, 4: config4_mixed, 5: config5_prefix_long}
