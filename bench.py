@@ -58,8 +58,9 @@ def parse():
 
 
 def profile_pass(args):
-    """A short program for rocprofv3 counter passes: the decode step and the
-    prefill kernel a few times each, and one plain device-to-device copy of
+    """A short program for rocprofv3 counter passes: the decode step, the
+    prefill kernel and the long-context decode a few times each (the long one
+    last, unless --no-long), and one plain device-to-device copy of
     --copy-mib MiB whose counter readings calibrate the byte counters."""
     import torch
     from paged_kv_gqa_scatter_amd import workloads as W
@@ -77,11 +78,23 @@ def profile_pass(args):
     pc.append(pc.steps[0]["append"])
     for _ in range(n):
         pc.prefill(pc.steps[0]["prefill"])
+    nl = 0
+    if not args.no_long:
+        lc = DeviceCase(W.config5_prefix_long(draw_values=False))
+        lc.run_fills()
+        lc.append(lc.steps[0]["append"])
+        nl = n
+        for _ in range(n):
+            lc.decode(lc.steps[0]["decode"])
+        torch.cuda.synchronize()
+        del lc
+        torch.cuda.empty_cache()
     src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     dst.copy_(src)
     torch.cuda.synchronize()
-    print(f"profile pass done: {n} decode steps, {n} prefills, copy of {args.copy_mib} MiB", flush=True)
+    print(f"profile pass done: {n} decode steps, {n} prefills, {nl} long-context decodes, copy of {args.copy_mib} MiB",
+          flush=True)
 
 
 def library_source_hash() -> str:

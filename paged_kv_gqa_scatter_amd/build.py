@@ -15,6 +15,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # no packed fp32 VALU instructions (v_pk_*_f32) anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs (no AGPR copies around the VALU rescale)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-result",
 ]
 

@@ -7,32 +7,36 @@
 // section 3.3).  The design on gfx950:
 //
 //  * Work item = (sequence, KV head, chunk of `chunk` keys), one workgroup of
-//    4 waves.  Each wave takes every 4th step of 64 keys of the chunk; the
-//    waves' partial softmax states are merged through LDS.  Short batches use
-//    a direct grid over (chunk, sequence, KV head) whose empty items exit at
-//    once; long, uneven batches use a persistent grid over a compact item list
-//    that each workgroup derives from seq_lens (a block scan in LDS).  Either
-//    way nothing is read back to the host, and the KV head sits in the low
-//    bits of the workgroup index, so items of one KV head run on one XCD
-//    (workgroups are dealt round-robin over the 8 XCDs) and K/V rows shared
-//    between sequences (a common prefix) are re-read from that XCD's L2.
-//  * Within a step all K and V loads are issued before any is used: D/8 lanes
-//    cover one row with 16-byte loads, a wave load reads 64/(D/8) consecutive
-//    rows of one contiguous (block, head) tile, and D/8 such loads cover the 64
-//    keys -- 32 KB in flight per wave.  Each K row, once in registers, serves
-//    all G query heads of the group.
-//  * Scores: each lane dots its 8 dims of each of its keys with the G query
-//    heads (bf16 dot2, fp32 accumulate).  The D/8 partial sums are folded
-//    across the row's lanes with DPP moves in a transposing order: at every
-//    fold a lane keeps half of its values and adds its partner's copy of that
-//    half, so after log2(D/8) folds each lane holds the complete G scores of
-//    exactly one key.  The softmax then costs G exponentials per lane.
-//  * Online softmax in the exp2 domain (scale * log2 e folded in); the step
-//    max is a wave reduction; rows past the sequence end are excluded by a
-//    select, never multiplied by zero (unwritten slots may hold NaN).
-//  * P V: each lane needs the weights of the keys whose V rows it holds; they
-//    are broadcast inside each group of D/8 lanes (DPP row broadcast or an LDS
-//    swizzle) and accumulated into G x 8 fp32 outputs per lane.
+//    4 waves.  The chunk is cut into tiles of 16 keys and wave w takes tiles
+//    w, w + 4, w + 8, ...; the waves' softmax states are merged through LDS.
+//    Short batches use a direct grid over (chunk, sequence, KV head) whose
+//    empty items exit at once; long, uneven batches use a persistent grid over
+//    a compact item list that each workgroup derives from seq_lens (a block
+//    scan in LDS).  Nothing is read back to the host, and the KV head sits in
+//    the low bits of the workgroup index, so items of one KV head run on one
+//    XCD (workgroups are dealt round-robin over the 8 XCDs) and K/V rows
+//    shared between sequences (a common prefix) are re-read from that XCD's L2.
+//  * Every wave streams its own tiles through a private ring of 4 LDS stages:
+//    the K and V rows of a tile (16 rows of one contiguous (block, head) slab,
+//    as B >= 16) are copied by global_load_lds_dwordx4, each wave load moving
+//    1 KB of consecutive bytes, and three tiles are in flight while one is
+//    computed.  The block id is wave-uniform, so the slab address is scalar
+//    arithmetic and every lane's offset is fixed for the item.  No barrier is
+//    needed inside the loop: a wave only reads what it loaded itself.
+//  * The G query heads of the group are the N side of the matrix cores,
+//    padded to 16 columns: S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (K rows
+//    from LDS, Q in registers, fp32 accumulate) leaves each lane the scores
+//    of 4 keys for one head, which is already the operand layout of
+//    O^T += V^T P^T (v_mfma_f32_16x16x16_bf16, keys as the contraction
+//    index); V^T comes from LDS with ds_read_b64_tr_b16.  Counted per key,
+//    the dot products on the vector ALUs alone cost more issue cycles than
+//    HBM needs to deliver the row; on the matrix cores they are a few cycles.
+//  * Online softmax in the exp2 domain (scale * log2 e folded in).  The
+//    running max of a head moves only when a score outgrows it by more than
+//    2^8 (checked per tile with one wave vote); the weights are rounded to
+//    bf16 for the MFMA and the running sum adds exactly those values.  Rows
+//    past the sequence end are masked to -inf, and their DMA reads a copy of
+//    the last valid row, so no unwritten (NaN) slot reaches the MFMA.
 //  * Chunks of a sequence write a normalised partial and its log2-sum-exp; a
 //    second kernel merges them in one pass with a running maximum
 //    (out = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M)).  The hand-off goes
@@ -51,13 +55,22 @@ namespace {
 
 constexpr int kDecodeThreads = 256;  // 4 waves share one work item
 constexpr int kDecodeWaves = kDecodeThreads / kWave;
-constexpr int kStepKeys = 64;        // keys whose K/V loads are in flight together
+constexpr int kTileKeys = 16;        // keys per MFMA tile and per LDS stage of a wave
+constexpr int kStages = 4;           // LDS ring depth of a wave
+constexpr int kMaxTilesPerWave = 128;  // ids of a wave's tiles sit in two registers
+constexpr int kMaxChunk = kMaxTilesPerWave * kTileKeys * kDecodeWaves;
+constexpr int kMaxPersistentSeqs = 2048;  // chunk prefix kept in LDS
 constexpr int kXcds = 8;
 constexpr float kRescaleSlack = 8.f;  // log2 of the largest weight a stale running max may give
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // the bf16 pair (1.0, 1.0)
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct DecodeKernelArgs {
     DecodeArgs a;
-    int32_t chunk;       // keys per work item (multiple of 4 * 64)
+    int32_t chunk;       // keys per work item (multiple of 256, at most kMaxChunk)
     int32_t log2_block;
     int32_t max_chunks;  // chunks of the longest sequence
     int32_t persistent;  // 1: persistent grid over the compact item list
@@ -70,6 +83,15 @@ struct DecodeKernelArgs {
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
 __device__ __forceinline__ int num_chunks(int L, int chunk) { return L > 0 ? (L + chunk - 1) / chunk : 0; }
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (loads retire in issue order).  The memory clobber keeps the compiler from
+// moving LDS reads above it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Exclusive prefix of chunk counts over all sequences into s_prefix[0..S];
 // every thread of the block takes part.
@@ -102,196 +124,218 @@ __device__ void chunk_prefix(const DecodeKernelArgs& p, int32_t* s_prefix, int32
     __syncthreads();
 }
 
-// One fold of the transposing reduction over the lanes of a key row: lanes
-// whose `upper` bit is set keep the upper half of v[0..N) and the others the
-// lower half; each adds its partner's copy of the half it keeps.  kCtrl must
-// pair every lane with one whose `upper` bit differs and whose bits above it
-// agree.
-template <int N, int kCtrl>
-__device__ __forceinline__ void fold(float* v, bool upper) {
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ s16x4 as_s16x4(u32x2 v) { return __builtin_bit_cast(s16x4, v); }
+
+// Transposing LDS read: within each 16-lane group, lane i receives element
+// i % 4 of the 8 bytes addressed by lanes 4r + i / 4 (r = 0..3).
+__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
+    s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+    return __builtin_bit_cast(u32x2, t);
+}
+
+// LDS slot of 16-byte piece `piece` of stage row `row` (an involution, so it
+// also names the piece that lands in a slot).  The K reads (16 rows, one
+// piece each) and the transposing V reads (4 rows, two adjacent pieces each)
+// then never put two lanes of a group on one bank.
+template <int D>
+__device__ __forceinline__ int swz(int row, int piece) {
+    return piece ^ ((((row & 3) << 1) | ((row >> 2) & 1)) & (D / 8 - 1));
+}
+
+// What a lane does with a 16-key tile, fixed for the whole item.
+template <int D>
+struct TileLanes {
+    static constexpr int kPieces = D / 8;               // 16-byte pieces per row
+    static constexpr int kRowsPerLoad = kWave / kPieces;
+    static constexpr int kLoads = kTileKeys / kRowsPerLoad;  // wave loads per matrix and tile
+    static constexpr int kDma = 2 * kLoads;                  // K and V
+    int row[kLoads];     // DMA: row of the tile this lane's 16 bytes belong to
+    int piece8[kLoads];  // DMA: element offset of the piece within the row
+    int k_off[D / 32];   // QK: LDS element offset of this lane's K fragment, per 32 dims
+    int v_off[D / 16];   // PV: LDS element offset of this lane's transposing read, per 16 dims
+};
+
+template <int D>
+__device__ __forceinline__ TileLanes<D> tile_lanes(int lane) {
+    using T = TileLanes<D>;
+    TileLanes<D> tl;
 #pragma unroll
-    for (int i = 0; i < N / 2; ++i) {
-        const float keep = upper ? v[N / 2 + i] : v[i];
-        const float send = upper ? v[i] : v[N / 2 + i];
-        v[i] = keep + dpp<kCtrl>(send);
+    for (int i = 0; i < T::kLoads; ++i) {
+        tl.row[i] = i * T::kRowsPerLoad + lane / T::kPieces;
+        tl.piece8[i] = swz<D>(tl.row[i], lane % T::kPieces) * 8;
     }
+    const int j = lane >> 4, i16 = lane & 15;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) tl.k_off[c] = i16 * D + swz<D>(i16, c * 4 + j) * 8;
+    const int vrow = 4 * j + (i16 >> 2), q = i16 & 3;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) tl.v_off[db] = vrow * D + swz<D>(vrow, 2 * db + (q >> 1)) * 8 + 4 * (q & 1);
+    return tl;
 }
 
-// Reductions over the 64 lanes, returned wave-uniform: DPP inside each row of
-// 16 lanes; then every lane of a row holds the row's result, and the row
-// broadcasts 15 and 31 fold rows 0..2 into row 3, whose last lane is read into
-// a scalar register.
-__device__ __forceinline__ float wave_max(float x) {
-    x = fmaxf(x, dpp<kDppXor1>(x));
-    x = fmaxf(x, dpp<kDppXor2>(x));
-    x = fmaxf(x, dpp<kDppHalfMirror>(x));
-    x = fmaxf(x, dpp<kDppMirror>(x));
-    x = fmaxf(x, dpp_rows<kDppRowBcast15, 0xA>(x, x));
-    x = fmaxf(x, dpp_rows<kDppRowBcast31, 0xC>(x, x));
-    return readlane(x, 63);
+// The four LDS stages of the block's waves (distinct objects, so the
+// compiler never confuses the loads in flight into one with reads of another).
+template <int D>
+struct Stages {
+    uint16_t* k[kStages];
+    uint16_t* v[kStages];
+};
+
+// LDS byte address of a __shared__ object (what M0 holds for an LDS DMA).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-    x += dpp<kDppXor1>(x);
-    x += dpp<kDppXor2>(x);
-    x += dpp<kDppHalfMirror>(x);
-    x += dpp<kDppMirror>(x);
-    x += dpp_rows<kDppRowBcast15, 0xA>(0.f, x);
-    x += dpp_rows<kDppRowBcast31, 0xC>(0.f, x);
-    return readlane(x, 63);
+// global_load_lds_dwordx4 with a scalar base: lane l's 16 bytes at
+// base + voff land at LDS byte address lds + 16 l.  Written as inline asm so
+// that the compiler, which cannot tell the four stages apart, does not wait
+// for every copy in flight before each LDS read; the ring's waits are
+// explicit (wait_vmcnt).
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
 }
 
-// Broadcast lane u of each group of kLanes lanes (16: DPP row broadcast;
-// 8: LDS swizzle in broadcast mode).
-template <int kLanes, int u>
-__device__ __forceinline__ float group_bcast(float x) {
-    if constexpr (kLanes == 16) {
-        return dpp<kDppRowBcast0 + u>(x);
+// Copy tile rows [kt, kt + 16) of (block blk, KV head g) into a stage; rows at
+// or past kend repeat row kend - 1.
+template <int D>
+__device__ __forceinline__ void issue_tile(const DecodeArgs& a, int log2_block, int g, int blk, int kt, int kend,
+                                           const TileLanes<D>& tl, uint32_t sk, uint32_t sv) {
+    using T = TileLanes<D>;
+    const int B = 1 << log2_block;
+    const int64_t slab = ((int64_t)blk * a.num_kv_heads + g) * ((int64_t)B * D) + (int64_t)(kt & (B - 1)) * D;
+    const uint16_t* kb = a.k_pool + slab;
+    const uint16_t* vb = a.v_pool + slab;
+    const int last = kend - 1 - kt;
+    if (last >= kTileKeys - 1) {
+#pragma unroll
+        for (int i = 0; i < T::kLoads; ++i) {
+            const uint32_t off = (uint32_t)(tl.row[i] * D + tl.piece8[i]) * 2u;
+            dma16(kb, off, sk + i * kWave * 16);
+            dma16(vb, off, sv + i * kWave * 16);
+        }
     } else {
-        static_assert(kLanes == 8, "groups of 8 or 16 lanes");
-        return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x18 | (u << 5)));
-    }
-}
-
-// P V for the key pair (2a, 2a+1) of a step: their bf16 weights (already
-// rounded, so the packing is exact) times their V rows, two keys per dot2.
-template <int kLanes, int G, int a>
-__device__ __forceinline__ void pv_pair(float (&o)[G][8], const float (&pk)[G], const u32x4& va, const u32x4& vb) {
-    uint32_t pp[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-        pp[h] = pack_bf16x2(group_bcast<kLanes, 2 * a>(pk[h]), group_bcast<kLanes, 2 * a + 1>(pk[h]));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = (va[i] & 0xFFFFu) | (vb[i] << 16);         // dim 2i of keys 2a, 2a+1
-        const uint32_t hi = (va[i] >> 16) | (vb[i] & 0xFFFF0000u);     // dim 2i+1
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            o[h][2 * i] = dot2_bf16(lo, pp[h], o[h][2 * i]);
-            o[h][2 * i + 1] = dot2_bf16(hi, pp[h], o[h][2 * i + 1]);
+        for (int i = 0; i < T::kLoads; ++i) {
+            const uint32_t off = (uint32_t)(min(tl.row[i], last) * D + tl.piece8[i]) * 2u;
+            dma16(kb, off, sk + i * kWave * 16);
+            dma16(vb, off, sv + i * kWave * 16);
         }
     }
 }
 
-template <int kLanes, int G, int a>
-struct PvAll {
-    static __device__ __forceinline__ void run(float (&o)[G][8], const float (&pk)[G], const u32x4* vr) {
-        PvAll<kLanes, G, a - 1>::run(o, pk, vr);
-        pv_pair<kLanes, G, a - 1>(o, pk, vr[2 * a - 2], vr[2 * a - 1]);
+// One wave's running softmax state: O^T fragments (rows = dims, column =
+// this lane's head), the head's running max and this lane's share of the sum.
+template <int D>
+struct WaveState {
+    f32x4 acc[D / 16];
+    float m;
+    float l;
+};
+
+// Per-wave view of the item.
+template <int D>
+struct WaveItem {
+    const DecodeArgs* a;
+    int log2_block, g, k0, kend, wave, lane, n_tiles;
+    int ids0, ids1;  // block id of tile t in lane t % 64 of ids(t / 64)
+    float c;         // scale * log2 e
+    u32x4 qf[D / 32];
+    TileLanes<D> tl;
+    Stages<D> st;
+};
+
+template <int D>
+__device__ __forceinline__ int tile_blk(const WaveItem<D>& w, int t) {
+    const int v = t < kWave ? w.ids0 : w.ids1;
+    return __builtin_amdgcn_readlane(v, t & (kWave - 1));
+}
+
+template <int D>
+__device__ __forceinline__ int tile_key(const WaveItem<D>& w, int t) {
+    return w.k0 + kTileKeys * (w.wave + kDecodeWaves * t);
+}
+
+template <int D>
+__device__ __forceinline__ void issue(const WaveItem<D>& w, int t, int stage) {
+    const int blk = tile_blk(w, t);
+    const int b = (unsigned)blk < (unsigned)w.a->num_blocks ? blk : 0;  // a bad id reads block 0, masked below
+    const uint32_t wave_bytes = (uint32_t)(w.wave * kTileKeys * D * 2);
+    issue_tile<D>(*w.a, w.log2_block, w.g, b, tile_key(w, t), w.kend, w.tl, lds_addr(w.st.k[stage]) + wave_bytes,
+                  lds_addr(w.st.v[stage]) + wave_bytes);
+}
+
+// Tile t from stage kS: wait for it, refill the stage freed by tile t - 1
+// with tile t + 3, then S^T, softmax, O^T.
+template <int D, int kS>
+__device__ __forceinline__ void tile_step(const WaveItem<D>& w, int t, WaveState<D>& ws) {
+    constexpr int kDma = TileLanes<D>::kDma;
+    const int after = min(kStages - 2, w.n_tiles - 1 - t);  // tiles issued after t
+    if (after >= 2) wait_vmcnt<2 * kDma>();
+    else if (after == 1) wait_vmcnt<kDma>();
+    else wait_vmcnt<0>();
+    if (t + kStages - 1 < w.n_tiles) issue(w, t + kStages - 1, (kS + kStages - 1) % kStages);
+
+    // every LDS read of the tile goes out before the first MFMA waits on one
+    const uint16_t* sk = w.st.k[kS] + w.wave * kTileKeys * D;
+    const uint16_t* sv = w.st.v[kS] + w.wave * kTileKeys * D;
+    u32x4 kf[D / 32];
+    u32x2 vf[D / 16];
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) kf[c] = *reinterpret_cast<const u32x4*>(sk + w.tl.k_off[c]);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) vf[db] = lds_read_tr(sv + w.tl.v_off[db]);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[c]), as_bf16x8(w.qf[c]), s, 0, 0, 0);
+
+    // lane (j, h) holds the scores of keys kt + 4j + r (r = 0..3) for head h
+    const int kt = tile_key(w, t);
+    const bool ok_blk = (unsigned)tile_blk(w, t) < (unsigned)w.a->num_blocks;
+    float z[4];
+    if (ok_blk && kt + kTileKeys <= w.kend) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) z[r] = s[r] * w.c;
+    } else {
+        const int key0 = kt + 4 * (w.lane >> 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) z[r] = ok_blk && key0 + r < w.kend ? s[r] * w.c : -INFINITY;
     }
-};
-template <int kLanes, int G>
-struct PvAll<kLanes, G, 0> {
-    static __device__ __forceinline__ void run(float (&)[G][8], const float (&)[G], const u32x4*) {}
-};
+    const float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    if (__any(mx > ws.m + kRescaleSlack)) {
+        float mh = fmaxf(mx, __shfl_xor(mx, 16, kWave));  // the head's max over the tile
+        mh = fmaxf(mh, __shfl_xor(mh, 32, kWave));
+        const float m_new = fmaxf(ws.m, mh);
+        const float alpha = fast_exp2(ws.m - m_new);  // 0 while m is -inf
+        ws.l *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) ws.acc[db] *= alpha;
+        ws.m = m_new;
+    }
+    // a head whose tile is all masked keeps m = -inf and gets zero weights
+    const float mref = ws.m == -INFINITY ? 0.f : ws.m;
+    const u32x2 pk = {pack_bf16x2(fast_exp2(z[0] - mref), fast_exp2(z[1] - mref)),
+                      pack_bf16x2(fast_exp2(z[2] - mref), fast_exp2(z[3] - mref))};
+    ws.l = dot2_bf16(pk[0], kOnesBf16x2, ws.l);
+    ws.l = dot2_bf16(pk[1], kOnesBf16x2, ws.l);
 
-// LDS of one workgroup: the waves' softmax states, then the item's merge.
-// o keeps each wave's per-row partial sums (rows of a wave load are summed by
-// the merge, which is cheaper than cross-row lane exchanges).
-template <int D, int G>
-struct DecodeShared {
-    static constexpr int kRows = kWave / (D / 8);  // keys per wave load
-    float o[kDecodeWaves][kRows][G][D];
-    float m[kDecodeWaves][G];
-    float l[kDecodeWaves][G];
-    int32_t wave_sum[kDecodeWaves];
-};
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+        ws.acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(vf[db]), as_s16x4(pk), ws.acc[db], 0, 0, 0);
+}
 
-// Steps base = k_begin + wave*64, + 4*64, ... below k_end of sequence s, KV
-// head g; leaves the running max m (wave-uniform), the per-key-lane sums l and
-// the per-row outputs o.  first_blk is the block id of this wave's first step,
-// loaded by the caller together with the sequence length.
-template <int D, int G, bool kWholeStep>
-__device__ __forceinline__ void wave_steps(const DecodeKernelArgs& p, int s, int g, int k_begin, int k_end,
-                                           int first_blk, const u32x4 (&qv)[G], int lane, int wave, float (&m)[G],
-                                           float (&l)[G], float (&o)[G][8]) {
-    constexpr int kLanesPerKey = D / 8;                 // lanes per key row (16 B each)
-    constexpr int kKeysPerLoad = kWave / kLanesPerKey;  // rows per wave load
-    constexpr int kLoads = kStepKeys / kKeysPerLoad;    // wave loads per step (= kLanesPerKey)
-    static_assert(kLoads == kLanesPerKey, "one key per lane after the fold");
-    const DecodeArgs& a = p.a;
-    const int kq = lane / kLanesPerKey;
-    const int dl = lane % kLanesPerKey;
-    const int B = 1 << p.log2_block;
-    const int64_t tile = (int64_t)B * D;  // elements of one (block, head) tile
-    const int32_t* table = a.block_table + (int64_t)s * a.max_blocks_per_seq;
-    const int last_entry = a.max_blocks_per_seq - 1;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    int blk_step = first_blk;  // the whole step's block when kWholeStep (blocks of >= 64 keys)
-
-    for (int base = k_begin + wave * kStepKeys; base < k_end; base += kDecodeWaves * kStepKeys) {
-        // ---- block ids of the step's rows first (one batch of loads when blocks
-        //      are smaller than a step), so that the K/V loads below go out back
-        //      to back with no wait between them
-        int blks[kLoads];
-        if constexpr (kWholeStep) {
+template <int D>
+__device__ __forceinline__ void wave_tiles(const WaveItem<D>& w, WaveState<D>& ws) {
 #pragma unroll
-            for (int u = 0; u < kLoads; ++u) blks[u] = blk_step;
-        } else {
-#pragma unroll
-            for (int u = 0; u < kLoads; ++u) {
-                const int j = base + u * kKeysPerLoad + kq;
-                blks[u] = table[min(j, k_end - 1) >> p.log2_block];
-            }
-        }
-        // ---- issue every K and V load of the step
-        u32x4 kr[kLoads], vr[kLoads];
-#pragma unroll
-        for (int u = 0; u < kLoads; ++u) {
-            const int j = base + u * kKeysPerLoad + kq;
-            const bool ok = j < k_end && (unsigned)blks[u] < (unsigned)a.num_blocks;
-            const int blk = ok ? blks[u] : 0;  // masked lanes keep an in-bounds address
-            const int64_t off = ((int64_t)blk * a.num_kv_heads + g) * tile + (int64_t)(j & (B - 1)) * D + dl * 8;
-            kr[u] = ok ? load16(a.k_pool + off) : zero;
-            vr[u] = ok ? load16(a.v_pool + off) : zero;
-        }
-        const int cur_blk = blk_step;
-        blk_step = table[min((base + kDecodeWaves * kStepKeys) >> p.log2_block, last_entry)];  // next step's
-        // ---- partial dots: sc[u * G + h] over this lane's 8 dims
-        float sc[kLoads * G];
-#pragma unroll
-        for (int u = 0; u < kLoads; ++u)
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float acc = 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc = dot2_bf16(qv[h][i], kr[u][i], acc);
-                sc[u * G + h] = acc;
-            }
-        // ---- transposing fold: afterwards sc[0..G) are the scores of key u = dl
-        if constexpr (kLanesPerKey == 16) {
-            fold<16 * G, kDppMirror>(sc, dl & 8);
-            fold<8 * G, kDppHalfMirror>(sc, dl & 4);
-            fold<4 * G, kDppXor2>(sc, dl & 2);
-            fold<2 * G, kDppXor1>(sc, dl & 1);
-        } else {
-            fold<8 * G, kDppHalfMirror>(sc, dl & 4);
-            fold<4 * G, kDppXor2>(sc, dl & 2);
-            fold<2 * G, kDppXor1>(sc, dl & 1);
-        }
-        const int key = base + dl * kKeysPerLoad + kq;
-        bool valid = key < k_end;
-        if (valid) valid = (unsigned)(kWholeStep ? cur_blk : table[key >> p.log2_block]) < (unsigned)a.num_blocks;
-        // ---- online softmax (exp2 domain), one key per lane; the running max
-        //      is wave-uniform and moves only when it would grow by > 2^8
-        float pk[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float z = valid ? sc[h] * p.qk_scale_log2 : -INFINITY;
-            const float mx = wave_max(z);
-            if (mx > m[h] + kRescaleSlack) {
-                const float alpha = fast_exp2(m[h] - mx);  // 0 while m is -inf
-                l[h] *= alpha;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) o[h][i] *= alpha;
-                m[h] = mx;
-            }
-            // weights are rounded to bf16 for the dot2 P V; the sums take the same values
-            pk[h] = valid ? round_bf16(fast_exp2(z - m[h])) : 0.f;
-            l[h] += pk[h];
-        }
-        // ---- P V over the step's keys, two keys per dot2
-        PvAll<kLanesPerKey, G, kLoads / 2>::run(o, pk, vr);
+    for (int t = 0; t < kStages - 1; ++t)
+        if (t < w.n_tiles) issue(w, t, t);
+    for (int t = 0; t < w.n_tiles; t += kStages) {
+        tile_step<D, 0>(w, t, ws);
+        if (t + 1 < w.n_tiles) tile_step<D, 1>(w, t + 1, ws);
+        if (t + 2 < w.n_tiles) tile_step<D, 2>(w, t + 2, ws);
+        if (t + 3 < w.n_tiles) tile_step<D, 3>(w, t + 3, ws);
     }
 }
 
@@ -338,63 +382,102 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_merge_kernel(DecodeKern
 }
 
 // What a work item needs before its first K/V load, fetched in one round
-// trip: the sequence length, the G query rows and this wave's first block id.
-template <int D, int G>
+// trip: the sequence length, this lane's query fragments and the block ids
+// of this wave's tiles.
+template <int D>
 struct ItemInputs {
     int L_raw;
-    int first_blk;
-    u32x4 qv[G];
+    int ids0, ids1;
+    u32x4 qf[D / 32];
 };
 
+// This wave's index, known to the compiler to be the same on every lane.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Wait for every vector-memory operation of the wave, in a form the
+// compiler's own wait placement sees (so it adds none for those loads later).
+__device__ __forceinline__ void wait_all_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0) only
+
 template <int D, int G>
-__device__ __forceinline__ ItemInputs<D, G> load_item_inputs(const DecodeKernelArgs& p, int s, int g, int c) {
+__device__ __forceinline__ ItemInputs<D> load_item_inputs(const DecodeKernelArgs& p, int s, int g, int c) {
     const DecodeArgs& a = p.a;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int dl = lane % (D / 8);
-    ItemInputs<D, G> in;
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    ItemInputs<D> in;
     in.L_raw = a.seq_lens[s];
+    // Q^T fragment: head lane % 16 (zero past G), dims 32 c' + 8 (lane / 16) + [0, 8)
+    const int h = lane & 15, j = lane >> 4;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const uint16_t* qp = a.q + ((int64_t)s * a.num_q_heads + g * G + min(h, G - 1)) * D + 8 * j;
 #pragma unroll
-    for (int h = 0; h < G; ++h) in.qv[h] = load16(a.q + ((int64_t)s * a.num_q_heads + g * G + h) * D + dl * 8);
-    in.first_blk = a.block_table[(int64_t)s * a.max_blocks_per_seq +
-                                 min((c * p.chunk + wave * kStepKeys) >> p.log2_block, a.max_blocks_per_seq - 1)];
+    for (int cc = 0; cc < D / 32; ++cc) in.qf[cc] = h < G ? load16(qp + 32 * cc) : zero;
+    // block ids of tiles t = lane and lane + 64 (entries past the table row clamp to its end)
+    const int32_t* table = a.block_table + (int64_t)s * a.max_blocks_per_seq;
+    const int k0 = c * p.chunk;
+    const int last = a.max_blocks_per_seq - 1;
+    in.ids0 = table[min((k0 + kTileKeys * (wave + kDecodeWaves * lane)) >> p.log2_block, last)];
+    in.ids1 = p.chunk > kTileKeys * kDecodeWaves * kWave
+                  ? table[min((k0 + kTileKeys * (wave + kDecodeWaves * (lane + kWave))) >> p.log2_block, last)]
+                  : 0;
     return in;
 }
 
+// LDS of one workgroup besides the stages: the waves' softmax states.
+template <int D, int G>
+struct __attribute__((aligned(16))) DecodeShared {
+    float o[kDecodeWaves][G][D];
+    float m[kDecodeWaves][G];
+    float l[kDecodeWaves][G];
+    int32_t wave_sum[kDecodeWaves];
+};
+
 // One work item: chunk c of sequence s, KV head g; `slot` is its partial slot.
-template <int D, int G, bool kWholeStep>
-__device__ void decode_item(const DecodeKernelArgs& p, DecodeShared<D, G>& sh, int s, int g, int c, int nchunks,
-                            int64_t slot, const ItemInputs<D, G>& in) {
-    constexpr int kLanesPerKey = D / 8;
+template <int D, int G>
+__device__ __forceinline__ void decode_item(const DecodeKernelArgs& p, DecodeShared<D, G>& sh, const Stages<D>& st,
+                                            int s, int g, int c, int nchunks, int64_t slot,
+                                            const ItemInputs<D>& in) {
     const DecodeArgs& a = p.a;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int kq = lane / kLanesPerKey, dl = lane % kLanesPerKey;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int Hq = a.num_q_heads;
     const int k0 = c * p.chunk;
     const int L = clamp_len(in.L_raw, a.max_blocks_per_seq << p.log2_block);
     const int k1 = min(k0 + p.chunk, L);
+    const int tiles = (k1 - k0 + kTileKeys - 1) / kTileKeys;
 
-    float m[G], l[G], o[G][8];
+    WaveItem<D> w;
+    w.a = &a;
+    w.log2_block = p.log2_block;
+    w.g = g;
+    w.k0 = k0;
+    w.kend = k1;
+    w.wave = wave;
+    w.lane = lane;
+    w.n_tiles = tiles > wave ? (tiles - wave + kDecodeWaves - 1) / kDecodeWaves : 0;
+    w.ids0 = in.ids0;
+    w.ids1 = in.ids1;
+    w.c = p.qk_scale_log2;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[h][i] = 0.f;
-    }
-    wave_steps<D, G, kWholeStep>(p, s, g, k0, k1, in.first_blk, in.qv, lane, wave, m, l, o);
+    for (int cc = 0; cc < D / 32; ++cc) w.qf[cc] = in.qf[cc];
+    w.tl = tile_lanes<D>(lane);
+    w.st = st;
 
-    // ---- wave totals: l over every key lane; o per row, summed by the merge
+    WaveState<D> ws;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        l[h] = wave_sum(l[h]);
-        *reinterpret_cast<f32x4*>(&sh.o[wave][kq][h][dl * 8]) = f32x4{o[h][0], o[h][1], o[h][2], o[h][3]};
-        *reinterpret_cast<f32x4*>(&sh.o[wave][kq][h][dl * 8 + 4]) = f32x4{o[h][4], o[h][5], o[h][6], o[h][7]};
-    }
-    if (lane == 0) {
+    for (int db = 0; db < D / 16; ++db) ws.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ws.m = -INFINITY;
+    ws.l = 0.f;
+    wait_all_vm();  // the item's inputs (block ids, q) are in
+    wave_tiles<D>(w, ws);
+
+    // ---- wave totals: the sum over the head's four lane groups; O^T rows to LDS
+    float l = ws.l + __shfl_xor(ws.l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    const int h = lane & 15, j = lane >> 4;
+    if (h < G) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            sh.m[wave][h] = m[h];
-            sh.l[wave][h] = l[h];
+        for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4*>(&sh.o[wave][h][16 * db + 4 * j]) = ws.acc[db];
+        if (j == 0) {
+            sh.m[wave][h] = ws.m;
+            sh.l[wave][h] = l;
         }
     }
     __syncthreads();
@@ -403,26 +486,21 @@ __device__ void decode_item(const DecodeKernelArgs& p, DecodeShared<D, G>& sh, i
     constexpr int kElems = elems_per_thread<D, G>();
     const int e0 = threadIdx.x * kElems;
     const bool active = e0 < G * D;  // fewer outputs than threads when G * D < 256
-    const int h = active ? e0 / D : 0, d0 = active ? e0 % D : 0;
+    const int hh = active ? e0 / D : 0, d0 = active ? e0 % D : 0;
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) mx = fmaxf(mx, sh.m[w][h]);
+    for (int v = 0; v < kDecodeWaves; ++v) mx = fmaxf(mx, sh.m[v][hh]);
     float den = 0.f, val[kElems];
 #pragma unroll
     for (int k = 0; k < kElems; ++k) val[k] = 0.f;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-        const float sc = sh.m[w][h] == -INFINITY ? 0.f : fast_exp2(sh.m[w][h] - mx);  // a wave without keys adds 0
-        den += sh.l[w][h] * sc;
+    for (int v = 0; v < kDecodeWaves; ++v) {
+        const float sc = sh.m[v][hh] == -INFINITY ? 0.f : fast_exp2(sh.m[v][hh] - mx);  // a wave without keys adds 0
+        den += sh.l[v][hh] * sc;
 #pragma unroll
-        for (int k = 0; k < kElems; ++k) {
-            float rows = 0.f;
-#pragma unroll
-            for (int r = 0; r < DecodeShared<D, G>::kRows; ++r) rows += sh.o[w][r][h][d0 + k];
-            val[k] += rows * sc;
-        }
+        for (int k = 0; k < kElems; ++k) val[k] += sh.o[v][hh][d0 + k] * sc;
     }
-    const int qh = g * G + h;
+    const int qh = g * G + hh;
     const float inv = 1.f / den;
     if (nchunks == 1) {
         uint16_t* dst = a.out + ((int64_t)s * Hq + qh) * D + d0;
@@ -441,9 +519,28 @@ __device__ void decode_item(const DecodeKernelArgs& p, DecodeShared<D, G>& sh, i
     __syncthreads();  // LDS is reused by the next item
 }
 
-template <int D, int G, bool kWholeStep>
+template <int D, int G>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeKernelArgs p, int32_t* prefix_out) {
     __shared__ DecodeShared<D, G> sh;
+    __shared__ __attribute__((aligned(16))) uint16_t sK0[kDecodeWaves * kTileKeys * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sK1[kDecodeWaves * kTileKeys * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sK2[kDecodeWaves * kTileKeys * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sK3[kDecodeWaves * kTileKeys * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sV0[kDecodeWaves * kTileKeys * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sV1[kDecodeWaves * kTileKeys * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sV2[kDecodeWaves * kTileKeys * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sV3[kDecodeWaves * kTileKeys * D];
+    static_assert(kStages == 4, "four stage arrays");
+    Stages<D> st;
+    st.k[0] = sK0;
+    st.k[1] = sK1;
+    st.k[2] = sK2;
+    st.k[3] = sK3;
+    st.v[0] = sV0;
+    st.v[1] = sV1;
+    st.v[2] = sV2;
+    st.v[3] = sV3;
+
     const int S = p.a.num_seqs;
     const int Hq = p.a.num_q_heads;
     const int Hkv = p.a.num_kv_heads;
@@ -456,13 +553,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeKernelArgs
         idx /= Hkv;
         const int s = idx % S;
         const int c = idx / S;
-        const ItemInputs<D, G> in = load_item_inputs<D, G>(p, s, g, c);  // before the exit test: one round trip
+        const ItemInputs<D> in = load_item_inputs<D, G>(p, s, g, c);  // before the exit test: one round trip
         const int L = clamp_len(in.L_raw, cap);
         const int n = num_chunks(L, p.chunk);
         if (L == 0 && c == 0)  // a sequence without keys: zero rows
             for (int e = threadIdx.x; e < G * D; e += kDecodeThreads) p.a.out[((int64_t)s * Hq + g * G) * D + e] = 0;
         if (c >= n) return;
-        decode_item<D, G, kWholeStep>(p, sh, s, g, c, n, (int64_t)s * p.max_chunks + c, in);
+        decode_item<D, G>(p, sh, st, s, g, c, n, (int64_t)s * p.max_chunks + c, in);
         return;
     }
 
@@ -490,20 +587,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeKernelArgs
         }
         const int n = s_prefix[lo + 1] - s_prefix[lo];
         const int c = chunk - s_prefix[lo];
-        decode_item<D, G, kWholeStep>(p, sh, lo, g, c, n, chunk, load_item_inputs<D, G>(p, lo, g, c));
+        decode_item<D, G>(p, sh, st, lo, g, c, n, chunk, load_item_inputs<D, G>(p, lo, g, c));
     }
 }
 
-template <int D, int G, bool kWholeStep>
-hipError_t launch_grid(const DecodeKernelArgs& kp, int32_t* prefix, hipStream_t stream) {
+template <int D, int G>
+hipError_t launch_typed(const DecodeKernelArgs& kp, int32_t* prefix, hipStream_t stream) {
     const DecodeArgs& a = kp.a;
     if (!kp.persistent) {
         const int64_t blocks = (int64_t)kp.max_chunks * a.num_seqs * a.num_kv_heads;
-        hipLaunchKernelGGL((decode_kernel<D, G, kWholeStep>), dim3((unsigned)blocks), dim3(kDecodeThreads), 0, stream, kp, prefix);
+        hipLaunchKernelGGL((decode_kernel<D, G>), dim3((unsigned)blocks), dim3(kDecodeThreads), 0, stream, kp, prefix);
     } else {
         const size_t lds = sizeof(int32_t) * (size_t)(a.num_seqs + 1);
         int per_cu = 0;
-        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, G, kWholeStep>, kDecodeThreads, lds);
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, G>, kDecodeThreads, lds);
         if (e != hipSuccess) return e;
         if (per_cu < 1) per_cu = 1;
         const int64_t direct = (int64_t)a.num_seqs * kp.max_chunks;
@@ -512,21 +609,13 @@ hipError_t launch_grid(const DecodeKernelArgs& kp, int32_t* prefix, hipStream_t 
         int64_t resident = (int64_t)per_cu * device_cu_count() / kXcds * kXcds;
         if (resident < kXcds) resident = kXcds;
         if (blocks > resident) blocks = resident;
-        hipLaunchKernelGGL((decode_kernel<D, G, kWholeStep>), dim3((unsigned)blocks), dim3(kDecodeThreads), lds, stream, kp,
-                           prefix);
+        hipLaunchKernelGGL((decode_kernel<D, G>), dim3((unsigned)blocks), dim3(kDecodeThreads), lds, stream, kp, prefix);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || kp.max_chunks < 2) return e;  // no sequence has two chunks: nothing to merge
     hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3((unsigned)(a.num_seqs * a.num_kv_heads)),
                        dim3(kDecodeThreads), 0, stream, kp, (const int32_t*)prefix);
     return hipGetLastError();
-}
-
-template <int D, int G>
-hipError_t launch_typed(const DecodeKernelArgs& kp, int32_t* prefix, hipStream_t stream) {
-    // a 64-key step lies in one block when blocks hold >= 64 keys
-    if ((1 << kp.log2_block) >= kStepKeys) return launch_grid<D, G, true>(kp, prefix, stream);
-    return launch_grid<D, G, false>(kp, prefix, stream);
 }
 
 int ilog2(int x) {
@@ -543,16 +632,19 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
     const int64_t bound_tokens = (int64_t)num_seqs * max_seq_len;
     int64_t total = total_kv_tokens > 0 ? total_kv_tokens : bound_tokens;
     if (total > bound_tokens) total = bound_tokens;
-    // chunk: about 4 workgroups per CU-slot's worth of work, 256..8192 keys
+    // chunk: about 4 workgroups per CU-slot's worth of work, 256..kMaxChunk keys
     const int64_t key_heads = total * num_kv_heads;
-    int chunk = kDecodeWaves * kStepKeys;
-    while (chunk < 8192 && (int64_t)chunk * 2 * 4096 <= key_heads) chunk *= 2;
+    int chunk = kDecodeWaves * 4 * kTileKeys;
+    while (chunk < kMaxChunk && (int64_t)chunk * 2 * 4096 <= key_heads) chunk *= 2;
     pl.chunk = chunk;
     pl.max_chunks = (max_seq_len + chunk - 1) / chunk;
     const int64_t direct_items = (int64_t)num_seqs * pl.max_chunks;
     const int64_t real_items = (total + chunk - 1) / chunk + num_seqs;  // bound on chunks actually present
     // a direct grid when its empty workgroups are few (or the launch is small)
-    pl.persistent = (direct_items > 2 * real_items && direct_items * num_kv_heads > 4096) ? 1 : 0;
+    pl.persistent = (num_seqs <= kMaxPersistentSeqs && direct_items > 2 * real_items &&
+                     direct_items * num_kv_heads > 4096)
+                        ? 1
+                        : 0;
     pl.max_partials = pl.persistent ? (direct_items < real_items ? direct_items : real_items) : direct_items;
     auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
     pl.prefix_offset = 0;

@@ -63,18 +63,6 @@ __device__ __forceinline__ float dpp_rows(float old, float v) {
                                                                   kCtrl, kRowMask, 0xF, false));
 }
 
-// Combine every lane with lane ^ 32 (v_permlane32_swap: one VALU op, no LDS).
-__device__ __forceinline__ float max_with_lane_xor32(float x) {
-    const unsigned u = __builtin_bit_cast(unsigned, x);
-    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
-}
-__device__ __forceinline__ float sum_with_lane_xor32(float x) {
-    const unsigned u = __builtin_bit_cast(unsigned, x);
-    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
-}
-
 __device__ __forceinline__ float readlane(float v, int lane) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
