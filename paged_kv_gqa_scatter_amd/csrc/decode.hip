@@ -61,6 +61,8 @@ constexpr int kMaxTilesPerWave = 128;  // ids of a wave's tiles sit in two regis
 constexpr int kMaxChunk = kMaxTilesPerWave * kTileKeys * kDecodeWaves;
 constexpr int kMaxPersistentSeqs = 2048;  // chunk prefix kept in LDS
 constexpr int kXcds = 8;
+constexpr int kPlanCus = 256;        // compute units the split plan assumes (MI355X)
+constexpr int kRoundTripTiles = 12;  // a load round trip, in tile compute times
 constexpr float kRescaleSlack = 8.f;  // log2 of the largest weight a stale running max may give
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // the bf16 pair (1.0, 1.0)
 
@@ -632,10 +634,22 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
     const int64_t bound_tokens = (int64_t)num_seqs * max_seq_len;
     int64_t total = total_kv_tokens > 0 ? total_kv_tokens : bound_tokens;
     if (total > bound_tokens) total = bound_tokens;
-    // chunk: about 4 workgroups per CU-slot's worth of work, 256..kMaxChunk keys
-    const int64_t key_heads = total * num_kv_heads;
+    // chunk: the power of two in [256, kMaxChunk] with the least estimated
+    // time, counted in tile times: rounds of resident workgroups (one per CU
+    // at D = 128, two at D = 64, on a 256-CU part) times the round's length,
+    // a load round trip (about 12 tiles) plus the tiles each wave streams.
+    // The item count is a bound (each sequence adds at most one partial chunk).
+    const int64_t slots = (int64_t)kPlanCus * (head_dim == 64 ? 2 : 1);
     int chunk = kDecodeWaves * 4 * kTileKeys;
-    while (chunk < kMaxChunk && (int64_t)chunk * 2 * 4096 <= key_heads) chunk *= 2;
+    int64_t best = -1;
+    for (int c = chunk; c <= kMaxChunk; c *= 2) {
+        const int64_t items = ((total + c - 1) / c + num_seqs) * num_kv_heads;
+        const int64_t cost = (items + slots - 1) / slots * (kRoundTripTiles + c / (kDecodeWaves * kTileKeys));
+        if (best < 0 || cost < best) {
+            best = cost;
+            chunk = c;
+        }
+    }
     pl.chunk = chunk;
     pl.max_chunks = (max_seq_len + chunk - 1) / chunk;
     const int64_t direct_items = (int64_t)num_seqs * pl.max_chunks;
