@@ -4,7 +4,9 @@ Headline workload: one Qwen3-8B layer decode step -- 8 sequences, 32 query /
 8 KV heads, head_dim 128, bf16, 256-token blocks, cached context uniform in
 [512, 2048]; a step appends one token per sequence (kv_append) and decodes
 (paged_gqa_decode).  ``value`` is the decode KV-read rate: the unique K/V bytes
-a step must read, divided by the wall time per step.  Pool copies are rotated
+a step must read, divided by the wall time per step.  The step is captured in
+a HIP graph and replayed, as a serving loop replays its decode step (the
+eagerly launched step's time is reported beside it).  Pool copies are rotated
 (>= 1 GiB in total) so that every step reads from HBM, not from the 256 MB
 last-level cache.
 
@@ -12,7 +14,9 @@ The metric also names prefill: the Qwen3-8B causal prefill workload (4 prompts
 of 1024..4096 tokens) is timed in the same run and reported as causal TFLOP/s
 (4 * D * Hq flops per unmasked query/key pair) under ``prefill``.  Decode at a
 bandwidth-bound scale (3.24 GB of unique K/V, shared prefixes and 32K-token
-sequences) is reported under ``long_context_decode``.
+sequences) is reported under ``long_context_decode``, and the mixed
+continuous-batching step (64 decodes + two 512-row chunks) under
+``mixed_step``.
 
 Kernel durations are measured with HIP events on the stream the kernels run
 on; ``roofline`` relates the decode call to HBM peak, ``prefill.roofline`` the
@@ -46,10 +50,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=3000)
-    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--prefill-steps", type=int, default=50)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long", action="store_true", help="skip the long-context decode measurement")
+    ap.add_argument("--no-mixed", action="store_true", help="skip the mixed continuous-batching step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile-pass", action="store_true",
                     help="for counter runs: a few untimed steps of each kernel plus a reference device copy, no JSON")
@@ -124,7 +129,30 @@ def traffic_record(op: str):
     return None
 
 
+def _timed_replays(graphs, n, warmup):
+    """Mean ms per replay of `n` graph replays (cycling over `graphs`),
+    bracketed by events on the current stream after `warmup` replays."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(n):
+        graphs[i % len(graphs)].replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / n
+
+
 def time_decode_workload(args):
+    """The headline step: kv_append of one row per sequence, then the decode,
+    captured once per pool copy in a HIP graph (as a serving loop replays its
+    decode step).  Returns the step time, the decode call's time per launch
+    (its own graphs, replayed back to back) and the eagerly launched step's
+    time for context."""
     import torch
     from paged_kv_gqa_scatter_amd import workloads as W
     from paged_kv_gqa_scatter_amd.runner import DeviceCase
@@ -138,29 +166,52 @@ def time_decode_workload(args):
     step = dc.steps[0]
     stream = torch.cuda.current_stream()
 
-    def run(i, ev=None):
+    def eager(i):
         r = i % n_rot
         dc.append(step["append"], pool=r)
-        if ev is not None:
-            ev[0].record(stream)
         dc.decode(step["decode"], pool=r)
-        if ev is not None:
-            ev[1].record(stream)
 
-    for i in range(args.warmup):
-        run(i)
+    for i in range(min(args.warmup, 200)):
+        eager(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for i in range(args.steps):
-        run(i, evs[i])
+        eager(i)
     t1.record(stream)
     torch.cuda.synchronize()
-    step_ms = t0.elapsed_time(t1) / args.steps
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    return case, dec, kv_bytes, n_rot, step_ms, dec_ms
+    eager_ms = t0.elapsed_time(t1) / args.steps
+
+    steps = [dc.capture_step(0, pool=r) for r in range(n_rot)]
+    decodes = [dc.capture(lambda r=r: dc.decode(step["decode"], pool=r)) for r in range(n_rot)]
+    step_ms = _timed_replays(steps, args.steps, args.warmup)
+    dec_ms = _timed_replays(decodes, args.steps, max(args.warmup // 2, 10))
+    return case, dec, kv_bytes, n_rot, step_ms, dec_ms, eager_ms
+
+
+def time_mixed_step(args):
+    """The mixed continuous-batching step (one kv_append of 64 + 1024 rows,
+    a 64-sequence decode, two 512-row chunks on 1024 cached tokens), captured
+    in a HIP graph and replayed."""
+    import torch
+    from paged_kv_gqa_scatter_amd import workloads as W
+    from paged_kv_gqa_scatter_amd.runner import DeviceCase
+
+    case = W.config4_mixed()
+    st = case.steps[0]
+    kv_bytes = W.decode_unique_kv_bytes(case, st.decode)
+    flops = W.prefill_causal_flops(case, st.prefill)
+    dc = DeviceCase(case)
+    dc.run_fills()
+    g = dc.capture_step(0)
+    ms = _timed_replays([g], max(20, args.steps // 4), 20)
+    del g, dc
+    torch.cuda.empty_cache()
+    return {"workload": "qwen3-8b mixed step: 64 decode seqs (ctx log-uniform [128, 8192]) + 2 x 512-row chunks on "
+                        "1024 cached; 32q/8kv, d128, block 256; one HIP graph",
+            "ms": round(ms, 5), "decode_unique_kv_bytes": int(kv_bytes), "prefill_causal_flops": int(flops),
+            "decode_gbs_if_alone": round(kv_bytes / (ms * 1e-3) / 1e9, 2)}
 
 
 def time_prefill_workload(args):
@@ -176,9 +227,11 @@ def time_prefill_workload(args):
     step = dc.steps[0]
     dc.append(step["append"])
     stream = torch.cuda.current_stream()
-    for _ in range(3):
-        dc.prefill(step["prefill"])
-    torch.cuda.synchronize()
+    t = time.perf_counter()
+    while time.perf_counter() - t < 0.5:  # steady clocks
+        for _ in range(10):
+            dc.prefill(step["prefill"])
+        torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.prefill_steps)]
     for a, b in evs:
@@ -268,7 +321,7 @@ def main():
         profile_pass(args)
         return
 
-    case, dec, kv_bytes, n_rot, step_ms, dec_ms = time_decode_workload(args)
+    case, dec, kv_bytes, n_rot, step_ms, dec_ms, eager_ms = time_decode_workload(args)
     gbs = kv_bytes / (step_ms * 1e-3) / 1e9
     dec_gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
     line = {
@@ -287,7 +340,8 @@ def main():
         "config": {"workload": "qwen3-8b one-layer decode step: kv_append + paged_gqa_decode, 8 seqs, ctx U[512,2048], "
                                "32q/8kv heads, d128, block 256",
                    "seqs": int(dec.seq_lens.shape[0]), "keys": int(dec.seq_lens.sum()),
-                   "unique_kv_bytes": int(kv_bytes), "pool_copies_rotated": n_rot},
+                   "unique_kv_bytes": int(kv_bytes), "pool_copies_rotated": n_rot, "hip_graph": True,
+                   "eager_ms_per_step": round(eager_ms, 5)},
         "roofline": {"bound": "hbm", "kernel": "paged_gqa_decode (decode_kernel + decode_merge_kernel)",
                      "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": int(kv_bytes),
@@ -310,6 +364,8 @@ def main():
             line["prefill"]["roofline"]["traffic"] = int(prec["hbm_bytes_per_launch"])
     if not args.no_long:
         line["long_context_decode"] = time_long_decode(args)
+    if not args.no_mixed:
+        line["mixed_step"] = time_mixed_step(args)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, dec, kv_bytes, args.cpu_seconds)
     print(json.dumps(line), flush=True)

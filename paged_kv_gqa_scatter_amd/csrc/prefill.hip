@@ -17,14 +17,21 @@
 //    O^T += V^T P^T (keys as the contraction index), so they are packed to bf16
 //    in place.  V stays row-major in LDS and the V^T operand is read with
 //    ds_read_b64_tr_b16, the gfx950 transposing LDS read.
-//  * K/V tiles of 64 keys are gathered through the block table straight into
-//    LDS with global_load_lds_dwordx4 (no register staging), double-buffered:
-//    the loads of tile t+1 are in flight while tile t is computed.  The LDS
-//    tile is unpadded; 16-byte pieces are XOR-swizzled per row so that the
-//    K reads (16 rows, one piece) and the transposing V reads (4 rows, four
-//    pieces) hit distinct banks.  Rows past the last visible key load a copy
-//    of a visible row, so no unwritten (NaN) slot reaches the MFMA, and are
-//    excluded by the mask.
+//  * K/V tiles of 64 keys are copied from the pools straight into LDS with
+//    global_load_lds_dwordx4, double-buffered: the loads of tile t+1 are in
+//    flight while tile t is computed.  Wave w copies rows [16 w, 16 w + 16) of
+//    both tiles; as blocks hold at least 16 keys, those rows sit in one
+//    (block, KV head) slab, so the slab address is scalar arithmetic on a
+//    block id read with a scalar load one tile ahead, and every lane's offset
+//    within the slab is fixed for the whole workgroup.  The LDS tile is
+//    unpadded; 16-byte pieces are XOR-swizzled per row so that the K reads
+//    (16 rows, one piece) and the transposing V reads (4 rows, four pieces)
+//    hit distinct banks.  Every LDS read address is a per-lane register set
+//    up once plus a compile-time offset (stage, row block), so the tile loop
+//    spends no vector instructions on addressing.  Rows past the last visible
+//    key copy a visible row of the same slab (or are zero-filled when the
+//    wave's rows hold none), so no unwritten (NaN) slot reaches the MFMA;
+//    the causal mask excludes them.
 //  * Softmax in the exp2 domain with one FMA per score; the causal mask is
 //    applied only on tiles that cross a wave's diagonal; the output is rescaled
 //    only when a row maximum grows by more than 2^8 (the weights of a stale
@@ -32,8 +39,9 @@
 //    adds exactly the bf16-rounded weights the MFMA uses (dot with (1, 1)),
 //    keeping the output a true weighted average of V rows.
 //  * Causal tile skipping: a workgroup stops at its last query's position and
-//    a wave skips tiles that lie wholly after its rows.  Row r of a chunk of n
-//    rows on a sequence of length L is at position L - n + r.
+//    a wave skips tiles that lie wholly after its rows (and all compute when
+//    it has no rows of the chunk).  Row r of a chunk of n rows on a sequence
+//    of length L is at position L - n + r.
 //  * Launch order: the longest query tiles first, and the KV head in the low
 //    bits of the workgroup index, so that workgroups reading the same K/V land
 //    on the same XCD (workgroups are dealt round-robin over the 8 XCDs) and
@@ -50,12 +58,12 @@ constexpr int kPrefillThreads = 256;
 constexpr int kPrefillWaves = kPrefillThreads / kWave;
 constexpr int kTileQ = 128;  // query rows per workgroup (32 per wave)
 constexpr int kTileK = 64;   // keys per LDS tile
+constexpr int kWaveRows = kTileK / kPrefillWaves;  // tile rows each wave copies
 constexpr float kRescaleSlack = 8.f;             // log2 of the largest stale weight
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // the bf16 pair (1.0, 1.0)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 struct PrefillKernelArgs {
     PrefillArgs a;
@@ -74,106 +82,185 @@ __device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
     return __builtin_bit_cast(u32x2, t);
 }
 
-// Slot of 16-byte piece `piece` of LDS tile row `row` (D/8 pieces per row).
-// The XOR key maps the 16 rows a K read touches (same piece) to 16 different
-// slots, and gives each of the 4 consecutive rows a transposing V read
-// touches (4 pieces) its own group of 4 slots, so neither read has two lanes
-// on one bank.
+// Slot of 16-byte piece `piece` of LDS tile row `row` (D/8 pieces per row);
+// it depends on row % 16 only.  The XOR key maps the 16 rows a K read touches
+// (same piece) to 16 different slots, and gives each of the 4 consecutive rows
+// a transposing V read touches (4 pieces) its own group of 4 slots, so neither
+// read has two lanes on one bank.  An involution: it also names the piece a
+// slot holds.
 template <int D>
 __device__ __forceinline__ int swizzle(int row, int piece) {
     constexpr int kPieces = D / 8;
     return piece ^ ((((row & 3) << 2) | ((row >> 2) & 3)) & (kPieces - 1));
 }
 
-// Rows of a 64-key tile this wave moves into LDS: rows [16 w, 16 w + 16),
-// kLoads wave loads of kRowsPerLoad rows each.
-template <int D>
-struct TileShare {
-    static constexpr int kPieces = D / 8;  // 16-byte pieces per row
-    static constexpr int kRowsPerLoad = kWave / kPieces;
-    static constexpr int kLoads = kTileK / kPrefillWaves / kRowsPerLoad;
-};
-
-// Block ids of this lane's rows of the tile starting at key kt (read one tile
-// ahead, so that no table load sits between the LDS-bound loads).  Rows at or
-// past kend stand in for row kend - 1, a written row; the mask excludes them.
-template <int D>
-__device__ __forceinline__ void tile_blocks(const PrefillKernelArgs& p, const int32_t* table, int kt, int kend,
-                                            int wave, int lane, int (&blk)[TileShare<D>::kLoads]) {
-    using T = TileShare<D>;
-#pragma unroll
-    for (int i = 0; i < T::kLoads; ++i) {
-        const int row = wave * (kTileK / kPrefillWaves) + i * T::kRowsPerLoad + lane / T::kPieces;
-        const int key = min(kt + row, kend - 1);
-        blk[i] = table[key >> p.log2_block];
-    }
+// LDS byte address of a __shared__ object (what M0 holds for an LDS DMA).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// This wave's share of one K/V tile, straight from the pools into LDS.
+// global_load_lds_dwordx4 with a scalar base: lane l's 16 bytes at
+// base + voff land at LDS byte address lds + 16 l.  Inline asm, so that the
+// compiler does not wait for the copies in flight before unrelated LDS reads;
+// the loop waits for them explicitly (vmcnt) before its barrier.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+
+// This wave's index, known to the compiler to be the same on every lane.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// What a lane does in the copies and the LDS reads, fixed for the workgroup.
 template <int D>
-__device__ __forceinline__ void load_tile(const PrefillKernelArgs& p, int g, int kt, int kend,
-                                          const int (&blk)[TileShare<D>::kLoads], uint16_t* sK, uint16_t* sV, int wave,
-                                          int lane) {
-    using T = TileShare<D>;
-    const PrefillArgs& a = p.a;
-    const int B = 1 << p.log2_block;
-    const int64_t tile = (int64_t)B * D;
+struct Lanes {
+    static constexpr int kPieces = D / 8;               // 16-byte pieces per row
+    static constexpr int kRowsPerLoad = kWave / kPieces;
+    static constexpr int kLoads = kWaveRows / kRowsPerLoad;  // wave loads per matrix and tile
+    int row[kLoads];          // copy: row (within the wave's 16) of this lane's 16 bytes
+    uint32_t voff[kLoads];    // copy: byte offset of those 16 bytes in the wave's rows of the slab
+    int koff[D / 16];         // QK: element offset of this lane's K fragment in a stage, per 16 dims
+    int voff_lo[D / 32];      // PV: element offset of this lane's transposing V reads, per 32 dims
+    int voff_hi[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ Lanes<D> lanes(int lane) {
+    using L = Lanes<D>;
+    Lanes<D> ln;
 #pragma unroll
-    for (int i = 0; i < T::kLoads; ++i) {
-        const int row0 = wave * (kTileK / kPrefillWaves) + i * T::kRowsPerLoad;  // first row of this wave load
-        const int row = row0 + lane / T::kPieces;
-        const int piece = swizzle<D>(row, lane % T::kPieces);  // the piece this lane's LDS slot holds
-        const int key = min(kt + row, kend - 1);
-        const int b = (unsigned)blk[i] < (unsigned)a.num_blocks ? blk[i] : 0;
-        const int64_t off = ((int64_t)b * a.num_kv_heads + g) * tile + (int64_t)(key & (B - 1)) * D + piece * 8;
-        __builtin_amdgcn_global_load_lds(a.k_pool + off, (lds_void*)(sK + row0 * D), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(a.v_pool + off, (lds_void*)(sV + row0 * D), 16, 0, 0);
+    for (int i = 0; i < L::kLoads; ++i) {
+        const int r = i * L::kRowsPerLoad + lane / L::kPieces;
+        ln.row[i] = r;
+        ln.voff[i] = (uint32_t)(r * D + swizzle<D>(r, lane % L::kPieces) * 8) * 2u;
     }
+    const int half = lane >> 5, r32 = lane & 31;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) ln.koff[ks] = r32 * D + swizzle<D>(r32, ks * 2 + half) * 8;
+    const int vrow = half * 4 + ((lane & 15) >> 2);
+    const int dq = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;  // column within a 32-wide block
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+        const int d = i * 32 + dq;
+        ln.voff_lo[i] = vrow * D + swizzle<D>(vrow, d >> 3) * 8 + (d & 7);
+        ln.voff_hi[i] = (vrow + 8) * D + swizzle<D>(vrow + 8, d >> 3) * 8 + (d & 7);
+    }
+    return ln;
 }
 
 // Per-workgroup constants of the tile loop.
-struct RowState {
-    int g, kend, ntiles, wave, lane, half, qpos, wave_qpos_min, wave_qpos_max;
+template <int D>
+struct Loop {
+    const PrefillKernelArgs* p;
     const int32_t* table;
-    float c;
+    int g, kend, ntiles, wave, lane, qpos, wave_qpos_min, wave_qpos_max;
+    bool wave_rows;   // the wave holds at least one row of the chunk
+    float c;          // scale * log2 e
+    uint16_t* lds;    // [2 stages][K tile, V tile][kTileK][D]
+    Lanes<D> ln;
 };
 
-// One tile of the loop: wait for tile t (stage kCur), start tile t+1 into the
-// other stage, then compute tile t.  The stage is a template argument so the
-// two stages are distinct LDS objects and the compiler need not wait for the
-// loads in flight into one stage before reading the other.
-template <int D, int kCur>
-__device__ __forceinline__ void tile_step(const PrefillKernelArgs& p, const RowState& rs, int t, uint16_t* sKcur,
-                                          uint16_t* sVcur, uint16_t* sKnext, uint16_t* sVnext,
-                                          int (&blk)[TileShare<D>::kLoads], const u32x4 (&qreg)[D / 16],
+template <int D>
+constexpr int stage_elems() { return 2 * kTileK * D; }
+
+// Block ids of the slabs holding this wave's rows, a window of 64 tiles at a
+// time: lane l holds the id for tile win + l, and a tile's id is read with
+// v_readlane.  The window is refilled (one vector load and a wait) only when
+// no copy is in flight, so no per-tile memory access waits behind the tile
+// copies (vector-memory waits are in issue order).
+struct BlockIds {
+    int ids;
+    int win;
+};
+
+template <int D>
+__device__ __forceinline__ void fill_ids(const Loop<D>& lp, BlockIds& bi, int t) {
+    bi.win = t & ~(kWave - 1);
+    const int key = (bi.win + lp.lane) * kTileK + lp.wave * kWaveRows;
+    const int idx = min(key >> lp.p->log2_block, lp.p->a.max_blocks_per_seq - 1);
+    bi.ids = lp.table[idx];
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), seen by the compiler
+}
+
+template <int D>
+__device__ __forceinline__ int tile_block(const Loop<D>& lp, BlockIds& bi, int t) {
+    if (t - bi.win >= kWave) fill_ids<D>(lp, bi, t);
+    return __builtin_amdgcn_readlane(bi.ids, t - bi.win);
+}
+
+// Copy this wave's rows of tile kt (K and V) into a stage.  Rows at or past
+// kend repeat row kend - 1 of the same slab; a wave with no visible row
+// writes zeros instead.
+template <int D>
+__device__ __forceinline__ void copy_tile(const Loop<D>& lp, int kt, int blk, uint16_t* stage) {
+    using L = Lanes<D>;
+    const PrefillArgs& a = lp.p->a;
+    const int r0 = kt + lp.wave * kWaveRows;  // first key of this wave's rows
+    uint16_t* sk = stage + lp.wave * kWaveRows * D;
+    uint16_t* sv = sk + kTileK * D;
+    const int visible = lp.kend - r0;
+    if (visible <= 0) {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < L::kLoads; ++i) {
+            *reinterpret_cast<u32x4*>(sk + i * L::kRowsPerLoad * D + lp.lane * 8) = zero;
+            *reinterpret_cast<u32x4*>(sv + i * L::kRowsPerLoad * D + lp.lane * 8) = zero;
+        }
+        return;
+    }
+    const int B = 1 << lp.p->log2_block;
+    const int b = (unsigned)blk < (unsigned)a.num_blocks ? blk : 0;  // a bad id reads block 0
+    const int64_t slab = (((int64_t)b * a.num_kv_heads + lp.g) << lp.p->log2_block) * D + (int64_t)(r0 & (B - 1)) * D;
+    const uint16_t* kb = a.k_pool + slab;
+    const uint16_t* vb = a.v_pool + slab;
+    const uint32_t lk = lds_addr(sk), lv = lds_addr(sv);
+    if (visible >= kWaveRows) {
+#pragma unroll
+        for (int i = 0; i < L::kLoads; ++i) {
+            dma16(kb, lp.ln.voff[i], lk + i * kWave * 16);
+            dma16(vb, lp.ln.voff[i], lv + i * kWave * 16);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < L::kLoads; ++i) {
+            const int shift = lp.ln.row[i] >= visible ? (lp.ln.row[i] - visible + 1) * D * 2 : 0;
+            dma16(kb, lp.ln.voff[i] - shift, lk + i * kWave * 16);
+            dma16(vb, lp.ln.voff[i] - shift, lv + i * kWave * 16);
+        }
+    }
+}
+
+// One tile: wait for tile t (stage kCur), start tile t+1 into the other
+// stage, then compute tile t.
+template <int D, int kCur, bool kNegScale>
+__device__ __forceinline__ void tile_step(const Loop<D>& lp, int t, BlockIds& bi, const u32x4 (&qreg)[D / 16],
                                           f32x16 (&acc)[D / 32], float& m, float& lsum) {
     const int kt = t * kTileK;
-    const int lane = rs.lane, half = rs.half;
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt(0): this wave's part of tile t (and the next ids) arrived
-    __syncthreads();                     // every part is; the other stage is free
-    if (t + 1 < rs.ntiles) {
-        load_tile<D>(p, rs.g, kt + kTileK, rs.kend, blk, sKnext, sVnext, rs.wave, lane);
-        if (t + 2 < rs.ntiles) tile_blocks<D>(p, rs.table, kt + 2 * kTileK, rs.kend, rs.wave, lane, blk);
+    const int lane = lp.lane;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies of tile t arrived
+    __syncthreads();                                    // every wave's have; the other stage is free
+    if (t + 1 < lp.ntiles) {
+        copy_tile<D>(lp, kt + kTileK, tile_block<D>(lp, bi, t + 1), lp.lds + (kCur ^ 1) * stage_elems<D>());
     }
-    if (kt > rs.wave_qpos_max) return;  // every key of this tile is after this wave's rows
-    const float c = rs.c;
+    if (!lp.wave_rows || kt > lp.wave_qpos_max) return;  // every key of this tile is after this wave's rows
+    const float c = lp.c;
+    const uint16_t* sk = lp.lds + kCur * stage_elems<D>();
+    const uint16_t* sv = sk + kTileK * D;
 
-    // S^T = K Q^T for two 32-key blocks
+    // S^T = K Q^T for the two 32-key halves of the tile, interleaved
     f32x16 st[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int r = 0; r < 16; ++r) st[0][r] = st[1][r] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
-        const int row = kb * 32 + (lane & 31);
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            const u32x4 kf = *reinterpret_cast<const u32x4*>(sKcur + row * D + swizzle<D>(row, ks * 2 + half) * 8);
-            st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qreg[ks]), st[kb], 0, 0, 0);
-        }
+    for (int ks = 0; ks < D / 16; ++ks) {
+        const u32x4 k0 = *reinterpret_cast<const u32x4*>(sk + lp.ln.koff[ks]);
+        const u32x4 k1 = *reinterpret_cast<const u32x4*>(sk + lp.ln.koff[ks] + 32 * D);
+        st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), as_bf16x8(qreg[ks]), st[0], 0, 0, 0);
+        st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), as_bf16x8(qreg[ks]), st[1], 0, 0, 0);
     }
 
     // scores -> exp2 domain; mask only where the tile crosses this wave's diagonal
-    const bool diag = kt + kTileK - 1 > rs.wave_qpos_min;
+    const int half = lane >> 5;
+    const bool diag = kt + kTileK - 1 > lp.wave_qpos_min;
     float mt;
     if (diag) {
         mt = -INFINITY;
@@ -182,20 +269,17 @@ __device__ __forceinline__ void tile_step(const PrefillKernelArgs& p, const RowS
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = kt + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-                const float z = key <= rs.qpos ? st[kb][r] * c : -INFINITY;
+                const float z = key <= lp.qpos ? st[kb][r] * c : -INFINITY;
                 st[kb][r] = z;
                 mt = fmaxf(mt, z);
             }
     } else {
-        float hi = st[0][0], lo = st[0][0];
+        float e = st[0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                hi = fmaxf(hi, st[kb][r]);
-                lo = fminf(lo, st[kb][r]);
-            }
-        mt = c >= 0.f ? hi * c : lo * c;
+            for (int r = 0; r < 16; ++r) e = kNegScale ? fminf(e, st[kb][r]) : fmaxf(e, st[kb][r]);
+        mt = e * c;
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
     // rescale only when a row maximum outgrows the stale one by 2^8
@@ -233,13 +317,11 @@ __device__ __forceinline__ void tile_step(const PrefillKernelArgs& p, const RowS
                 pb[i] = pack_bf16x2(st[kb][sub * 8 + 2 * i], st[kb][sub * 8 + 2 * i + 1]);
                 ps = dot2_bf16(pb[i], kOnesBf16x2, ps);
             }
-            const int row = kb * 32 + sub * 16 + half * 4 + ((lane & 15) >> 2);
-            const int dq = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;  // column within a 32-wide block
+            const uint16_t* v16 = sv + (kb * 32 + sub * 16) * D;
 #pragma unroll
             for (int i = 0; i < D / 32; ++i) {
-                const int d = i * 32 + dq;
-                const u32x2 lo = lds_read_tr(sVcur + row * D + swizzle<D>(row, d >> 3) * 8 + (d & 7));
-                const u32x2 hi = lds_read_tr(sVcur + (row + 8) * D + swizzle<D>(row + 8, d >> 3) * 8 + (d & 7));
+                const u32x2 lo = lds_read_tr(v16 + lp.ln.voff_lo[i]);
+                const u32x2 hi = lds_read_tr(v16 + lp.ln.voff_hi[i]);
                 const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
                 acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pb), acc[i], 0, 0, 0);
             }
@@ -247,12 +329,9 @@ __device__ __forceinline__ void tile_step(const PrefillKernelArgs& p, const RowS
     lsum += ps;
 }
 
-template <int D>
+template <int D, bool kNegScale>
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillKernelArgs p) {
-    __shared__ __attribute__((aligned(16))) uint16_t sK0[kTileK * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sV0[kTileK * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sK1[kTileK * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sV1[kTileK * D];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * stage_elems<D>()];
     const PrefillArgs& a = p.a;
 
     // workgroup -> (query tile, sequence, query head); KV head in the low bits
@@ -275,14 +354,25 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillKern
     L = L < 0 ? 0 : (L > cap ? cap : L);
     const int ctx = L - n;  // cached keys before the chunk
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+    const int lane = threadIdx.x & 63, wave = wave_id(), half = lane >> 5;
     const int qrow = tile * kTileQ + wave * 32 + (lane & 31);  // this lane's query row in the chunk
-    const int qpos = ctx + qrow;                                // its absolute position
-    const int wave_qpos_min = ctx + tile * kTileQ + wave * 32;
-    const int wave_qpos_max = ctx + min(tile * kTileQ + wave * 32 + 31, n - 1);
-    const int kend = min(L, ctx + min((tile + 1) * kTileQ, n));  // keys this workgroup may see: [0, kend)
-    const int32_t* table = a.block_table + (int64_t)s * a.max_blocks_per_seq;
-    const float c = p.qk_scale_log2;
+    const int wave_row0 = tile * kTileQ + wave * 32;
+
+    Loop<D> lp;
+    lp.p = &p;
+    lp.table = a.block_table + (int64_t)s * a.max_blocks_per_seq;
+    lp.g = g;
+    lp.kend = min(L, ctx + min((tile + 1) * kTileQ, n));  // keys this workgroup may see: [0, kend)
+    lp.ntiles = lp.kend > 0 ? (lp.kend + kTileK - 1) / kTileK : 0;
+    lp.wave = wave;
+    lp.lane = lane;
+    lp.qpos = ctx + qrow;  // this lane's absolute position
+    lp.wave_qpos_min = ctx + wave_row0;
+    lp.wave_qpos_max = ctx + min(wave_row0 + 31, n - 1);
+    lp.wave_rows = wave_row0 < n;
+    lp.c = p.qk_scale_log2;
+    lp.lds = lds;
+    lp.ln = lanes<D>(lane);
 
     u32x4 qreg[D / 16];
     {
@@ -291,6 +381,11 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillKern
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) qreg[ks] = qrow < n ? load16(qp + ks * 16) : zero;
     }
+    // Wait for q here, in a form the compiler's wait placement sees: the
+    // tile copies are inline asm it cannot track, so otherwise it would keep
+    // a full vector-memory wait before the first MFMA of every tile, which
+    // would also wait for the next tile's copies.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
     f32x16 acc[D / 32];
 #pragma unroll
@@ -299,33 +394,21 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillKern
         for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
     float m = -INFINITY, lsum = 0.f;
 
-    RowState rs;
-    rs.g = g;
-    rs.kend = kend;
-    rs.ntiles = kend > 0 ? (kend + kTileK - 1) / kTileK : 0;
-    rs.wave = wave;
-    rs.lane = lane;
-    rs.half = half;
-    rs.qpos = qpos;
-    rs.wave_qpos_min = wave_qpos_min;
-    rs.wave_qpos_max = wave_qpos_max;
-    rs.table = table;
-    rs.c = c;
-    int blk[TileShare<D>::kLoads];
-    if (rs.ntiles > 0) {
-        tile_blocks<D>(p, table, 0, kend, wave, lane, blk);
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        load_tile<D>(p, g, 0, kend, blk, sK0, sV0, wave, lane);
-        if (rs.ntiles > 1) tile_blocks<D>(p, table, kTileK, kend, wave, lane, blk);
+    BlockIds bi;
+    bi.ids = 0;
+    bi.win = 0;
+    if (lp.ntiles > 0) {
+        fill_ids<D>(lp, bi, 0);
+        copy_tile<D>(lp, 0, tile_block<D>(lp, bi, 0), lds);
     }
-    for (int t = 0; t < rs.ntiles; t += 2) {
-        tile_step<D, 0>(p, rs, t, sK0, sV0, sK1, sV1, blk, qreg, acc, m, lsum);
-        if (t + 1 < rs.ntiles) tile_step<D, 1>(p, rs, t + 1, sK1, sV1, sK0, sV0, blk, qreg, acc, m, lsum);
+    for (int t = 0; t < lp.ntiles; t += 2) {
+        tile_step<D, 0, kNegScale>(lp, t, bi, qreg, acc, m, lsum);
+        if (t + 1 < lp.ntiles) tile_step<D, 1, kNegScale>(lp, t + 1, bi, qreg, acc, m, lsum);
     }
 
     lsum += __shfl_xor(lsum, 32, kWave);
     if (qrow >= n) return;
-    const float inv = (qpos >= 0 && lsum > 0.f) ? 1.f / lsum : 0.f;  // a row with no key is zero
+    const float inv = (lp.qpos >= 0 && lsum > 0.f) ? 1.f / lsum : 0.f;  // a row with no key is zero
     uint16_t* op = a.out + ((int64_t)(q0 + qrow) * Hq + h) * D;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i)
@@ -344,6 +427,14 @@ int ilog2(int x) {
     return r;
 }
 
+template <int D>
+void launch_d(const PrefillKernelArgs& kp, int64_t blocks, hipStream_t stream) {
+    if (kp.qk_scale_log2 < 0.f)
+        hipLaunchKernelGGL((prefill_kernel<D, true>), dim3((unsigned)blocks), dim3(kPrefillThreads), 0, stream, kp);
+    else
+        hipLaunchKernelGGL((prefill_kernel<D, false>), dim3((unsigned)blocks), dim3(kPrefillThreads), 0, stream, kp);
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
@@ -356,9 +447,9 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     kp.qk_scale_log2 = a.scale * kLog2e;
     const int64_t blocks = (int64_t)kp.q_tiles * a.num_seqs * a.num_q_heads;
     if (a.head_dim == 128)
-        hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)blocks), dim3(kPrefillThreads), 0, stream, kp);
+        launch_d<128>(kp, blocks, stream);
     else
-        hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)blocks), dim3(kPrefillThreads), 0, stream, kp);
+        launch_d<64>(kp, blocks, stream);
     return hipGetLastError();
 }
 

@@ -153,6 +153,27 @@ class DeviceCase:
             res["prefill"] = self.prefill(st["prefill"], pool)
         return res
 
+    def capture(self, fn) -> "torch.cuda.CUDAGraph":
+        """Record what ``fn()`` launches on the current stream into a HIP
+        graph (torch.cuda.CUDAGraph); ``replay()`` reruns it with the same
+        buffers.  The library's calls allocate nothing, synchronise nothing and
+        clear nothing with memset, so a whole step can be captured; ``fn`` runs
+        once eagerly first, on a side stream, as torch's capture requires."""
+        cur = torch.cuda.current_stream()
+        side = torch.cuda.Stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            fn()
+        cur.wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    def capture_step(self, i: int, pool: int = 0) -> "torch.cuda.CUDAGraph":
+        """A HIP graph of step ``i`` (append, then decode and/or prefill)."""
+        return self.capture(lambda: self.run_step(i, pool))
+
     def run_all(self) -> list:
         """Fills, then every step in order; returns each step's outputs as fp64 numpy."""
         self.run_fills(0)

@@ -274,3 +274,36 @@ def test_chunked_equals_unchunked(orc):
     a = _dev()(whole).run_all()[0]["prefill"][1024:]
     b = _dev()(chunk).run_all()[0]["prefill"]
     compare(b, a, "chunk vs whole rows 1024..1535")
+
+
+# ---------------------------------------------------------------- HIP graphs
+
+def test_graph_replays_match_eager(orc):
+    # the mixed step (one append, a 64-sequence decode, two 512-row chunks)
+    # captured in a HIP graph: every replay, with eager calls and
+    # synchronisations between replays, equals the eager step bit for bit
+    case = W.config4_mixed()
+    _say(f"case {case.name}: graph replays vs eager")
+    dc = _dev()(case)
+    dc.run_fills()
+    st = dc.steps[0]
+    eager = dc.run_step(0)
+    torch.cuda.synchronize()
+    want = {k: v.clone() for k, v in eager.items()}
+    ref, _ = oracle_outputs(case, orc)
+    compare(_f64(want["decode"]), ref[0]["decode"], "eager decode")
+    compare(_f64(want["prefill"]), ref[0]["prefill"], "eager prefill")
+    g = dc.capture_step(0)
+    for rep in range(4):
+        st["decode"].out.zero_()
+        st["prefill"].out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in ("decode", "prefill"):
+            got = st[k].out
+            assert torch.equal(got.view(torch.int16), want[k].view(torch.int16)), f"replay {rep}: {k} differs"
+        dc.decode(st["decode"])  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(st["decode"].out.view(torch.int16), want["decode"].view(torch.int16))
+    _say("  4 replays bit-identical to the eager step")
