@@ -13,6 +13,9 @@
  *                        chunked prefill on "从零搭建AI工程能力：手写KV Cache与
  *                        动态批处理实战" section 3.3).
  *
+ * plus pkv_paged_gqa_decode_append, a decode step's append and decode in one
+ * launch.
+ *
  * Attention is softmax(Q K^T * scale) V with an inclusive causal mask, as
  * "从零手搓AI推理引擎：避开调包陷阱的工程实践指南" section 2.2 defines it.
  *
@@ -140,6 +143,32 @@ int32_t pkv_paged_gqa_decode(uint16_t* out, const uint16_t* q,
                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
                              float scale, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/*
+ * paged_gqa_decode_append: one decode step in one launch -- kv_append of one
+ * new K/V row per sequence followed by paged_gqa_decode (the same two steps
+ * the engine of "扔掉 vLLM！从零构建 Qwen3-8B 推理引擎" sections 4.3.1 and
+ * 4.4.2 runs per generated token).
+ *
+ *   k_new, v_new     [num_seqs][num_kv_heads][head_dim] bf16: the row of
+ *                    position seq_lens[s] - 1 of each sequence (a sequence
+ *                    with seq_lens[s] == 0 appends nothing and yields zeros)
+ *   k_pool, v_pool   written at that position (bit copies, as kv_append)
+ *   other arguments  as for pkv_paged_gqa_decode (same workspace size)
+ *
+ * The outputs equal pkv_kv_append followed by pkv_paged_gqa_decode up to
+ * summation order.  Preconditions as for both: the new rows' slots belong to
+ * their sequence alone (no other sequence's table maps that slot).
+ */
+int32_t pkv_paged_gqa_decode_append(uint16_t* out, const uint16_t* q,
+                                    const uint16_t* k_new, const uint16_t* v_new,
+                                    uint16_t* k_pool, uint16_t* v_pool,
+                                    const int32_t* block_table, int32_t max_blocks_per_seq,
+                                    const int32_t* seq_lens, int32_t max_seq_len, int64_t total_kv_tokens,
+                                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                    float scale, void* workspace, size_t workspace_bytes,
+                                    void* stream);
 
 /*
  * paged_gqa_prefill: causal attention for a chunk of q_len_s query rows per

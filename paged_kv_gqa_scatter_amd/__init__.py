@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 STATUS = {0: "PKV_OK", 1: "PKV_ERR_NULL_POINTER", 2: "PKV_ERR_BAD_SHAPE", 3: "PKV_ERR_MISALIGNED",
           4: "PKV_ERR_WORKSPACE", 5: "PKV_ERR_HIP"}
 EXPORTS = ("pkv_abi_version", "pkv_status_string", "pkv_kv_append", "pkv_decode_workspace_bytes",
-           "pkv_paged_gqa_decode", "pkv_paged_gqa_prefill")
+           "pkv_paged_gqa_decode", "pkv_paged_gqa_decode_append", "pkv_paged_gqa_prefill")
 
 
 class PkvError(RuntimeError):
@@ -50,6 +50,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I64]
     lib.pkv_paged_gqa_decode.restype = I32
     lib.pkv_paged_gqa_decode.argtypes = [P, P, P, P, P, I32, P, I32, I64, I32, I32, I32, I32, I32, I32, F32, P, SZ, P]
+    lib.pkv_paged_gqa_decode_append.restype = I32
+    lib.pkv_paged_gqa_decode_append.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I64, I32, I32, I32, I32, I32, I32,
+                                                F32, P, SZ, P]
     lib.pkv_paged_gqa_prefill.restype = I32
     lib.pkv_paged_gqa_prefill.argtypes = [P, P, P, I32, I32, P, P, P, I32, P, I32, I32, I32, I32, I32, I32, I32,
                                           F32, P]
@@ -159,6 +162,43 @@ def paged_gqa_decode(q, k_pool, v_pool, block_table, seq_lens, scale: float, *, 
                                    total_kv_tokens, S, Hq, Hkv, D, B, NB, float(scale), workspace.data_ptr(),
                                    workspace.numel(), _stream())
     _check(st, "paged_gqa_decode")
+    return out
+
+
+def paged_gqa_decode_append(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, scale: float, *,
+                            max_seq_len: int, total_kv_tokens: int = 0, out=None, workspace=None):
+    """One decode step in one launch: append ``k_new/v_new [S][Hkv][D]`` at
+    position ``seq_lens[s] - 1`` of each sequence (the pools are written),
+    then decode ``q [S][Hq][D]`` over all ``seq_lens[s]`` keys -> ``out``."""
+    NB, Hkv, B, D = _pool_shape(k_pool, v_pool)
+    _bf16(q, "q", 3)
+    S, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError("q head_dim differs from the pools'")
+    _bf16(k_new, "k_new", 3)
+    _bf16(v_new, "v_new", 3)
+    if tuple(k_new.shape) != (S, Hkv, D) or tuple(v_new.shape) != (S, Hkv, D):
+        raise ValueError("k_new/v_new must be [S][num_kv_heads][head_dim]")
+    _i32(block_table, "block_table", 2)
+    _i32(seq_lens, "seq_lens", 1)
+    if block_table.shape[0] != S or seq_lens.shape[0] != S:
+        raise ValueError("block_table and seq_lens need one row per sequence")
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _bf16(out, "out", 3)
+    if tuple(out.shape) != (S, Hq, D):
+        raise ValueError("out must be [S][Hq][D]")
+    need = decode_workspace_bytes(S, Hq, Hkv, D, max_seq_len, total_kv_tokens) if S > 0 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
+    st = lib().pkv_paged_gqa_decode_append(out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                          k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(),
+                                          block_table.shape[1], seq_lens.data_ptr(), max_seq_len, total_kv_tokens,
+                                          S, Hq, Hkv, D, B, NB, float(scale), workspace.data_ptr(),
+                                          workspace.numel(), _stream())
+    _check(st, "paged_gqa_decode_append")
     return out
 
 

@@ -37,6 +37,12 @@
 //    bf16 for the MFMA and the running sum adds exactly those values.  Rows
 //    past the sequence end are masked to -inf, and their DMA reads a copy of
 //    the last valid row, so no unwritten (NaN) slot reaches the MFMA.
+//  * decode_append folds the step's kv_append into the same launch: the
+//    workgroup of a sequence's last chunk writes the new K/V row (position
+//    seq_len - 1) to the pools, and the wave that computes the tile holding
+//    that position overwrites the row in its LDS stage with the new row once
+//    the tile's copy has landed (and the rows past it, so that no unwritten
+//    slot reaches the MFMA), so nothing waits for the store.
 //  * Chunks of a sequence write a normalised partial and its log2-sum-exp; a
 //    second kernel merges them in one pass with a running maximum
 //    (out = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M)).  The hand-off goes
@@ -241,6 +247,9 @@ struct WaveItem {
     const DecodeArgs* a;
     int log2_block, g, k0, kend, wave, lane, n_tiles;
     int ids0, ids1;  // block id of tile t in lane t % 64 of ids(t / 64)
+    int L;           // keys of the sequence
+    bool append;     // decode_append: the new row (kn, vn: this lane's piece) is key L - 1
+    u32x4 kn, vn;
     float c;         // scale * log2 e
     u32x4 qf[D / 32];
     TileLanes<D> tl;
@@ -267,6 +276,34 @@ __device__ __forceinline__ void issue(const WaveItem<D>& w, int t, int stage) {
                   lds_addr(w.st.v[stage]) + wave_bytes);
 }
 
+// decode_append, on the tile holding key L - 1 (row r0 of the tile): the new
+// K/V row replaces rows r0.. of the wave's stage (its copy may predate the
+// store, or be a clamped copy of that row), and goes to the pools.
+template <int D>
+__device__ __forceinline__ void put_new_row(const WaveItem<D>& w, int t, int kS) {
+    constexpr int kPieces = D / 8, kRowsPerLoad = kWave / kPieces;
+    const int kt = tile_key(w, t);
+    const int r0 = w.L - 1 - kt;
+    uint16_t* sk = w.st.k[kS] + w.wave * kTileKeys * D;
+    uint16_t* sv = w.st.v[kS] + w.wave * kTileKeys * D;
+    const int piece = w.lane % kPieces;
+#pragma unroll
+    for (int j = 0; j < kTileKeys / kRowsPerLoad; ++j) {
+        const int r = j * kRowsPerLoad + w.lane / kPieces;
+        if (r >= r0) {
+            store16(sk + r * D + swz<D>(r, piece) * 8, w.kn);
+            store16(sv + r * D + swz<D>(r, piece) * 8, w.vn);
+        }
+    }
+    const int blk = tile_blk(w, t);
+    if ((unsigned)blk < (unsigned)w.a->num_blocks && w.lane < 2 * kPieces) {
+        const int B = 1 << w.log2_block;
+        const int64_t row = (((int64_t)blk * w.a->num_kv_heads + w.g) * B + ((w.L - 1) & (B - 1))) * D;
+        if (w.lane < kPieces) store16(w.a->k_pool_w + row + piece * 8, w.kn);
+        else store16(w.a->v_pool_w + row + piece * 8, w.vn);
+    }
+}
+
 // Tile t from stage kS: wait for it, refill the stage freed by tile t - 1
 // with tile t + 3, then S^T, softmax, O^T.
 template <int D, int kS>
@@ -277,6 +314,7 @@ __device__ __forceinline__ void tile_step(const WaveItem<D>& w, int t, WaveState
     else if (after == 1) wait_vmcnt<kDma>();
     else wait_vmcnt<0>();
     if (t + kStages - 1 < w.n_tiles) issue(w, t + kStages - 1, (kS + kStages - 1) % kStages);
+    if (w.append && w.kend == w.L && tile_key(w, t) + kTileKeys >= w.kend) put_new_row<D>(w, t, kS);
 
     // every LDS read of the tile goes out before the first MFMA waits on one
     const uint16_t* sk = w.st.k[kS] + w.wave * kTileKeys * D;
@@ -391,6 +429,7 @@ struct ItemInputs {
     int L_raw;
     int ids0, ids1;
     u32x4 qf[D / 32];
+    u32x4 kn, vn;  // decode_append: this lane's piece of the new K/V row
 };
 
 // This wave's index, known to the compiler to be the same on every lane.
@@ -420,6 +459,12 @@ __device__ __forceinline__ ItemInputs<D> load_item_inputs(const DecodeKernelArgs
     in.ids1 = p.chunk > kTileKeys * kDecodeWaves * kWave
                   ? table[min((k0 + kTileKeys * (wave + kDecodeWaves * (lane + kWave))) >> p.log2_block, last)]
                   : 0;
+    in.kn = in.vn = zero;
+    if (a.k_new) {
+        const int64_t row = ((int64_t)s * a.num_kv_heads + g) * D + (lane % (D / 8)) * 8;
+        in.kn = load16(a.k_new + row);
+        in.vn = load16(a.v_new + row);
+    }
     return in;
 }
 
@@ -456,6 +501,10 @@ __device__ __forceinline__ void decode_item(const DecodeKernelArgs& p, DecodeSha
     w.n_tiles = tiles > wave ? (tiles - wave + kDecodeWaves - 1) / kDecodeWaves : 0;
     w.ids0 = in.ids0;
     w.ids1 = in.ids1;
+    w.L = L;
+    w.append = a.k_new != nullptr;
+    w.kn = in.kn;
+    w.vn = in.vn;
     w.c = p.qk_scale_log2;
 #pragma unroll
     for (int cc = 0; cc < D / 32; ++cc) w.qf[cc] = in.qf[cc];

@@ -94,27 +94,63 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
     return plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, total_kv_tokens).bytes;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the two decode entry points; on PKV_OK, `a` and `pl`
+// describe the launch (nothing to launch when num_seqs == 0).
+int32_t check_decode(DecodeArgs& a, DecodePlan& pl) {
+    int32_t st = check_heads(a.num_q_heads, a.num_kv_heads, a.head_dim, a.block_size);
+    if (st != PKV_OK) return st;
+    if (a.num_seqs < 0 || a.num_seqs > kMaxDecodeSeqs || a.max_seq_len < 0 || a.num_blocks < 0 ||
+        a.max_blocks_per_seq < 0)
+        return PKV_ERR_BAD_SHAPE;
+    if ((int64_t)a.max_seq_len > (int64_t)a.max_blocks_per_seq * a.block_size) return PKV_ERR_BAD_SHAPE;
+    if (a.num_seqs == 0) return PKV_OK;
+    if (!a.out || !a.q || !a.block_table || !a.seq_lens) return PKV_ERR_NULL_POINTER;
+    if (a.max_seq_len > 0 && (!a.k_pool || !a.v_pool)) return PKV_ERR_NULL_POINTER;
+    if (!aligned16(a.out) || !aligned16(a.q) || !aligned16(a.k_pool) || !aligned16(a.v_pool) ||
+        !aligned16(a.workspace))
+        return PKV_ERR_MISALIGNED;
+    pl = plan_decode(a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim, a.max_seq_len, a.total_kv_tokens);
+    if (!a.workspace || a.workspace_bytes < pl.bytes) return PKV_ERR_WORKSPACE;
+    if (a.total_kv_tokens <= 0) a.total_kv_tokens = (int64_t)a.num_seqs * a.max_seq_len;
+    return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int32_t pkv_paged_gqa_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
                              const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
                              int32_t max_seq_len, int64_t total_kv_tokens, int32_t num_seqs, int32_t num_q_heads,
                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                              float scale, void* workspace, size_t workspace_bytes, void* stream) {
-    int32_t st = check_heads(num_q_heads, num_kv_heads, head_dim, block_size);
-    if (st != PKV_OK) return st;
-    if (num_seqs < 0 || num_seqs > kMaxDecodeSeqs || max_seq_len < 0 || num_blocks < 0 || max_blocks_per_seq < 0)
-        return PKV_ERR_BAD_SHAPE;
-    if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size) return PKV_ERR_BAD_SHAPE;
-    if (num_seqs == 0) return PKV_OK;
-    if (!out || !q || !block_table || !seq_lens) return PKV_ERR_NULL_POINTER;
-    if (max_seq_len > 0 && (!k_pool || !v_pool)) return PKV_ERR_NULL_POINTER;
-    if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(workspace))
-        return PKV_ERR_MISALIGNED;
-    const DecodePlan pl = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, total_kv_tokens);
-    if (!workspace || workspace_bytes < pl.bytes) return PKV_ERR_WORKSPACE;
-    const int64_t bound = total_kv_tokens > 0 ? total_kv_tokens : (int64_t)num_seqs * max_seq_len;
-    DecodeArgs a{out, q, k_pool, v_pool, block_table, max_blocks_per_seq, seq_lens, max_seq_len, bound,
+    DecodeArgs a{out, q, k_pool, v_pool, block_table, max_blocks_per_seq, seq_lens, max_seq_len, total_kv_tokens,
                  num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, workspace,
                  workspace_bytes};
+    DecodePlan pl{};
+    const int32_t st = check_decode(a, pl);
+    if (st != PKV_OK || num_seqs == 0) return st;
+    return hip_status(launch_decode(a, pl, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pkv_paged_gqa_decode_append(uint16_t* out, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                                    uint16_t* k_pool, uint16_t* v_pool, const int32_t* block_table,
+                                    int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                    int64_t total_kv_tokens, int32_t num_seqs, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                    float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    DecodeArgs a{out, q, k_pool, v_pool, block_table, max_blocks_per_seq, seq_lens, max_seq_len, total_kv_tokens,
+                 num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, workspace,
+                 workspace_bytes, k_new, v_new, k_pool, v_pool};
+    DecodePlan pl{};
+    const int32_t st = check_decode(a, pl);
+    if (st != PKV_OK || num_seqs == 0) return st;
+    if (!k_new || !v_new) return PKV_ERR_NULL_POINTER;
+    if (!aligned16(k_new) || !aligned16(v_new)) return PKV_ERR_MISALIGNED;
     return hip_status(launch_decode(a, pl, static_cast<hipStream_t>(stream)));
 }
 

@@ -44,6 +44,13 @@ struct DecodeArgs {
     float scale;
     void* workspace;
     size_t workspace_bytes;
+    // decode_append only (else null): one new K/V row per sequence
+    // [num_seqs][num_kv_heads][head_dim], at position seq_lens[s] - 1, and
+    // the same pools, writable
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    uint16_t* k_pool_w;
+    uint16_t* v_pool_w;
 };
 
 struct PrefillArgs {

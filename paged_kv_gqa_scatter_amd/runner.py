@@ -13,7 +13,7 @@ from typing import Dict, Optional
 import numpy as np
 import torch
 
-from . import kv_append, paged_gqa_decode, paged_gqa_prefill, decode_workspace_bytes
+from . import kv_append, paged_gqa_decode, paged_gqa_decode_append, paged_gqa_prefill, decode_workspace_bytes
 from .workloads import NAN_SENTINEL, AppendBatch, Case, DecodeBatch, Deferred, PrefillBatch
 
 
@@ -131,6 +131,16 @@ class DeviceCase:
         return paged_gqa_decode(dd.q, k, v, dd.block_table, dd.seq_lens, float(self.case.scale),
                                 max_seq_len=dd.max_seq_len, total_kv_tokens=dd.total_kv_tokens, out=dd.out,
                                 workspace=dd.workspace)
+
+    def decode_append(self, a: DevAppend, dd: DevDecode, pool: int = 0):
+        """The step's append and decode in one launch; `a` must add exactly
+        one row per sequence of `dd`, in the same order (a decode step)."""
+        k, v = self.pools[pool]
+        S = dd.q.shape[0]
+        return paged_gqa_decode_append(dd.q, a.k_new.view(S, *a.k_new.shape[1:]), a.v_new.view(S, *a.v_new.shape[1:]),
+                                       k, v, dd.block_table, dd.seq_lens, float(self.case.scale),
+                                       max_seq_len=dd.max_seq_len, total_kv_tokens=dd.total_kv_tokens, out=dd.out,
+                                       workspace=dd.workspace)
 
     def prefill(self, pp: DevPrefill, pool: int = 0):
         k, v = self.pools[pool]

@@ -101,6 +101,26 @@ def test_decode_workspace_bytes(lib):
     assert f(272, 32, 8, 128, 32769, 1_830_000) < f(272, 32, 8, 128, 32769, 0)
 
 
+def decode_append_args(**kw):
+    a = dict(out=A16, q=A16, kn=A16, vn=A16, kp=A16, vp=A16, table=A16, mbs=9, lens=A16, maxlen=2049, total=0, S=8,
+             hq=32, hkv=8, d=128, bs=256, nb=90, scale=0.088, ws=A16, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return tuple(a[k] for k in ("out", "q", "kn", "vn", "kp", "vp", "table", "mbs", "lens", "maxlen", "total", "S",
+                                "hq", "hkv", "d", "bs", "nb", "scale", "ws", "wsb", "stream"))
+
+
+def test_decode_append_rejects(lib):
+    f = lib.pkv_paged_gqa_decode_append
+    assert f(*decode_append_args(hq=30)) == 2
+    assert f(*decode_append_args(maxlen=9 * 256 + 1)) == 2
+    assert f(*decode_append_args(kn=None)) == 1
+    assert f(*decode_append_args(vn=None)) == 1
+    assert f(*decode_append_args(q=None)) == 1
+    assert f(*decode_append_args(kn=A16 + 2)) == 3
+    assert f(*decode_append_args(ws=None)) == 4
+    assert f(*decode_append_args(S=0)) == 0
+
+
 def prefill_args(**kw):
     a = dict(out=A16, q=A16, cu=A16, T=1000, maxq=512, kp=A16, vp=A16, table=A16, mbs=8, lens=A16, maxlen=1536,
              S=2, hq=32, hkv=8, d=128, bs=256, nb=20, scale=0.088, stream=None)

@@ -307,3 +307,67 @@ def test_graph_replays_match_eager(orc):
         torch.cuda.synchronize()
         assert torch.equal(st["decode"].out.view(torch.int16), want["decode"].view(torch.int16))
     _say("  4 replays bit-identical to the eager step")
+
+
+# ---------------------------------------------------------------- decode_append
+
+def _decode_append_check(orc, case, k_new, v_new, q, seq_lens, table, what):
+    """Run decode_append on a case's fills (the step's rows not yet appended)
+    and compare pools (bit for bit) and outputs with kv_append + decode on
+    the oracle."""
+    import paged_kv_gqa_scatter_amd as pkv
+    dc = _dev()(case)
+    dc.run_fills()
+    dev = lambda a, dt=torch.int32: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    bits = lambda a: dev(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    S = seq_lens.shape[0]
+    ws = torch.empty(pkv.decode_workspace_bytes(S, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                                                int(seq_lens.max())), dtype=torch.uint8, device="cuda")
+    out = pkv.paged_gqa_decode_append(bits(q), bits(k_new), bits(v_new), dc.k_pool, dc.v_pool,
+                                      dev(table.astype(np.int32)), dev(seq_lens.astype(np.int32)),
+                                      float(case.scale), max_seq_len=int(seq_lens.max()), workspace=ws)
+    torch.cuda.synchronize()
+    K, V = case.empty_pool(), case.empty_pool()
+    for f in case.fills:
+        orc.kv_append(K, V, f.k_new, f.v_new, f.cu_new_lens, f.ctx_lens, f.block_table)
+    live = np.nonzero(seq_lens > 0)[0]
+    cu = np.arange(live.size + 1, dtype=np.int32)
+    orc.kv_append(K, V, k_new[live], v_new[live], cu, (seq_lens[live] - 1).astype(np.int32),
+                  np.ascontiguousarray(table[live]))
+    gk, gv = dc.pools_numpy()
+    assert np.array_equal(gk, K) and np.array_equal(gv, V), "pools differ from kv_append"
+    ref = orc.decode(q, K, V, table, seq_lens, case.scale)
+    compare(_f64(out), ref, what)
+    return _f64(out)
+
+
+def test_decode_append_config2(orc):
+    case = W.config2_decode()
+    _say(f"case {case.name}: decode_append")
+    a, d = case.steps[0].append, case.steps[0].decode
+    got = _decode_append_check(orc, case, a.k_new, a.v_new, d.q, d.seq_lens, d.block_table, "decode_append 8 seqs")
+    plain = _dev()(case).run_all()[0]["decode"]  # kv_append + decode
+    compare(got, plain, "decode_append vs kv_append + decode")
+
+
+@pytest.mark.parametrize("d,bs,hq,hkv", [(128, 256, 32, 8), (64, 16, 4, 1), (128, 16, 16, 2)])
+def test_decode_append_edge_lengths(orc, d, bs, hq, hkv):
+    # the new row is key 0 (seq_len 1), the last key of a block, the first of
+    # a new block, deep in a long many-chunk sequence, or absent (seq_len 0)
+    lens = [1, bs - 1, bs, bs + 1, 2 * bs, 700, 32769, 0]
+    rng = np.random.default_rng(3000 + d + bs)
+    ctx = [max(L - 1, 0) for L in lens]
+    case = W.build_case(f"decode_append_edges_d{d}_b{bs}", rng, hq=hq, hkv=hkv, d=d, bs=bs, ctx_lens=ctx[:-1],
+                        new_lens=[1] * (len(lens) - 1), kinds="d" * (len(lens) - 1))
+    a, dec = case.steps[0].append, case.steps[0].decode
+    S = len(lens)
+    pad = W.bf16_normal(rng, (1, hkv, d))
+    k_new = np.concatenate([a.k_new, pad])
+    v_new = np.concatenate([a.v_new, pad])
+    q = np.concatenate([dec.q, W.bf16_normal(rng, (1, hq, d))])
+    seq_lens = np.append(dec.seq_lens, 0).astype(np.int32)
+    table = np.vstack([dec.block_table, np.full((1, dec.block_table.shape[1]), -1, np.int32)])
+    assert seq_lens.shape[0] == S
+    _say(f"case {case.name}: lens {lens}")
+    out = _decode_append_check(orc, case, k_new, v_new, q, seq_lens, table, "decode_append edge lengths")
+    assert np.array_equal(out[-1], np.zeros_like(out[-1])), "empty sequence must give zeros"
