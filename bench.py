@@ -61,47 +61,75 @@ def parse():
     ap.add_argument("--profile-pass", action="store_true",
                     help="for counter runs: a few untimed steps of each kernel plus a reference device copy, no JSON")
     ap.add_argument("--copy-mib", type=int, default=256, help="size of the reference copy in --profile-pass")
+    ap.add_argument("--profile-warm-s", type=float, default=0.0,
+                    help="--profile-pass: run each workload this long before its counted calls (steady clocks)")
+    ap.add_argument("--profile-only", choices=("decode", "prefill", "long", "copy"), default=None,
+                    help="--profile-pass: run only this workload (counter passes per workload)")
     return ap.parse_args()
 
 
 def profile_pass(args):
-    """A short program for rocprofv3 counter passes: the decode step, the
-    prefill kernel and the long-context decode a few times each (the long one
-    last, unless --no-long), and one plain device-to-device copy of
-    --copy-mib MiB whose counter readings calibrate the byte counters."""
+    """A short program for rocprofv3 counter passes: the decode step (one
+    decode_append launch), the prefill kernel and the long-context decode a
+    few times each (the long one last, unless --no-long), and one plain
+    device-to-device copy of --copy-mib MiB whose counter readings calibrate
+    the byte counters."""
     import torch
     from paged_kv_gqa_scatter_amd import workloads as W
     from paged_kv_gqa_scatter_amd.runner import DeviceCase
 
     n = max(1, args.steps)
-    case = W.config2_decode()
-    n_rot = max(1, -(-ROTATE_BYTES // case.pool_bytes))  # as timed: every step reads HBM
-    dc = DeviceCase(case, pools=n_rot)
-    dc.run_fills()
-    for i in range(n):
-        dc.run_step(0, pool=i % n_rot)
-    pc = DeviceCase(W.config3_prefill())
-    pc.run_fills()
-    pc.append(pc.steps[0]["append"])
-    for _ in range(n):
-        pc.prefill(pc.steps[0]["prefill"])
-    nl = 0
-    if not args.no_long:
+    only = args.profile_only
+    done = []
+
+    def warm(fn):
+        t = time.perf_counter()
+        while time.perf_counter() - t < args.profile_warm_s:
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+
+    if only in (None, "decode"):
+        case = W.config2_decode()
+        n_rot = max(1, -(-ROTATE_BYTES // case.pool_bytes))  # as timed: every step reads HBM
+        dc = DeviceCase(case, pools=n_rot)
+        dc.run_fills()
+        st = dc.steps[0]
+        warm(lambda: dc.decode_append(st["append"], st["decode"]))
+        torch.cuda.synchronize()
+        for i in range(n):
+            dc.decode_append(st["append"], st["decode"], pool=i % n_rot)
+        torch.cuda.synchronize()
+        del dc
+        done.append(f"{n} decode steps")
+    if only in (None, "prefill"):
+        pc = DeviceCase(W.config3_prefill())
+        pc.run_fills()
+        pc.append(pc.steps[0]["append"])
+        warm(lambda: pc.prefill(pc.steps[0]["prefill"]))
+        for _ in range(n):
+            pc.prefill(pc.steps[0]["prefill"])
+        torch.cuda.synchronize()
+        del pc
+        done.append(f"{n} prefills")
+    if only == "long" or (only is None and not args.no_long):
         lc = DeviceCase(W.config5_prefix_long(draw_values=False))
         lc.run_fills()
         lc.append(lc.steps[0]["append"])
-        nl = n
+        warm(lambda: lc.decode(lc.steps[0]["decode"]))
         for _ in range(n):
             lc.decode(lc.steps[0]["decode"])
         torch.cuda.synchronize()
         del lc
-        torch.cuda.empty_cache()
-    src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    print(f"profile pass done: {n} decode steps, {n} prefills, {nl} long-context decodes, copy of {args.copy_mib} MiB",
-          flush=True)
+        done.append(f"{n} long-context decodes")
+    torch.cuda.empty_cache()
+    if only in (None, "copy"):
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        done.append(f"a copy of {args.copy_mib} MiB")
+    print("profile pass done: " + ", ".join(done), flush=True)
 
 
 def library_source_hash() -> str:
@@ -288,7 +316,9 @@ def time_long_decode(args):
             "value": round(gbs, 2), "unit": "GB/s", "logical_gbs": round(logical / (ms * 1e-3) / 1e9, 2),
             "roofline": {"bound": "hbm", "kernel": "paged_gqa_decode (decode_kernel + decode_merge_kernel)",
                          "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": (lambda r: int(r["hbm_bytes_per_launch"]) if r else None)(
+                             traffic_record("long_decode"))}}
 
 
 def cpu_baseline(case, dec, kv_bytes, seconds):
@@ -329,7 +359,6 @@ def main():
 
     case, dec, kv_bytes, n_rot, step_ms, dec_ms, eager_ms, split_ms = time_decode_workload(args)
     gbs = kv_bytes / (step_ms * 1e-3) / 1e9
-    dec_gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
     line = {
         "metric": "paged GQA attn: decode KV-read GB/s + prefill causal TFLOP/s (bf16, 1 GPU)",
         "value": round(gbs, 2),
@@ -349,13 +378,13 @@ def main():
                    "unique_kv_bytes": int(kv_bytes), "pool_copies_rotated": n_rot, "hip_graph": True,
                    "ms_per_step_append_then_decode": round(split_ms, 5),
                    "eager_ms_per_step_append_then_decode": round(eager_ms, 5)},
-        "roofline": {"bound": "hbm", "kernel": "paged_gqa_decode (decode_kernel + decode_merge_kernel), one HIP-graph "
-                                                "replay per launch",
-                     "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": int(kv_bytes),
-                     "ms": round(dec_ms, 5)},
+        "roofline": {"bound": "hbm", "kernel": "paged_gqa_decode_append (decode_kernel + decode_merge_kernel), "
+                                                "one HIP-graph replay per launch, back to back",
+                     "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": int(kv_bytes),
+                     "ms": round(step_ms, 5), "decode_only_ms": round(dec_ms, 5)},
     }
-    rec = traffic_record("paged_gqa_decode")
+    rec = traffic_record("decode_append")
     if rec is not None:
         line["roofline"]["traffic"] = int(rec["hbm_bytes_per_launch"])
     if not args.no_prefill:
@@ -367,7 +396,7 @@ def main():
             "roofline": {"bound": "mfma", "kernel": "paged_gqa_prefill (prefill_kernel)", "achieved": round(tfs, 2),
                          "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
                          "traffic": None}}
-        prec = traffic_record("paged_gqa_prefill")
+        prec = traffic_record("prefill")
         if prec is not None:
             line["prefill"]["roofline"]["traffic"] = int(prec["hbm_bytes_per_launch"])
     if not args.no_long:
