@@ -23,9 +23,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 STATUS = {0: "PKV_OK", 1: "PKV_ERR_NULL_POINTER", 2: "PKV_ERR_BAD_SHAPE", 3: "PKV_ERR_MISALIGNED",
-          4: "PKV_ERR_WORKSPACE", 5: "PKV_ERR_HIP"}
+          4: "PKV_ERR_WORKSPACE", 5: "PKV_ERR_HIP", 6: "PKV_ERR_NO_BLOCKS", 7: "PKV_ERR_UNKNOWN_SEQ"}
 EXPORTS = ("pkv_abi_version", "pkv_status_string", "pkv_kv_append", "pkv_decode_workspace_bytes",
            "pkv_paged_gqa_decode", "pkv_paged_gqa_decode_append", "pkv_paged_gqa_prefill")
+BLOCK_EXPORTS = ("pkv_bm_create", "pkv_bm_destroy", "pkv_bm_available", "pkv_bm_seq_len", "pkv_bm_append",
+                 "pkv_bm_free_sequence", "pkv_bm_block_table", "pkv_bm_cache_prefix", "pkv_bm_fork",
+                 "pkv_copy_blocks")
 
 
 class PkvError(RuntimeError):
@@ -53,6 +56,26 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_paged_gqa_decode_append.restype = I32
     lib.pkv_paged_gqa_decode_append.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I64, I32, I32, I32, I32, I32, I32,
                                                 F32, P, SZ, P]
+    lib.pkv_bm_create.restype = P
+    lib.pkv_bm_create.argtypes = [I32, I32]
+    lib.pkv_bm_destroy.restype = None
+    lib.pkv_bm_destroy.argtypes = [P]
+    lib.pkv_bm_available.restype = I32
+    lib.pkv_bm_available.argtypes = [P]
+    lib.pkv_bm_seq_len.restype = I32
+    lib.pkv_bm_seq_len.argtypes = [P, I64]
+    lib.pkv_bm_append.restype = I32
+    lib.pkv_bm_append.argtypes = [P, I64, I32, P, P]
+    lib.pkv_bm_free_sequence.restype = I32
+    lib.pkv_bm_free_sequence.argtypes = [P, I64]
+    lib.pkv_bm_block_table.restype = I32
+    lib.pkv_bm_block_table.argtypes = [P, P, I32, I32, P]
+    lib.pkv_bm_cache_prefix.restype = I32
+    lib.pkv_bm_cache_prefix.argtypes = [P, I64, P, I32]
+    lib.pkv_bm_fork.restype = I32
+    lib.pkv_bm_fork.argtypes = [P, I64, P, I32, P]
+    lib.pkv_copy_blocks.restype = I32
+    lib.pkv_copy_blocks.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, P]
     lib.pkv_paged_gqa_prefill.restype = I32
     lib.pkv_paged_gqa_prefill.argtypes = [P, P, P, I32, I32, P, P, P, I32, P, I32, I32, I32, I32, I32, I32, I32,
                                           F32, P]
@@ -200,6 +223,20 @@ def paged_gqa_decode_append(q, k_new, v_new, k_pool, v_pool, block_table, seq_le
                                           workspace.numel(), _stream())
     _check(st, "paged_gqa_decode_append")
     return out
+
+
+def copy_blocks(k_pool, v_pool, src_ids, dst_ids) -> None:
+    """Copy whole blocks src_ids[i] -> dst_ids[i] of both pools (the device
+    side of the block manager's copy-on-write)."""
+    import numpy as np
+    NB, Hkv, B, D = _pool_shape(k_pool, v_pool)
+    src = np.ascontiguousarray(src_ids, dtype=np.int32)
+    dst = np.ascontiguousarray(dst_ids, dtype=np.int32)
+    if src.shape != dst.shape or src.ndim != 1:
+        raise ValueError("src_ids and dst_ids must be 1-d and of one length")
+    st = lib().pkv_copy_blocks(k_pool.data_ptr(), v_pool.data_ptr(), src.ctypes.data, dst.ctypes.data, src.size,
+                              Hkv, D, B, NB, _stream())
+    _check(st, "copy_blocks")
 
 
 def paged_gqa_prefill(q, cu_q_lens, k_pool, v_pool, block_table, seq_lens, scale: float, *, max_q_len: int,

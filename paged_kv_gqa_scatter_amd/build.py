@@ -22,7 +22,7 @@ FLAGS = [
 
 
 def sources():
-    return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+    return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")) + glob.glob(os.path.join(HERE, "csrc", "*.cpp")))
 
 
 def build(out: str = LIB, extra=()) -> str:

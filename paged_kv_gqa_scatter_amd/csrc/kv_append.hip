@@ -58,7 +58,26 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendArgs a)
     store16(a.v_pool + dst, vv);
 }
 
+// Copy-on-write: block src[p] -> dst[p] of both pools, one 16-byte piece per
+// thread; blockIdx.y is the pair.
+__global__ __launch_bounds__(kAppendThreads) void copy_blocks_kernel(CopyBlocksArgs a) {
+    const int p = blockIdx.y;
+    const int64_t e = ((int64_t)blockIdx.x * kAppendThreads + threadIdx.x) * 8;
+    if (p >= a.n_pairs || e >= a.slab_elems) return;
+    const int64_t s = (int64_t)a.src[p] * a.slab_elems + e, d = (int64_t)a.dst[p] * a.slab_elems + e;
+    store16(a.k_pool + d, load16(a.k_pool + s));
+    store16(a.v_pool + d, load16(a.v_pool + s));
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream) {
+    if (a.n_pairs <= 0) return hipSuccess;
+    const int64_t pieces = a.slab_elems / 8;
+    const dim3 grid((unsigned)((pieces + kAppendThreads - 1) / kAppendThreads), (unsigned)a.n_pairs);
+    hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kAppendThreads), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream) {
     const int64_t total = (int64_t)a.total_new_tokens * a.num_kv_heads * (a.head_dim / 8);

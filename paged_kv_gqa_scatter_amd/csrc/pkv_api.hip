@@ -6,6 +6,7 @@
 #include <vector>
 
 #include "../../include/pkv.h"
+#include "../../include/pkv_blocks.h"
 #include "pkv_launch.h"
 
 namespace pkv {
@@ -62,6 +63,8 @@ const char* pkv_status_string(int32_t status) {
         case PKV_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
         case PKV_ERR_WORKSPACE: return "decode workspace missing or too small";
         case PKV_ERR_HIP: return "a kernel launch failed";
+        case PKV_ERR_NO_BLOCKS: return "not enough free or evictable KV blocks";
+        case PKV_ERR_UNKNOWN_SEQ: return "no sequence with that id";
         default: return "unknown status";
     }
 }
@@ -85,6 +88,37 @@ int32_t pkv_kv_append(uint16_t* k_pool, uint16_t* v_pool, const uint16_t* k_new,
     AppendArgs a{k_pool, v_pool, k_new, v_new, cu_new_lens, ctx_lens, block_table, max_blocks_per_seq,
                  num_seqs, total_new_tokens, num_kv_heads, head_dim, block_size, num_blocks};
     return hip_status(launch_kv_append(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pkv_copy_blocks(uint16_t* k_pool, uint16_t* v_pool, const int32_t* src_ids, const int32_t* dst_ids,
+                        int32_t n_pairs, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t num_blocks, void* stream) {
+    if (n_pairs < 0 || num_kv_heads <= 0 || num_blocks < 0) return PKV_ERR_BAD_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return PKV_ERR_BAD_SHAPE;
+    if (!pow2_in(block_size, 16, 256)) return PKV_ERR_BAD_SHAPE;
+    if (n_pairs == 0) return PKV_OK;
+    if (!k_pool || !v_pool || !src_ids || !dst_ids) return PKV_ERR_NULL_POINTER;
+    if (!aligned16(k_pool) || !aligned16(v_pool)) return PKV_ERR_MISALIGNED;
+    for (int32_t i = 0; i < n_pairs; ++i) {
+        if (src_ids[i] < 0 || src_ids[i] >= num_blocks || dst_ids[i] < 0 || dst_ids[i] >= num_blocks)
+            return PKV_ERR_BAD_SHAPE;
+        for (int32_t j = 0; j < n_pairs; ++j)
+            if (dst_ids[i] == src_ids[j] || (j != i && dst_ids[i] == dst_ids[j])) return PKV_ERR_BAD_SHAPE;
+    }
+    CopyBlocksArgs a{};
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.slab_elems = (int64_t)num_kv_heads * block_size * head_dim;
+    for (int32_t i0 = 0; i0 < n_pairs; i0 += kCopyPairsPerLaunch) {
+        a.n_pairs = n_pairs - i0 < kCopyPairsPerLaunch ? n_pairs - i0 : kCopyPairsPerLaunch;
+        for (int32_t i = 0; i < a.n_pairs; ++i) {
+            a.src[i] = src_ids[i0 + i];
+            a.dst[i] = dst_ids[i0 + i];
+        }
+        const int32_t st = hip_status(launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
+        if (st != PKV_OK) return st;
+    }
+    return PKV_OK;
 }
 
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,

@@ -90,7 +90,19 @@ struct DecodePlan {
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t max_seq_len, int64_t total_kv_tokens);
 
+// Whole-block copies of both pools (copy-on-write of a shared block).
+constexpr int kCopyPairsPerLaunch = 32;
+struct CopyBlocksArgs {
+    uint16_t* k_pool;
+    uint16_t* v_pool;
+    int32_t src[kCopyPairsPerLaunch];
+    int32_t dst[kCopyPairsPerLaunch];
+    int32_t n_pairs;         // <= kCopyPairsPerLaunch
+    int64_t slab_elems;      // num_kv_heads * block_size * head_dim
+};
+
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

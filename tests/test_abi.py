@@ -11,6 +11,7 @@ import paged_kv_gqa_scatter_amd as pkv
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pkv.h")
+BLOCKS_HEADER = os.path.join(ROOT, "include", "pkv_blocks.h")
 
 
 @pytest.fixture(scope="module")
@@ -21,8 +22,8 @@ def lib():
     return pkv.lib()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(pkv_\w+)\s*\(", text, flags=re.M)))
 
 
@@ -33,14 +34,18 @@ def test_header_declares_the_three_operations():
     assert set(names) == set(pkv.EXPORTS)
 
 
+def test_block_header_declares_its_functions():
+    assert set(declared_functions(BLOCKS_HEADER)) == set(pkv.BLOCK_EXPORTS)
+
+
 def test_every_declared_symbol_is_exported(lib):
-    for name in declared_functions():
+    for name in declared_functions() + declared_functions(BLOCKS_HEADER):
         assert hasattr(lib, name), name
 
 
 def test_version_and_status_strings(lib):
     assert lib.pkv_abi_version() == 1
-    for code in range(6):
+    for code in range(8):
         assert lib.pkv_status_string(code)
     assert lib.pkv_status_string(99) == b"unknown status"
 

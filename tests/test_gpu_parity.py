@@ -371,3 +371,81 @@ def test_decode_append_edge_lengths(orc, d, bs, hq, hkv):
     _say(f"case {case.name}: lens {lens}")
     out = _decode_append_check(orc, case, k_new, v_new, q, seq_lens, table, "decode_append edge lengths")
     assert np.array_equal(out[-1], np.zeros_like(out[-1])), "empty sequence must give zeros"
+
+
+# ---------------------------------------------------------------- block manager
+
+def test_block_manager_prefix_sharing_end_to_end(orc):
+    # one prompt cached, three forks that share it (its last block is
+    # partial, so each fork's first append copies it), then a decode step
+    # for all four with decode_append; pools bit-exact against the oracle's
+    # kv_append and copies, outputs against the oracle through the same tables
+    import paged_kv_gqa_scatter_amd as pkv
+    from paged_kv_gqa_scatter_amd.blocks import BlockManager
+    rng = np.random.default_rng(909)
+    NB, Hq, Hkv, D, B, MBS = 96, 16, 4, 128, 16, 40
+    scale = 1.0 / math.sqrt(D)
+    bm = BlockManager(NB, B)
+    kp = torch.full((NB, Hkv, B, D), W.NAN_SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    vp = torch.full_like(kp, 0).view(torch.int16).fill_(W.NAN_SENTINEL).view(torch.bfloat16)
+    K = np.full((NB, Hkv, B, D), W.NAN_SENTINEL, np.uint16)
+    V = K.copy()
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    bits = lambda a: dev(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    one = np.array([0, 0], np.int32)
+
+    def write(seq, k_rows, v_rows):
+        n = k_rows.shape[0]
+        ctx = max(bm.seq_len(seq), 0)  # -1: a sequence the manager has not seen yet
+        cow = bm.append(seq, n)
+        if cow is not None:
+            pkv.copy_blocks(kp, vp, [cow[0]], [cow[1]])
+            K[cow[1]] = K[cow[0]]
+            V[cow[1]] = V[cow[0]]
+        table = bm.block_table([seq], MBS)
+        cu = np.array([0, n], np.int32)
+        cl = np.array([ctx], np.int32)
+        pkv.kv_append(kp, vp, bits(k_rows), bits(v_rows), dev(cu), dev(cl), dev(table))
+        orc.kv_append(K, V, k_rows, v_rows, cu, cl, table)
+
+    prompt = [int(x) for x in rng.integers(50000, size=300)]
+    kv = {}
+    kv[0] = (W.bf16_normal(rng, (300, Hkv, D)), W.bf16_normal(rng, (300, Hkv, D)))
+    write(0, *kv[0])
+    bm.cache_prefix(0, prompt)
+    for s in (1, 2, 3):
+        extra = int(rng.integers(1, 70))
+        toks = prompt + [int(x) for x in rng.integers(50000, size=extra)]
+        assert bm.fork(s, toks) == 300
+        kn, vn = W.bf16_normal(rng, (extra, Hkv, D)), W.bf16_normal(rng, (extra, Hkv, D))
+        write(s, kn, vn)
+    seqs = [0, 1, 2, 3]
+    table = bm.block_table(seqs, MBS)
+    assert len({int(table[s, 0]) for s in seqs}) == 1, "the prompt's first block is shared"
+    # decode step: one new row per sequence, appended and attended in one launch
+    lens, cows = [], 0
+    for s in seqs:
+        cow = bm.append(s, 1)
+        if cow is not None:  # a sequence whose shared block another one wrote past its length
+            pkv.copy_blocks(kp, vp, [cow[0]], [cow[1]])
+            K[cow[1]] = K[cow[0]]
+            V[cow[1]] = V[cow[0]]
+            cows += 1
+        lens.append(bm.seq_len(s))
+    _say(f"  copy-on-write copies in the decode step: {cows}")
+    table = bm.block_table(seqs, MBS)
+    seq_lens = np.array(lens, np.int32)
+    kn, vn = W.bf16_normal(rng, (4, Hkv, D)), W.bf16_normal(rng, (4, Hkv, D))
+    q = W.bf16_normal(rng, (4, Hq, D))
+    ws = torch.empty(pkv.decode_workspace_bytes(4, Hq, Hkv, D, int(seq_lens.max())), dtype=torch.uint8,
+                     device="cuda")
+    out = pkv.paged_gqa_decode_append(bits(q), bits(kn), bits(vn), kp, vp, dev(table), dev(seq_lens), scale,
+                                      max_seq_len=int(seq_lens.max()), workspace=ws)
+    torch.cuda.synchronize()
+    orc.kv_append(K, V, kn, vn, np.arange(5, dtype=np.int32), seq_lens - 1, table)
+    gk = kp.view(torch.int16).cpu().numpy().view(np.uint16)
+    gv = vp.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(gk, K) and np.array_equal(gv, V), "pools differ"
+    ref = orc.decode(q, K, V, table, seq_lens, scale)
+    compare(_f64(out), ref, "decode_append over shared prefix blocks")
+    bm.close()
