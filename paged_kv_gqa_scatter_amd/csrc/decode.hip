@@ -478,10 +478,10 @@ struct __attribute__((aligned(16))) DecodeShared {
 };
 
 // One work item: chunk c of sequence s, KV head g; `slot` is its partial slot.
-template <int D, int G>
+template <int D, int G, typename Prefetch>
 __device__ __forceinline__ void decode_item(const DecodeKernelArgs& p, DecodeShared<D, G>& sh, const Stages<D>& st,
                                             int s, int g, int c, int nchunks, int64_t slot,
-                                            const ItemInputs<D>& in) {
+                                            const ItemInputs<D>& in, Prefetch prefetch) {
     const DecodeArgs& a = p.a;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int Hq = a.num_q_heads;
@@ -517,6 +517,10 @@ __device__ __forceinline__ void decode_item(const DecodeKernelArgs& p, DecodeSha
     ws.m = -INFINITY;
     ws.l = 0.f;
     wait_all_vm();  // the item's inputs (block ids, q) are in
+    // the next item's inputs go out before this item's tile copies: counted
+    // in issue order, they retire with the first tile, so the next item
+    // starts without a round trip of its own
+    prefetch();
     wave_tiles<D>(w, ws);
 
     // ---- wave totals: the sum over the head's four lane groups; O^T rows to LDS
@@ -610,7 +614,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeKernelArgs
         if (L == 0 && c == 0)  // a sequence without keys: zero rows
             for (int e = threadIdx.x; e < G * D; e += kDecodeThreads) p.a.out[((int64_t)s * Hq + g * G) * D + e] = 0;
         if (c >= n) return;
-        decode_item<D, G>(p, sh, st, s, g, c, n, (int64_t)s * p.max_chunks + c, in);
+        decode_item<D, G>(p, sh, st, s, g, c, n, (int64_t)s * p.max_chunks + c, in, [] {});
         return;
     }
 
@@ -628,17 +632,39 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeKernelArgs
     // a multiple of 8 workgroups, so a workgroup only meets KV heads congruent
     // to its XCD modulo 8
     const int64_t total_items = (int64_t)s_prefix[S] * Hkv;
-    for (int64_t item = blockIdx.x; item < total_items; item += gridDim.x) {
-        const int chunk = (int)(item / Hkv);
-        const int g = (int)(item - (int64_t)chunk * Hkv);
+    struct Item {
+        int s, g, c, n, chunk;
+    };
+    auto locate = [&](int64_t item) {
+        Item it;
+        it.chunk = (int)(item / Hkv);
+        it.g = (int)(item - (int64_t)it.chunk * Hkv);
         int lo = 0, hi = S - 1;  // the sequence owning this chunk: last s with s_prefix[s] <= chunk
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (s_prefix[mid] <= chunk) lo = mid; else hi = mid - 1;
+            if (s_prefix[mid] <= it.chunk) lo = mid; else hi = mid - 1;
         }
-        const int n = s_prefix[lo + 1] - s_prefix[lo];
-        const int c = chunk - s_prefix[lo];
-        decode_item<D, G>(p, sh, st, lo, g, c, n, chunk, load_item_inputs<D, G>(p, lo, g, c));
+        it.s = lo;
+        it.n = s_prefix[lo + 1] - s_prefix[lo];
+        it.c = it.chunk - s_prefix[lo];
+        return it;
+    };
+    int64_t item = blockIdx.x;
+    if (item >= total_items) return;
+    Item cur = locate(item);
+    ItemInputs<D> in = load_item_inputs<D, G>(p, cur.s, cur.g, cur.c);
+    for (; item < total_items; item += gridDim.x) {
+        const int64_t nxt = item + gridDim.x;
+        Item next = cur;
+        ItemInputs<D> in_next = in;
+        decode_item<D, G>(p, sh, st, cur.s, cur.g, cur.c, cur.n, cur.chunk, in, [&] {
+            if (nxt < total_items) {
+                next = locate(nxt);
+                in_next = load_item_inputs<D, G>(p, next.s, next.g, next.c);
+            }
+        });
+        cur = next;
+        in = in_next;
     }
 }
 
