@@ -40,6 +40,8 @@ class OracleError(RuntimeError):
 _I32P = ctypes.POINTER(ctypes.c_int32)
 _U16P = ctypes.POINTER(ctypes.c_uint16)
 _F64P = ctypes.POINTER(ctypes.c_double)
+_I8P = ctypes.POINTER(ctypes.c_int8)
+_F32P = ctypes.POINTER(ctypes.c_float)
 
 
 def _p(a, typ):
@@ -57,6 +59,9 @@ class Oracle:
         self.lib.oracle_attention.restype = ctypes.c_int
         self.lib.oracle_attention_rows.restype = ctypes.c_int
         self.lib.oracle_max_threads.restype = ctypes.c_int
+        self.lib.oracle_quantize_int8.restype = None
+        self.lib.oracle_kv_append_int8.restype = ctypes.c_int
+        self.lib.oracle_attention_rows_int8.restype = ctypes.c_int
 
     @staticmethod
     def _check(rc):
@@ -115,6 +120,71 @@ class Oracle:
                                             num_threads)
         self._check(rc)
         return out
+
+    # ---- INT8 KV cache: codes [NB][Hkv][B][D] int8, scales [NB][Hkv][B] fp32
+
+    def quantize_int8(self, rows):
+        """Quantise bf16 rows ``[..., D]`` (uint16): returns (codes int8 of the
+        same shape, scales fp32 ``[...]``)."""
+        rows = np.ascontiguousarray(rows, dtype=np.uint16)
+        D = rows.shape[-1]
+        flat = rows.reshape(-1, D)
+        codes = np.zeros(flat.shape, np.int8)
+        scales = np.zeros(flat.shape[0], np.float32)
+        for i in range(flat.shape[0]):
+            self.lib.oracle_quantize_int8(_p(codes[i], _I8P), _p(scales[i:i + 1], _F32P), _p(flat[i], _U16P), D)
+        return codes.reshape(rows.shape), scales.reshape(rows.shape[:-1])
+
+    def kv_append_int8(self, k_codes, v_codes, k_scales, v_scales, k_new, v_new, cu_new_lens, ctx_lens,
+                       block_table):
+        """In place on host INT8 pools."""
+        NB, Hkv, B, D = k_codes.shape
+        for a in (k_codes, v_codes):
+            assert a.dtype == np.int8 and a.flags.c_contiguous
+        for a in (k_scales, v_scales):
+            assert a.dtype == np.float32 and a.flags.c_contiguous and a.shape == (NB, Hkv, B)
+        for a in (k_new, v_new):
+            assert a.dtype == np.uint16 and a.flags.c_contiguous
+        cu = np.ascontiguousarray(cu_new_lens, dtype=np.int32)
+        ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+        tab = np.ascontiguousarray(block_table, dtype=np.int32)
+        assert k_new.shape[1:] == (Hkv, D) and k_new.shape[0] >= cu[-1]
+        rc = self.lib.oracle_kv_append_int8(_p(k_codes, _I8P), _p(v_codes, _I8P), _p(k_scales, _F32P),
+                                            _p(v_scales, _F32P), _p(k_new, _U16P), _p(v_new, _U16P),
+                                            _p(cu, _I32P), _p(ctx, _I32P), _p(tab, _I32P), tab.shape[1],
+                                            ctx.shape[0], Hkv, D, B, NB)
+        self._check(rc)
+
+    def attention_rows_int8(self, items, q, cu_q_lens, k_codes, v_codes, k_scales, v_scales, block_table,
+                            seq_lens, num_q_heads, scale, num_threads: int = 0):
+        """Selected rows over an INT8 cache (dequantised keys and values)."""
+        NB, Hkv, B, D = k_codes.shape
+        items = np.asarray(items, dtype=np.int32).reshape(-1, 3)
+        s_, r_, h_ = (np.ascontiguousarray(items[:, i]) for i in range(3))
+        q = np.ascontiguousarray(q)
+        cu = np.ascontiguousarray(cu_q_lens, dtype=np.int32)
+        tab = np.ascontiguousarray(block_table, dtype=np.int32)
+        sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        kc, vc = np.ascontiguousarray(k_codes, np.int8), np.ascontiguousarray(v_codes, np.int8)
+        ks, vs = np.ascontiguousarray(k_scales, np.float32), np.ascontiguousarray(v_scales, np.float32)
+        out = np.zeros((items.shape[0], D), dtype=np.float64)
+        rc = self.lib.oracle_attention_rows_int8(_p(out, _F64P), items.shape[0], _p(s_, _I32P), _p(r_, _I32P),
+                                                 _p(h_, _I32P), _p(q, _U16P), _p(cu, _I32P), _p(kc, _I8P),
+                                                 _p(vc, _I8P), _p(ks, _F32P), _p(vs, _F32P), _p(tab, _I32P),
+                                                 tab.shape[1], _p(sl, _I32P), sl.shape[0], num_q_heads, Hkv, D,
+                                                 B, NB, ctypes.c_float(scale), num_threads)
+        self._check(rc)
+        return out
+
+    def decode_int8(self, q, k_codes, v_codes, k_scales, v_scales, block_table, seq_lens, scale,
+                    num_threads: int = 0):
+        """Decode over an INT8 cache: fp64 ``[S][Hq][D]``."""
+        S, Hq, D = q.shape
+        items = np.array([(s, 0, h) for s in range(S) for h in range(Hq)], np.int32).reshape(-1, 3)
+        cu = np.arange(S + 1, dtype=np.int32)
+        out = self.attention_rows_int8(items, q.reshape(S, Hq, D), cu, k_codes, v_codes, k_scales, v_scales,
+                                       block_table, seq_lens, Hq, scale, num_threads)
+        return out.reshape(S, Hq, D)
 
     # decode is the one-row-per-sequence case of the same definition
     def decode(self, q, k_pool, v_pool, block_table, seq_lens, scale, num_threads: int = 0):

@@ -37,6 +37,20 @@
  *    with no key at all (a decode row of an empty sequence, L = 0); such a row
  *    is defined here as all zeros.
  *
+ *  - oracle_quantize_int8 / oracle_kv_append_int8 / oracle_attention_rows_int8:
+ *    the INT8 KV cache of "从零搭建AI工程能力：手写KV Cache与动态批处理实战"
+ *    section 3.2 (the cache kept as 8-bit integers instead of 16-bit floats,
+ *    half the memory, with a quantisation error that every later step reads
+ *    again).  The page names no scheme; the reading taken here is the plainest
+ *    one that suits rows arriving one at a time: symmetric absmax quantisation
+ *    with one fp32 scale per (token, KV head) row, scale = max|x| / 127 and
+ *    code = x / scale rounded to the nearest integer (ties to even), so that
+ *    x is approximated by code * scale.  An all-zero row has scale 0 and
+ *    codes 0.  The quantiser runs in fp32 (IEEE division and rounding), the
+ *    precision in which both this oracle and the HIP path take the integer
+ *    decision; attention then reads the dequantised values code * scale,
+ *    which are exact in fp64.
+ *
  * bf16 inputs are widened exactly: the 16 bits become the top half of an IEEE
  * binary32 word, which is then converted to double.
  */
@@ -55,18 +69,39 @@
 #define ORACLE_ERR_DUP_SLOT (-3)  /* two new rows target the same slot */
 #define ORACLE_ERR_OOM (-4)
 
-static double bf16_to_double(uint16_t h) {
+static float bf16_to_float(uint16_t h) {
     uint32_t bits = ((uint32_t)h) << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
-    return (double)f;
+    return f;
 }
+
+static double bf16_to_double(uint16_t h) { return (double)bf16_to_float(h); }
 
 /* Sequence that owns packed row t, given cu[0..S] with cu[0] = 0. */
 static int owner_of_row(const int32_t* cu, int num_seqs, int t) {
     int s = 0;
     while (s + 1 < num_seqs && cu[s + 1] <= t) ++s;
     return s;
+}
+
+/*
+ * Where packed new row t goes: position ctx_lens[s] + (t - cu_new_lens[s]) of
+ * its sequence s, i.e. block block_table[s][pos / B], slot pos % B.
+ */
+static int target_slot(const int32_t* cu_new_lens, const int32_t* ctx_lens, const int32_t* block_table,
+                       int max_blocks_per_seq, int num_seqs, int block_size, int num_blocks, int t,
+                       int* blk_out, long* slot_out) {
+    int s = owner_of_row(cu_new_lens, num_seqs, t);
+    long pos = (long)ctx_lens[s] + (t - cu_new_lens[s]);
+    long lblock = pos / block_size;
+    long slot = pos % block_size;
+    if (pos < 0 || lblock >= max_blocks_per_seq) return ORACLE_ERR_BLOCK;
+    int blk = block_table[(size_t)s * max_blocks_per_seq + lblock];
+    if (blk < 0 || blk >= num_blocks) return ORACLE_ERR_BLOCK;
+    *blk_out = blk;
+    *slot_out = slot;
+    return ORACLE_OK;
 }
 
 int oracle_kv_append(uint16_t* k_pool, uint16_t* v_pool,
@@ -84,13 +119,11 @@ int oracle_kv_append(uint16_t* k_pool, uint16_t* v_pool,
     if (!written) return ORACLE_ERR_OOM;
     int rc = ORACLE_OK;
     for (int t = 0; t < total && rc == ORACLE_OK; ++t) {
-        int s = owner_of_row(cu_new_lens, num_seqs, t);
-        long pos = (long)ctx_lens[s] + (t - cu_new_lens[s]);
-        long lblock = pos / block_size;
-        long slot = pos % block_size;
-        if (pos < 0 || lblock >= max_blocks_per_seq) { rc = ORACLE_ERR_BLOCK; break; }
-        int blk = block_table[(size_t)s * max_blocks_per_seq + lblock];
-        if (blk < 0 || blk >= num_blocks) { rc = ORACLE_ERR_BLOCK; break; }
+        int blk;
+        long slot;
+        rc = target_slot(cu_new_lens, ctx_lens, block_table, max_blocks_per_seq, num_seqs, block_size,
+                         num_blocks, t, &blk, &slot);
+        if (rc != ORACLE_OK) break;
         size_t flag = (size_t)blk * block_size + slot;
         if (written[flag]) { rc = ORACLE_ERR_DUP_SLOT; break; }
         written[flag] = 1;
@@ -106,12 +139,87 @@ int oracle_kv_append(uint16_t* k_pool, uint16_t* v_pool,
 }
 
 /*
+ * Symmetric absmax quantisation of one row of head_dim bf16 values to INT8
+ * ("从零搭建AI工程能力：手写KV Cache与动态批处理实战" section 3.2, with the
+ * reading stated at the top of this file), in fp32.
+ */
+void oracle_quantize_int8(int8_t* codes, float* scale_out, const uint16_t* row, int head_dim) {
+    float amax = 0.0f;
+    for (int d = 0; d < head_dim; ++d) {
+        float a = fabsf(bf16_to_float(row[d]));
+        if (a > amax) amax = a;
+    }
+    float scale = amax / 127.0f;
+    for (int d = 0; d < head_dim; ++d) {
+        float c = scale > 0.0f ? rintf(bf16_to_float(row[d]) / scale) : 0.0f;
+        if (c > 127.0f) c = 127.0f;
+        if (c < -127.0f) c = -127.0f;
+        codes[d] = (int8_t)c;
+    }
+    *scale_out = scale;
+}
+
+/*
+ * kv_append into an INT8 cache: the same placement as oracle_kv_append, each
+ * new (token, KV head) row quantised on the way in.  Pools are
+ * [num_blocks][num_kv_heads][block_size][head_dim] int8 codes and
+ * [num_blocks][num_kv_heads][block_size] fp32 scales.
+ */
+int oracle_kv_append_int8(int8_t* k_codes, int8_t* v_codes, float* k_scales, float* v_scales,
+                          const uint16_t* k_new, const uint16_t* v_new,
+                          const int32_t* cu_new_lens, const int32_t* ctx_lens,
+                          const int32_t* block_table, int max_blocks_per_seq,
+                          int num_seqs, int num_kv_heads, int head_dim, int block_size,
+                          int num_blocks) {
+    if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks < 0)
+        return ORACLE_ERR_ARGS;
+    const int total = num_seqs > 0 ? cu_new_lens[num_seqs] : 0;
+    size_t nslots = (size_t)num_blocks * (size_t)block_size;
+    unsigned char* written = (unsigned char*)calloc(nslots ? nslots : 1, 1);
+    if (!written) return ORACLE_ERR_OOM;
+    int rc = ORACLE_OK;
+    for (int t = 0; t < total && rc == ORACLE_OK; ++t) {
+        int blk;
+        long slot;
+        rc = target_slot(cu_new_lens, ctx_lens, block_table, max_blocks_per_seq, num_seqs, block_size,
+                         num_blocks, t, &blk, &slot);
+        if (rc != ORACLE_OK) break;
+        if (written[(size_t)blk * block_size + slot]) { rc = ORACLE_ERR_DUP_SLOT; break; }
+        written[(size_t)blk * block_size + slot] = 1;
+        for (int g = 0; g < num_kv_heads; ++g) {
+            size_t row = ((size_t)blk * num_kv_heads + g) * block_size + slot;
+            size_t src = ((size_t)t * num_kv_heads + g) * head_dim;
+            oracle_quantize_int8(k_codes + row * head_dim, k_scales + row, k_new + src, head_dim);
+            oracle_quantize_int8(v_codes + row * head_dim, v_scales + row, v_new + src, head_dim);
+        }
+    }
+    free(written);
+    return rc;
+}
+
+/*
+ * A KV pool as attention reads it: bf16 rows, or INT8 codes with one fp32
+ * scale per row.  Row index = (block * num_kv_heads + kv_head) * block_size + slot.
+ */
+typedef struct {
+    const uint16_t* bf16;  /* [rows][head_dim], or NULL for an INT8 pool */
+    const int8_t* codes;   /* [rows][head_dim] */
+    const float* scales;   /* [rows] */
+} kv_pool;
+
+/* Element d of a pool row, as a double (an INT8 one dequantised: code * scale). */
+static double kv_elem(const kv_pool* pool, size_t row, int head_dim, int d) {
+    if (pool->bf16) return bf16_to_double(pool->bf16[row * head_dim + d]);
+    return (double)pool->codes[row * head_dim + d] * (double)pool->scales[row];
+}
+
+/*
  * One output row: query head h of sequence s at absolute position p attends to
  * keys 0..p of that sequence.  out_row receives head_dim doubles.
  * Returns ORACLE_ERR_BLOCK if a needed block id is invalid.
  */
 static int attend_one(double* out_row, const uint16_t* q_row,
-                      const uint16_t* k_pool, const uint16_t* v_pool,
+                      const kv_pool* k_pool, const kv_pool* v_pool,
                       const int32_t* table_row, int max_blocks_per_seq,
                       int p, int kv_head, int num_kv_heads, int head_dim,
                       int block_size, int num_blocks, double scale,
@@ -127,9 +235,9 @@ static int attend_one(double* out_row, const uint16_t* q_row,
     for (int j = 0; j < nkeys; ++j) {
         int blk = table_row[j / block_size];
         if (blk < 0 || blk >= num_blocks) return ORACLE_ERR_BLOCK;
-        const uint16_t* k = k_pool + (((size_t)blk * num_kv_heads + kv_head) * block_size + j % block_size) * head_dim;
+        size_t krow = ((size_t)blk * num_kv_heads + kv_head) * block_size + j % block_size;
         double dot = 0.0;
-        for (int d = 0; d < head_dim; ++d) dot += bf16_to_double(q_row[d]) * bf16_to_double(k[d]);
+        for (int d = 0; d < head_dim; ++d) dot += bf16_to_double(q_row[d]) * kv_elem(k_pool, krow, head_dim, d);
         z[j] = scale * dot;
         if (z[j] > zmax) zmax = z[j];
     }
@@ -142,8 +250,8 @@ static int attend_one(double* out_row, const uint16_t* q_row,
     for (int d = 0; d < head_dim; ++d) out_row[d] = 0.0;
     for (int j = 0; j < nkeys; ++j) {
         int blk = table_row[j / block_size];
-        const uint16_t* v = v_pool + (((size_t)blk * num_kv_heads + kv_head) * block_size + j % block_size) * head_dim;
-        for (int d = 0; d < head_dim; ++d) out_row[d] += z[j] * bf16_to_double(v[d]);
+        size_t vrow = ((size_t)blk * num_kv_heads + kv_head) * block_size + j % block_size;
+        for (int d = 0; d < head_dim; ++d) out_row[d] += z[j] * kv_elem(v_pool, vrow, head_dim, d);
     }
     for (int d = 0; d < head_dim; ++d) out_row[d] /= denom;
     return ORACLE_OK;
@@ -159,10 +267,10 @@ static int check_heads(int hq, int hkv, int d, int bs) {
  * item_head[i]); its result goes to out[i][0..head_dim).
  * q is packed [cu_q_lens[S]][Hq][D].  num_threads <= 0 uses the OpenMP default.
  */
-int oracle_attention_rows(double* out, int n_items,
+static int attention_rows(double* out, int n_items,
                           const int32_t* item_seq, const int32_t* item_row, const int32_t* item_head,
                           const uint16_t* q, const int32_t* cu_q_lens,
-                          const uint16_t* k_pool, const uint16_t* v_pool,
+                          const kv_pool* k_pool, const kv_pool* v_pool,
                           const int32_t* block_table, int max_blocks_per_seq,
                           const int32_t* seq_lens, int num_seqs,
                           int num_q_heads, int num_kv_heads, int head_dim, int block_size,
@@ -206,6 +314,39 @@ int oracle_attention_rows(double* out, int n_items,
         free(z);
     }
     return rc;
+}
+
+int oracle_attention_rows(double* out, int n_items,
+                          const int32_t* item_seq, const int32_t* item_row, const int32_t* item_head,
+                          const uint16_t* q, const int32_t* cu_q_lens,
+                          const uint16_t* k_pool, const uint16_t* v_pool,
+                          const int32_t* block_table, int max_blocks_per_seq,
+                          const int32_t* seq_lens, int num_seqs,
+                          int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                          int num_blocks, float scale, int num_threads) {
+    kv_pool k = {k_pool, NULL, NULL}, v = {v_pool, NULL, NULL};
+    return attention_rows(out, n_items, item_seq, item_row, item_head, q, cu_q_lens, &k, &v, block_table,
+                          max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                          block_size, num_blocks, scale, num_threads);
+}
+
+/*
+ * The same rows over an INT8 cache (codes and per-row scales as written by
+ * oracle_kv_append_int8), every key and value read as code * scale.
+ */
+int oracle_attention_rows_int8(double* out, int n_items,
+                               const int32_t* item_seq, const int32_t* item_row, const int32_t* item_head,
+                               const uint16_t* q, const int32_t* cu_q_lens,
+                               const int8_t* k_codes, const int8_t* v_codes,
+                               const float* k_scales, const float* v_scales,
+                               const int32_t* block_table, int max_blocks_per_seq,
+                               const int32_t* seq_lens, int num_seqs,
+                               int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                               int num_blocks, float scale, int num_threads) {
+    kv_pool k = {NULL, k_codes, k_scales}, v = {NULL, v_codes, v_scales};
+    return attention_rows(out, n_items, item_seq, item_row, item_head, q, cu_q_lens, &k, &v, block_table,
+                          max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                          block_size, num_blocks, scale, num_threads);
 }
 
 /*

@@ -36,6 +36,7 @@ from typing import List, Optional
 import numpy as np
 
 NAN_SENTINEL = 0x7FC1  # a quiet-NaN bf16 bit pattern
+INT8_CODE_SENTINEL = -128  # never produced by the symmetric INT8 quantiser (codes are in [-127, 127])
 _DRAW_CHUNK = 1 << 25  # fp32 samples drawn per numpy call
 
 

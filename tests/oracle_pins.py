@@ -28,7 +28,7 @@ import os
 import numpy as np
 import torch
 
-from paged_kv_gqa_scatter_amd.workloads import NAN_SENTINEL, bf16_normal
+from paged_kv_gqa_scatter_amd.workloads import INT8_CODE_SENTINEL, NAN_SENTINEL, bf16_normal
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -157,8 +157,40 @@ def golden_pools(g):
     return kp, vp, table
 
 
+def int8_pools(shape):
+    """Empty INT8 pools: codes hold the sentinel -128, scales NaN."""
+    codes = np.full(shape, INT8_CODE_SENTINEL, np.int8)
+    scales = np.full(shape[:3], np.nan, np.float32)
+    return codes, codes.copy(), scales, scales.copy()
+
+
+def pin_golden_int8(orc, g, name):
+    if g["kind"] == "quantize_int8":
+        codes, scales = orc.quantize_int8(to_bf16_exact(g["rows"]))
+        assert np.array_equal(codes, np.asarray(g["expected_codes"], np.int8)), name
+        assert np.array_equal(scales, np.asarray(g["expected_scales"], np.float32)), name
+        return
+    shape = (g["num_blocks"], g["num_kv_heads"], g["block_size"], g["head_dim"])
+    kc, vc, ks, vs = int8_pools(shape)
+    table = np.asarray(g["block_table"], np.int32)
+    orc.kv_append_int8(kc, vc, ks, vs, to_bf16_exact(g["k_new"]), to_bf16_exact(g["v_new"]), g["cu_new_lens"],
+                       g["ctx_lens"], table)
+    ekc, evc, eks, evs = int8_pools(shape)
+    for w in g["expected_writes"]:
+        at = (w["block"], w["kv_head"], w["slot"])
+        ekc[at], evc[at], eks[at], evs[at] = w["k_codes"], w["v_codes"], w["k_scale"], w["v_scale"]
+    assert np.array_equal(kc, ekc) and np.array_equal(vc, evc), name
+    assert np.array_equal(ks, eks, equal_nan=True) and np.array_equal(vs, evs, equal_nan=True), name
+    out = orc.decode_int8(to_bf16_exact(g["q"]), kc, vc, ks, vs, table, g["seq_lens"], np.float32(g["scale"]))
+    err = np.abs(out - np.asarray(g["expected"], np.float64)).max()
+    assert err <= g["tol"], f"{name}: max err {err}"
+
+
 def pin_golden(orc, name):
     g = load_golden(name)
+    if g["kind"] in ("quantize_int8", "int8_append_decode"):
+        pin_golden_int8(orc, g, name)
+        return
     if g["kind"] == "append":
         shape = (g["num_blocks"], g["num_kv_heads"], g["block_size"], g["head_dim"])
         kp = np.full(shape, NAN_SENTINEL, np.uint16)
@@ -371,7 +403,137 @@ def pin_append_rejects_duplicate_slot(orc):
     raise AssertionError("duplicate slot not reported")
 
 
+# ----------------------------------------------------------------------------
+# INT8 KV cache
+# ----------------------------------------------------------------------------
+
+def _int8_rows(rng):
+    """bf16 rows of several magnitudes, with ties for the maximum, an all-zero
+    row and rows whose entries are all equal."""
+    rows = [bf16_normal(rng, (40, 64))]
+    for mag in (1e-3, 1e3, 3.0):
+        x = rng.standard_normal((20, 64)).astype(np.float32) * np.float32(mag)
+        rows.append(torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    special = np.zeros((4, 64), np.float32)
+    special[1, :] = -2.5            # every entry is the maximum
+    special[2, ::7] = 6.0           # the maximum appears several times, both signs
+    special[2, 3::7] = -6.0
+    special[3, 5] = 1e-37           # a single tiny value (its scale is a subnormal fp32)
+    rows.append(torch.from_numpy(special).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    return np.concatenate(rows)
+
+
+def pin_int8_quantizer_bounds(orc):
+    """Closed-form properties of symmetric absmax quantisation: codes in
+    [-127, 127]; the largest |x| of a row maps to +-127 exactly; every value
+    is recovered within half a step (|x - code * scale| <= scale / 2, plus the
+    fp32 rounding of the quotient); a zero row has scale 0 and codes 0."""
+    rows = _int8_rows(np.random.default_rng(81))
+    x = bf16_to_f64(rows)
+    codes, scales = orc.quantize_int8(rows)
+    c = codes.astype(np.float64)
+    s = scales.astype(np.float64)
+    amax = np.abs(x).max(axis=1)
+    assert (np.abs(c) <= 127).all()
+    nz = amax > 0
+    assert (s[~nz] == 0).all() and (c[~nz] == 0).all()
+    at_max = np.abs(x) == amax[:, None]
+    assert (np.abs(c)[at_max & nz[:, None]] == 127).all(), "the row maximum does not map to 127"
+    assert (np.sign(c) == np.sign(np.round(x / np.where(s > 0, s, 1)[:, None]))).all()
+    err = np.abs(x - c * s[:, None])
+    assert (err <= s[:, None] * (0.5 + 1e-6) + 1e-45).all(), f"max step error {np.max(err / np.where(s > 0, s, 1)[:, None])}"
+    assert np.allclose(s[nz], amax[nz] / 127, rtol=1e-6, atol=0)
+
+
+def pin_int8_quantizer_symmetries(orc):
+    """Negating a row negates its codes; scaling it by a power of two scales
+    the scale and keeps the codes (both exact in fp32)."""
+    rows = _int8_rows(np.random.default_rng(82))[:60]
+    codes, scales = orc.quantize_int8(rows)
+    neg = rows ^ np.uint16(0x8000)
+    nc, ns = orc.quantize_int8(neg)
+    assert np.array_equal(nc, -codes) and np.array_equal(ns, scales)
+    x = bf16_to_f64(rows) * 8.0  # exact in bf16 for these magnitudes
+    big = to_bf16_exact(x.astype(np.float32))
+    bc, bs = orc.quantize_int8(big)
+    assert np.array_equal(bc, codes) and np.array_equal(bs, scales * np.float32(8))
+
+
+def _int8_tiny(seed, S, hq, hkv, d, bs, seq_lens, q_lens):
+    """A paged INT8 case with codes and scales drawn directly (not by the
+    quantiser), and its dequantised contiguous K/V as fp64."""
+    rng = np.random.default_rng(seed)
+    t = Tiny(rng, S, hq, hkv, d, bs, seq_lens, q_lens)
+    kc, vc, ks, vs = int8_pools(t.kp.shape)
+    dense = []
+    for s in range(S):
+        L = int(t.seq_lens[s])
+        rows = {}
+        for name, codes, scales in (("k", kc, ks), ("v", vc, vs)):
+            c = rng.integers(-127, 128, size=(L, hkv, d)).astype(np.int8)
+            sc = (rng.uniform(0.001, 0.05, size=(L, hkv)) * rng.choice([1.0, 8.0], size=(L, hkv))).astype(np.float32)
+            for p in range(L):
+                blk, slot = t.table[s][p // bs], p % bs
+                codes[blk, :, slot, :] = c[p]
+                scales[blk, :, slot] = sc[p]
+            rows[name] = c.astype(np.float64) * sc.astype(np.float64)[:, :, None]
+        dense.append(rows)
+    return t, kc, vc, ks, vs, dense
+
+
+def pin_int8_attention_vs_sdpa(orc):
+    """Attention over an INT8 cache equals torch's fp64
+    scaled_dot_product_attention over the dequantised K/V (codes times their
+    row's scale, computed here by plain numpy), for decode rows and chunked
+    prefill rows, GQA groups 1, 2 and 4."""
+    for seed, args in ((91, (3, 4, 2, 16, 4, [7, 12, 1], [1, 3, 1])),
+                       (92, (2, 4, 1, 8, 16, [40, 19], [5, 19])),
+                       (93, (2, 2, 2, 8, 4, [9, 6], [9, 1]))):
+        t, kc, vc, ks, vs, dense = _int8_tiny(seed, *args)
+        G = t.hq // t.hkv
+        items = [(s, r, h) for s in range(t.S) for r in range(int(t.q_lens[s])) for h in range(t.hq)]
+        out = orc.attention_rows_int8(items, t.q, t.cu, kc, vc, ks, vs, t.table, t.seq_lens, t.hq, t.scale)
+        i = 0
+        for s in range(t.S):
+            n, L = int(t.q_lens[s]), int(t.seq_lens[s])
+            q = torch.from_numpy(bf16_to_f64(t.q[t.cu[s]:t.cu[s] + n])).permute(1, 0, 2)
+            k = torch.from_numpy(dense[s]["k"]).permute(1, 0, 2).repeat_interleave(G, dim=0)
+            v = torch.from_numpy(dense[s]["v"]).permute(1, 0, 2).repeat_interleave(G, dim=0)
+            pos = torch.arange(n) + (L - n)
+            mask = torch.arange(L)[None, :] <= pos[:, None]
+            ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=float(t.scale))
+            ref = ref.permute(1, 0, 2).reshape(n * t.hq, t.d).numpy()
+            got = out[i:i + n * t.hq]
+            i += n * t.hq
+            assert np.abs(got - ref).max() <= 1e-9, f"seed {seed} seq {s}: {np.abs(got - ref).max()}"
+
+
+def pin_int8_append_matches_indexing(orc):
+    """kv_append into INT8 pools writes, at each new row's slot, exactly the
+    quantiser's codes and scale of that row (placed by plain numpy indexing)
+    and touches no other slot."""
+    rng = np.random.default_rng(94)
+    t = Tiny(rng, 3, 4, 2, 8, 4, [9, 14, 3], [1, 1, 1])
+    kc, vc, ks, vs = int8_pools(t.kp.shape)
+    ctx = np.array([2, 5, 0], np.int32)
+    cu = np.concatenate([[0], np.cumsum(t.seq_lens - ctx)]).astype(np.int32)
+    k_new = np.concatenate([t.k[s][ctx[s]:] for s in range(3)])
+    v_new = np.concatenate([t.v[s][ctx[s]:] for s in range(3)])
+    orc.kv_append_int8(kc, vc, ks, vs, k_new, v_new, cu, ctx, t.table)
+    ekc, evc, eks, evs = int8_pools(t.kp.shape)
+    for s in range(3):
+        for name, rows, codes, scales in (("k", t.k[s], ekc, eks), ("v", t.v[s], evc, evs)):
+            c, sc = orc.quantize_int8(rows[ctx[s]:])
+            for i in range(c.shape[0]):
+                p = int(ctx[s]) + i
+                codes[t.table[s][p // t.bs], :, p % t.bs, :] = c[i]
+                scales[t.table[s][p // t.bs], :, p % t.bs] = sc[i]
+    assert np.array_equal(kc, ekc) and np.array_equal(vc, evc)
+    assert np.array_equal(ks, eks, equal_nan=True) and np.array_equal(vs, evs, equal_nan=True)
+
+
 ALL_PINS = [pin_all_golden, pin_vs_sdpa, pin_vs_dense, pin_constant_v, pin_scale_zero_mean, pin_single_key,
             pin_empty_sequence, pin_block_permutation, pin_block_size_16_vs_256, pin_decode_is_last_prefill_row,
             pin_chunked_equals_unchunked, pin_gqa_is_expanded_mha, pin_head_permutation_in_group,
-            pin_append_matches_indexing, pin_append_rejects_duplicate_slot]
+            pin_append_matches_indexing, pin_append_rejects_duplicate_slot, pin_int8_quantizer_bounds,
+            pin_int8_quantizer_symmetries, pin_int8_attention_vs_sdpa, pin_int8_append_matches_indexing]

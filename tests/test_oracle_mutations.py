@@ -21,15 +21,22 @@ MUTATIONS = {
     "block_index_modulo": ("int blk = table_row[j / block_size];\n        if (blk < 0",
                            "int blk = table_row[j % block_size];\n        if (blk < 0"),
     "no_normalisation": ("out_row[d] /= denom;", "out_row[d] /= 1.0;"),
-    "pool_head_major": ("const uint16_t* k = k_pool + (((size_t)blk * num_kv_heads + kv_head) * block_size",
-                        "const uint16_t* k = k_pool + (((size_t)kv_head * num_blocks + blk) * block_size"),
-    "v_wrong_head": ("const uint16_t* v = v_pool + (((size_t)blk * num_kv_heads + kv_head)",
-                     "const uint16_t* v = v_pool + (((size_t)blk * num_kv_heads + 0)"),
+    "pool_head_major": ("size_t krow = ((size_t)blk * num_kv_heads + kv_head) * block_size",
+                        "size_t krow = ((size_t)kv_head * num_blocks + blk) * block_size"),
+    "v_wrong_head": ("size_t vrow = ((size_t)blk * num_kv_heads + kv_head)",
+                     "size_t vrow = ((size_t)blk * num_kv_heads + 0)"),
     "q_row_ignores_offset": ("(size_t)(cu_q_lens[s] + r) * num_q_heads + h", "(size_t)r * num_q_heads + h"),
     "append_ignores_ctx": ("long pos = (long)ctx_lens[s] + (t - cu_new_lens[s]);",
                            "long pos = (long)(t - cu_new_lens[s]);"),
     "append_v_from_k": ("memcpy(v_pool + dst, v_new + src", "memcpy(v_pool + dst, k_new + src"),
     "append_slot_off_by_one": ("long slot = pos % block_size;", "long slot = (pos + 1) % block_size;"),
+    "int8_scale_over_128": ("float scale = amax / 127.0f;", "float scale = amax / 128.0f;"),
+    "int8_round_half_away": ("rintf(bf16_to_float(row[d]) / scale)", "roundf(bf16_to_float(row[d]) / scale)"),
+    "int8_truncate": ("rintf(bf16_to_float(row[d]) / scale)", "truncf(bf16_to_float(row[d]) / scale)"),
+    "int8_dequant_drops_scale": ("(double)pool->codes[row * head_dim + d] * (double)pool->scales[row]",
+                                 "(double)pool->codes[row * head_dim + d]"),
+    "int8_scale_of_wrong_row": ("(double)pool->scales[row]", "(double)pool->scales[row ^ 1]"),
+    "int8_append_v_from_k": ("v_scales + row, v_new + src", "v_scales + row, k_new + src"),
     "softmax_sum_skips_last": ("for (int j = 0; j < nkeys; ++j) {\n        z[j] = exp",
                                "for (int j = 0; j < nkeys - 1; ++j) {\n        z[j] = exp"),
 }
