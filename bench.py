@@ -16,9 +16,11 @@ The metric also names prefill: the Qwen3-8B causal prefill workload (4 prompts
 of 1024..4096 tokens) is timed in the same run and reported as causal TFLOP/s
 (4 * D * Hq flops per unmasked query/key pair) under ``prefill``.  Decode at a
 bandwidth-bound scale (3.24 GB of unique K/V, shared prefixes and 32K-token
-sequences) is reported under ``long_context_decode``, and the mixed
+sequences) is reported under ``long_context_decode``, the mixed
 continuous-batching step (64 decodes + two 512-row chunks) under
-``mixed_step``.
+``mixed_step``, and the INT8 KV cache (quantising append, decode over codes
+and per-row scales) on the headline step and the long-context decode under
+``int8_kv_cache``.
 
 Kernel durations are measured with HIP events on the stream the kernels run
 on; ``roofline`` relates the decode call to HBM peak, ``prefill.roofline`` the
@@ -57,6 +59,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long", action="store_true", help="skip the long-context decode measurement")
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed continuous-batching step")
+    ap.add_argument("--no-int8", action="store_true", help="skip the INT8 KV cache measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile-pass", action="store_true",
                     help="for counter runs: a few untimed steps of each kernel plus a reference device copy, no JSON")
@@ -321,6 +324,73 @@ def time_long_decode(args):
                              traffic_record("long_decode"))}}
 
 
+def time_int8(args, bf16_step_ms, bf16_long_ms):
+    """The INT8 KV cache (quantising kv_append_int8, paged_gqa_decode_int8) on
+    the headline decode step (both calls in one HIP graph per pool copy,
+    rotated past the last-level cache) and on the long-context decode; bytes
+    are the unique code and scale bytes a call must read (D + 4 per row)."""
+    import torch
+    from paged_kv_gqa_scatter_amd import workloads as W
+    from paged_kv_gqa_scatter_amd.runner import Int8DeviceCase
+
+    res = {}
+    case = W.config2_decode()
+    dec = case.steps[0].decode
+    nbytes = W.decode_unique_int8_kv_bytes(case, dec)
+    pool_bytes = case.pool_bytes * (case.head_dim + 4) // (2 * case.head_dim)
+    n_rot = max(1, -(-ROTATE_BYTES // pool_bytes))
+    dc = Int8DeviceCase(case, pools=n_rot)
+    dc.run_fills()
+    step = dc.steps[0]
+    steps = [dc.capture_step(0, pool=r) for r in range(n_rot)]
+    decodes = [dc.capture(lambda r=r: dc.decode(step["decode"], pool=r)) for r in range(n_rot)]
+    ms = _timed_replays(steps, args.steps, max(args.warmup // 2, 10))
+    dms = _timed_replays(decodes, args.steps, max(args.warmup // 2, 10))
+    del steps, decodes, dc
+    torch.cuda.empty_cache()
+    gbs = nbytes / (dms * 1e-3) / 1e9
+    res["decode_step"] = {
+        "workload": "the headline decode step over an INT8 cache: kv_append_int8 then paged_gqa_decode_int8, "
+                    "one HIP graph",
+        "ms_per_step": round(ms, 5), "bf16_fused_step_ms": round(bf16_step_ms, 5),
+        "decode_ms": round(dms, 5), "unique_kv_bytes": int(nbytes),
+        "roofline": {"bound": "hbm", "kernel": "paged_gqa_decode_int8 (decode_int8_kernel + decode_merge_kernel)",
+                     "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    if not args.no_long:
+        case = W.config5_prefix_long(draw_values=False)
+        dec = case.steps[0].decode
+        nbytes = W.decode_unique_int8_kv_bytes(case, dec)
+        dc = Int8DeviceCase(case)
+        dc.run_fills()
+        step = dc.steps[0]
+        dc.append(step["append"])
+        stream = torch.cuda.current_stream()
+        for _ in range(3):
+            dc.decode(step["decode"])
+        torch.cuda.synchronize()
+        n = max(5, args.prefill_steps)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:
+            a.record(stream)
+            dc.decode(step["decode"])
+            b.record(stream)
+        torch.cuda.synchronize()
+        lms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        del dc
+        torch.cuda.empty_cache()
+        gbs = nbytes / (lms * 1e-3) / 1e9
+        res["long_context_decode"] = {
+            "workload": "the long-context decode (256 seqs on a shared 4096-token prefix + 16 x 32768) over an "
+                        "INT8 cache",
+            "ms": round(lms, 5), "unique_kv_bytes": int(nbytes),
+            "speedup_vs_bf16": round(bf16_long_ms / lms, 3) if bf16_long_ms else None,
+            "roofline": {"bound": "hbm", "kernel": "paged_gqa_decode_int8 (decode_int8_kernel + decode_merge_kernel)",
+                         "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    return res
+
+
 def cpu_baseline(case, dec, kv_bytes, seconds):
     """The fp64 oracle on the same decode step, repeated for about `seconds`."""
     import oracle
@@ -401,6 +471,8 @@ def main():
             line["prefill"]["roofline"]["traffic"] = int(prec["hbm_bytes_per_launch"])
     if not args.no_long:
         line["long_context_decode"] = time_long_decode(args)
+    if not args.no_int8:
+        line["int8_kv_cache"] = time_int8(args, step_ms, line.get("long_context_decode", {}).get("ms"))
     if not args.no_mixed:
         line["mixed_step"] = time_mixed_step(args)
     if not args.no_cpu_baseline:

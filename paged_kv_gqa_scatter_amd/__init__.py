@@ -29,6 +29,7 @@ EXPORTS = ("pkv_abi_version", "pkv_status_string", "pkv_kv_append", "pkv_decode_
 BLOCK_EXPORTS = ("pkv_bm_create", "pkv_bm_destroy", "pkv_bm_available", "pkv_bm_seq_len", "pkv_bm_append",
                  "pkv_bm_free_sequence", "pkv_bm_block_table", "pkv_bm_cache_prefix", "pkv_bm_fork",
                  "pkv_copy_blocks")
+INT8_EXPORTS = ("pkv_kv_append_int8", "pkv_decode_int8_workspace_bytes", "pkv_paged_gqa_decode_int8")
 
 
 class PkvError(RuntimeError):
@@ -76,6 +77,13 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_bm_fork.argtypes = [P, I64, P, I32, P]
     lib.pkv_copy_blocks.restype = I32
     lib.pkv_copy_blocks.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, P]
+    lib.pkv_kv_append_int8.restype = I32
+    lib.pkv_kv_append_int8.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P]
+    lib.pkv_decode_int8_workspace_bytes.restype = SZ
+    lib.pkv_decode_int8_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I64]
+    lib.pkv_paged_gqa_decode_int8.restype = I32
+    lib.pkv_paged_gqa_decode_int8.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I64, I32, I32, I32, I32, I32, I32,
+                                              F32, P, SZ, P]
     lib.pkv_paged_gqa_prefill.restype = I32
     lib.pkv_paged_gqa_prefill.argtypes = [P, P, P, I32, I32, P, P, P, I32, P, I32, I32, I32, I32, I32, I32, I32,
                                           F32, P]
@@ -222,6 +230,97 @@ def paged_gqa_decode_append(q, k_new, v_new, k_pool, v_pool, block_table, seq_le
                                           S, Hq, Hkv, D, B, NB, float(scale), workspace.data_ptr(),
                                           workspace.numel(), _stream())
     _check(st, "paged_gqa_decode_append")
+    return out
+
+
+# ---- INT8 KV cache (include/pkv_int8.h): codes [NB][Hkv][B][D] int8, one
+# fp32 scale per slot [NB][Hkv][B] for K and for V
+
+def _int8_cache(k_codes, v_codes, k_scales, v_scales):
+    for t, name in ((k_codes, "k_codes"), (v_codes, "v_codes")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int8:
+            raise TypeError(f"{name} must be an int8 tensor")
+        if t.dim() != 4 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous 4-d CUDA tensor")
+    for t, name in ((k_scales, "k_scales"), (v_scales, "v_scales")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32:
+            raise TypeError(f"{name} must be a float32 tensor")
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous CUDA tensor")
+    if k_codes.shape != v_codes.shape:
+        raise ValueError("k_codes and v_codes must have the same shape")
+    NB, Hkv, B, D = k_codes.shape
+    if tuple(k_scales.shape) != (NB, Hkv, B) or tuple(v_scales.shape) != (NB, Hkv, B):
+        raise ValueError("scales must be [num_blocks][num_kv_heads][block_size]")
+    return NB, Hkv, B, D
+
+
+def empty_int8_cache(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, device="cuda"):
+    """Uninitialised INT8 cache tensors (k_codes, v_codes, k_scales, v_scales)."""
+    codes = (num_blocks, num_kv_heads, block_size, head_dim)
+    return (torch.empty(codes, dtype=torch.int8, device=device), torch.empty(codes, dtype=torch.int8, device=device),
+            torch.empty(codes[:3], dtype=torch.float32, device=device),
+            torch.empty(codes[:3], dtype=torch.float32, device=device))
+
+
+def kv_append_int8(k_codes, v_codes, k_scales, v_scales, k_new, v_new, cu_new_lens, ctx_lens, block_table) -> None:
+    """Quantise rows ``k_new/v_new [T][Hkv][D]`` (bf16) into the INT8 cache at
+    positions ``ctx_lens[s] ..`` of each sequence (see ``pkv_kv_append_int8``)."""
+    NB, Hkv, B, D = _int8_cache(k_codes, v_codes, k_scales, v_scales)
+    _bf16(k_new, "k_new", 3)
+    _bf16(v_new, "v_new", 3)
+    if k_new.shape != v_new.shape or tuple(k_new.shape[1:]) != (Hkv, D):
+        raise ValueError("k_new/v_new must be [T][num_kv_heads][head_dim]")
+    _i32(cu_new_lens, "cu_new_lens", 1)
+    _i32(ctx_lens, "ctx_lens", 1)
+    _i32(block_table, "block_table", 2)
+    S = ctx_lens.shape[0]
+    if cu_new_lens.shape[0] != S + 1 or block_table.shape[0] != S:
+        raise ValueError("cu_new_lens must have num_seqs+1 entries and block_table num_seqs rows")
+    st = lib().pkv_kv_append_int8(k_codes.data_ptr(), v_codes.data_ptr(), k_scales.data_ptr(),
+                                 v_scales.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), cu_new_lens.data_ptr(),
+                                 ctx_lens.data_ptr(), block_table.data_ptr(), block_table.shape[1], S,
+                                 k_new.shape[0], Hkv, D, B, NB, _stream())
+    _check(st, "kv_append_int8")
+
+
+def decode_int8_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                                max_seq_len: int, total_kv_tokens: int = 0) -> int:
+    n = lib().pkv_decode_int8_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                             total_kv_tokens)
+    if n == 0 and num_seqs > 0:
+        raise PkvError(2, "decode_int8_workspace_bytes")
+    return int(n)
+
+
+def paged_gqa_decode_int8(q, k_codes, v_codes, k_scales, v_scales, block_table, seq_lens, scale: float, *,
+                          max_seq_len: int, total_kv_tokens: int = 0, out=None, workspace=None):
+    """Decode over the INT8 cache: ``q [S][Hq][D]`` -> ``out [S][Hq][D]`` bf16."""
+    NB, Hkv, B, D = _int8_cache(k_codes, v_codes, k_scales, v_scales)
+    _bf16(q, "q", 3)
+    S, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError("q head_dim differs from the cache's")
+    _i32(block_table, "block_table", 2)
+    _i32(seq_lens, "seq_lens", 1)
+    if block_table.shape[0] != S or seq_lens.shape[0] != S:
+        raise ValueError("block_table and seq_lens need one row per sequence")
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _bf16(out, "out", 3)
+    if tuple(out.shape) != (S, Hq, D):
+        raise ValueError("out must be [S][Hq][D]")
+    need = decode_int8_workspace_bytes(S, Hq, Hkv, D, max_seq_len, total_kv_tokens) if S > 0 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
+    st = lib().pkv_paged_gqa_decode_int8(out.data_ptr(), q.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(),
+                                        k_scales.data_ptr(), v_scales.data_ptr(), block_table.data_ptr(),
+                                        block_table.shape[1], seq_lens.data_ptr(), max_seq_len, total_kv_tokens, S,
+                                        Hq, Hkv, D, B, NB, float(scale), workspace.data_ptr(), workspace.numel(),
+                                        _stream())
+    _check(st, "paged_gqa_decode_int8")
     return out
 
 

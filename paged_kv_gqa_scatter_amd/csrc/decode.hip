@@ -6,16 +6,8 @@
 // point here, because decode is bound by HBM bandwidth ("从零搭建AI工程能力"
 // section 3.3).  The design on gfx950:
 //
-//  * Work item = (sequence, KV head, chunk of `chunk` keys), one workgroup of
-//    4 waves.  The chunk is cut into tiles of 16 keys and wave w takes tiles
-//    w, w + 4, w + 8, ...; the waves' softmax states are merged through LDS.
-//    Short batches use a direct grid over (chunk, sequence, KV head) whose
-//    empty items exit at once; long, uneven batches use a persistent grid over
-//    a compact item list that each workgroup derives from seq_lens (a block
-//    scan in LDS).  Nothing is read back to the host, and the KV head sits in
-//    the low bits of the workgroup index, so items of one KV head run on one
-//    XCD (workgroups are dealt round-robin over the 8 XCDs) and K/V rows
-//    shared between sequences (a common prefix) are re-read from that XCD's L2.
+//  * Work items, grids and the merge of chunks are those of decode_common.h;
+//    here a tile is 16 keys.
 //  * Every wave streams its own tiles through a private ring of 4 LDS stages:
 //    the K and V rows of a tile (16 rows of one contiguous (block, head) slab,
 //    as B >= 16) are copied by global_load_lds_dwordx4, each wave load moving
@@ -43,94 +35,19 @@
 //    that position overwrites the row in its LDS stage with the new row once
 //    the tile's copy has landed (and the rows past it, so that no unwritten
 //    slot reaches the MFMA), so nothing waits for the store.
-//  * Chunks of a sequence write a normalised partial and its log2-sum-exp; a
-//    second kernel merges them in one pass with a running maximum
-//    (out = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M)).  The hand-off goes
-//    through a kernel boundary on purpose: the L2 is per XCD, so a device-scope
-//    fence inside the kernel would write back and invalidate an XCD's whole
-//    L2 under every other workgroup's streaming loads.  A sequence with one
-//    chunk is written directly (and the merge kernel is not launched when no
-//    sequence can have two); a sequence with no keys gets zeros.
-#include <math.h>
-
-#include "pkv_device.h"
-#include "pkv_launch.h"
+#include "decode_common.h"
 
 namespace pkv {
 namespace {
 
-constexpr int kDecodeThreads = 256;  // 4 waves share one work item
-constexpr int kDecodeWaves = kDecodeThreads / kWave;
-constexpr int kTileKeys = 16;        // keys per MFMA tile and per LDS stage of a wave
-constexpr int kStages = 4;           // LDS ring depth of a wave
-constexpr int kMaxTilesPerWave = 128;  // ids of a wave's tiles sit in two registers
-constexpr int kMaxChunk = kMaxTilesPerWave * kTileKeys * kDecodeWaves;
-constexpr int kMaxPersistentSeqs = 2048;  // chunk prefix kept in LDS
-constexpr int kXcds = 8;
+constexpr int kTileKeys = kDecodeTileKeys;  // keys per MFMA tile and per LDS stage of a wave
 constexpr int kPlanCus = 256;        // compute units the split plan assumes (MI355X)
 constexpr int kRoundTripTiles = 12;  // a load round trip, in tile compute times
-constexpr float kRescaleSlack = 8.f;  // log2 of the largest weight a stale running max may give
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // the bf16 pair (1.0, 1.0)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
-
-struct DecodeKernelArgs {
-    DecodeArgs a;
-    int32_t chunk;       // keys per work item (multiple of 256, at most kMaxChunk)
-    int32_t log2_block;
-    int32_t max_chunks;  // chunks of the longest sequence
-    int32_t persistent;  // 1: persistent grid over the compact item list
-    int64_t max_partials;
-    float* lse;         // [max_partials][Hq]
-    float* part;        // [max_partials][Hq][D]
-    float qk_scale_log2;
-};
-
-__device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
-
-__device__ __forceinline__ int num_chunks(int L, int chunk) { return L > 0 ? (L + chunk - 1) / chunk : 0; }
-
-// Wait until at most N vector-memory operations of this wave are in flight
-// (loads retire in issue order).  The memory clobber keeps the compiler from
-// moving LDS reads above it.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Exclusive prefix of chunk counts over all sequences into s_prefix[0..S];
-// every thread of the block takes part.
-__device__ void chunk_prefix(const DecodeKernelArgs& p, int32_t* s_prefix, int32_t* s_wave) {
-    const int S = p.a.num_seqs;
-    const int cap = p.a.max_blocks_per_seq << p.log2_block;
-    const int tid = threadIdx.x;
-    const int per = (S + kDecodeThreads - 1) / kDecodeThreads;
-    const int lo = min(S, tid * per), hi = min(S, lo + per);
-    int sum = 0;
-    for (int i = lo; i < hi; ++i) sum += num_chunks(clamp_len(p.a.seq_lens[i], cap), p.chunk);
-    const int lane = tid & 63, wave = tid >> 6;
-    int incl = sum;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        int v = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += v;
-    }
-    if (lane == 63) s_wave[wave] = incl;
-    __syncthreads();
-    int wave_off = 0;
-    for (int w = 0; w < wave; ++w) wave_off += s_wave[w];
-    incl += wave_off;
-    int run = incl - sum;
-    for (int i = lo; i < hi; ++i) {
-        s_prefix[i] = run;
-        run += num_chunks(clamp_len(p.a.seq_lens[i], cap), p.chunk);
-    }
-    if (tid == kDecodeThreads - 1) s_prefix[S] = incl;
-    __syncthreads();
-}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ s16x4 as_s16x4(u32x2 v) { return __builtin_bit_cast(s16x4, v); }
@@ -190,19 +107,6 @@ struct Stages {
     uint16_t* v[kStages];
 };
 
-// LDS byte address of a __shared__ object (what M0 holds for an LDS DMA).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// global_load_lds_dwordx4 with a scalar base: lane l's 16 bytes at
-// base + voff land at LDS byte address lds + 16 l.  Written as inline asm so
-// that the compiler, which cannot tell the four stages apart, does not wait
-// for every copy in flight before each LDS read; the ring's waits are
-// explicit (wait_vmcnt).
-__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
-}
 
 // Copy tile rows [kt, kt + 16) of (block blk, KV head g) into a stage; rows at
 // or past kend repeat row kend - 1.
@@ -232,14 +136,6 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, int log2_block, 
     }
 }
 
-// One wave's running softmax state: O^T fragments (rows = dims, column =
-// this lane's head), the head's running max and this lane's share of the sum.
-template <int D>
-struct WaveState {
-    f32x4 acc[D / 16];
-    float m;
-    float l;
-};
 
 // Per-wave view of the item.
 template <int D>
@@ -379,47 +275,6 @@ __device__ __forceinline__ void wave_tiles(const WaveItem<D>& w, WaveState<D>& w
     }
 }
 
-// Merge kernel: one workgroup per (sequence, KV head) merges that sequence's
-// chunk partials into the bf16 output, one pass with a running maximum so all
-// loads are independent.  Sequences with fewer than two chunks were finished
-// by the split kernel.
-template <int D, int G>
-constexpr int elems_per_thread() { return (G * D + kDecodeThreads - 1) / kDecodeThreads; }
-
-template <int D, int G>
-__global__ __launch_bounds__(kDecodeThreads) void decode_merge_kernel(DecodeKernelArgs p, const int32_t* prefix) {
-    constexpr int kElems = elems_per_thread<D, G>();  // outputs per thread
-    const int Hkv = p.a.num_kv_heads, Hq = p.a.num_q_heads;
-    const int g = blockIdx.x % Hkv, s = blockIdx.x / Hkv;
-    const int cap = p.a.max_blocks_per_seq << p.log2_block;
-    const int n = num_chunks(clamp_len(p.a.seq_lens[s], cap), p.chunk);
-    if (n < 2) return;
-    const int64_t base = p.persistent ? (int64_t)prefix[s] : (int64_t)s * p.max_chunks;
-    if (base + n > p.max_partials) return;  // precondition broken: no partials to merge
-    const int e0 = threadIdx.x * kElems;
-    if (e0 >= G * D) return;
-    const int h = e0 / D, d0 = e0 % D;
-    const int qh = g * G + h;
-    float mx = -INFINITY, den = 0.f, num[kElems];
-#pragma unroll
-    for (int k = 0; k < kElems; ++k) num[k] = 0.f;
-#pragma unroll 8
-    for (int i = 0; i < n; ++i) {
-        const float li = p.lse[(base + i) * Hq + qh];
-        const float* src = p.part + ((base + i) * Hq + qh) * D + d0;
-        const float m_new = fmaxf(mx, li);
-        const float a_old = fast_exp2(mx - m_new);  // 0 on the first partial
-        const float w = fast_exp2(li - m_new);
-        den = den * a_old + w;
-#pragma unroll
-        for (int k = 0; k < kElems; ++k) num[k] = num[k] * a_old + w * src[k];
-        mx = m_new;
-    }
-    const float inv = 1.f / den;
-    uint16_t* dst = p.a.out + ((int64_t)s * Hq + qh) * D + d0;
-#pragma unroll
-    for (int k = 0; k < kElems; ++k) dst[k] = __builtin_bit_cast(uint16_t, (__bf16)(num[k] * inv));
-}
 
 // What a work item needs before its first K/V load, fetched in one round
 // trip: the sequence length, this lane's query fragments and the block ids
@@ -432,12 +287,6 @@ struct ItemInputs {
     u32x4 kn, vn;  // decode_append: this lane's piece of the new K/V row
 };
 
-// This wave's index, known to the compiler to be the same on every lane.
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-
-// Wait for every vector-memory operation of the wave, in a form the
-// compiler's own wait placement sees (so it adds none for those loads later).
-__device__ __forceinline__ void wait_all_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0) only
 
 template <int D, int G>
 __device__ __forceinline__ ItemInputs<D> load_item_inputs(const DecodeKernelArgs& p, int s, int g, int c) {
@@ -468,14 +317,6 @@ __device__ __forceinline__ ItemInputs<D> load_item_inputs(const DecodeKernelArgs
     return in;
 }
 
-// LDS of one workgroup besides the stages: the waves' softmax states.
-template <int D, int G>
-struct __attribute__((aligned(16))) DecodeShared {
-    float o[kDecodeWaves][G][D];
-    float m[kDecodeWaves][G];
-    float l[kDecodeWaves][G];
-    int32_t wave_sum[kDecodeWaves];
-};
 
 // One work item: chunk c of sequence s, KV head g; `slot` is its partial slot.
 template <int D, int G, typename Prefetch>
@@ -523,55 +364,7 @@ __device__ __forceinline__ void decode_item(const DecodeKernelArgs& p, DecodeSha
     prefetch();
     wave_tiles<D>(w, ws);
 
-    // ---- wave totals: the sum over the head's four lane groups; O^T rows to LDS
-    float l = ws.l + __shfl_xor(ws.l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
-    const int h = lane & 15, j = lane >> 4;
-    if (h < G) {
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4*>(&sh.o[wave][h][16 * db + 4 * j]) = ws.acc[db];
-        if (j == 0) {
-            sh.m[wave][h] = ws.m;
-            sh.l[wave][h] = l;
-        }
-    }
-    __syncthreads();
-
-    // ---- merge the 4 waves: thread -> kElems consecutive outputs of one head
-    constexpr int kElems = elems_per_thread<D, G>();
-    const int e0 = threadIdx.x * kElems;
-    const bool active = e0 < G * D;  // fewer outputs than threads when G * D < 256
-    const int hh = active ? e0 / D : 0, d0 = active ? e0 % D : 0;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < kDecodeWaves; ++v) mx = fmaxf(mx, sh.m[v][hh]);
-    float den = 0.f, val[kElems];
-#pragma unroll
-    for (int k = 0; k < kElems; ++k) val[k] = 0.f;
-#pragma unroll
-    for (int v = 0; v < kDecodeWaves; ++v) {
-        const float sc = sh.m[v][hh] == -INFINITY ? 0.f : fast_exp2(sh.m[v][hh] - mx);  // a wave without keys adds 0
-        den += sh.l[v][hh] * sc;
-#pragma unroll
-        for (int k = 0; k < kElems; ++k) val[k] += sh.o[v][hh][d0 + k] * sc;
-    }
-    const int qh = g * G + hh;
-    const float inv = 1.f / den;
-    if (nchunks == 1) {
-        uint16_t* dst = a.out + ((int64_t)s * Hq + qh) * D + d0;
-        if (active)
-#pragma unroll
-            for (int k = 0; k < kElems; ++k) dst[k] = __builtin_bit_cast(uint16_t, (__bf16)(val[k] * inv));
-        __syncthreads();  // LDS is reused by the next item
-        return;
-    }
-    if (active && slot < p.max_partials) {
-        float* dst = p.part + (slot * Hq + qh) * D + d0;
-#pragma unroll
-        for (int k = 0; k < kElems; ++k) dst[k] = val[k] * inv;
-        if (d0 == 0) p.lse[slot * Hq + qh] = mx + log2f(den);
-    }
-    __syncthreads();  // LDS is reused by the next item
+    finish_item<D, G>(p, sh, ws, s, g, nchunks, slot);
 }
 
 template <int D, int G>
@@ -596,130 +389,35 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeKernelArgs
     st.v[2] = sV2;
     st.v[3] = sV3;
 
-    const int S = p.a.num_seqs;
-    const int Hq = p.a.num_q_heads;
-    const int Hkv = p.a.num_kv_heads;
-    const int cap = p.a.max_blocks_per_seq << p.log2_block;
-
-    if (!p.persistent) {
-        // direct grid: workgroup -> (chunk, sequence, KV head), KV head fastest
-        int idx = blockIdx.x;
-        const int g = idx % Hkv;
-        idx /= Hkv;
-        const int s = idx % S;
-        const int c = idx / S;
-        const ItemInputs<D> in = load_item_inputs<D, G>(p, s, g, c);  // before the exit test: one round trip
-        const int L = clamp_len(in.L_raw, cap);
-        const int n = num_chunks(L, p.chunk);
-        if (L == 0 && c == 0)  // a sequence without keys: zero rows
-            for (int e = threadIdx.x; e < G * D; e += kDecodeThreads) p.a.out[((int64_t)s * Hq + g * G) * D + e] = 0;
-        if (c >= n) return;
-        decode_item<D, G>(p, sh, st, s, g, c, n, (int64_t)s * p.max_chunks + c, in, [] {});
-        return;
-    }
-
-    extern __shared__ int32_t s_prefix[];  // num_seqs + 1
-    chunk_prefix(p, s_prefix, sh.wave_sum);
-    if (blockIdx.x == 0) {  // the merge kernel's view of the list; sequences without keys: zero rows
-        for (int i = threadIdx.x; i <= S; i += kDecodeThreads) prefix_out[i] = s_prefix[i];
-        const int pieces = Hq * D / 8;
-        for (int64_t e = threadIdx.x; e < (int64_t)S * pieces; e += kDecodeThreads) {
-            const int s = (int)(e / pieces);
-            if (s_prefix[s + 1] == s_prefix[s]) store16(p.a.out + e * 8, u32x4{0u, 0u, 0u, 0u});
-        }
-    }
-    // item i = (chunk i / Hkv of the compact list, KV head i % Hkv); the grid is
-    // a multiple of 8 workgroups, so a workgroup only meets KV heads congruent
-    // to its XCD modulo 8
-    const int64_t total_items = (int64_t)s_prefix[S] * Hkv;
-    struct Item {
-        int s, g, c, n, chunk;
-    };
-    auto locate = [&](int64_t item) {
-        Item it;
-        it.chunk = (int)(item / Hkv);
-        it.g = (int)(item - (int64_t)it.chunk * Hkv);
-        int lo = 0, hi = S - 1;  // the sequence owning this chunk: last s with s_prefix[s] <= chunk
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_prefix[mid] <= it.chunk) lo = mid; else hi = mid - 1;
-        }
-        it.s = lo;
-        it.n = s_prefix[lo + 1] - s_prefix[lo];
-        it.c = it.chunk - s_prefix[lo];
-        return it;
-    };
-    int64_t item = blockIdx.x;
-    if (item >= total_items) return;
-    Item cur = locate(item);
-    ItemInputs<D> in = load_item_inputs<D, G>(p, cur.s, cur.g, cur.c);
-    for (; item < total_items; item += gridDim.x) {
-        const int64_t nxt = item + gridDim.x;
-        Item next = cur;
-        ItemInputs<D> in_next = in;
-        decode_item<D, G>(p, sh, st, cur.s, cur.g, cur.c, cur.n, cur.chunk, in, [&] {
-            if (nxt < total_items) {
-                next = locate(nxt);
-                in_next = load_item_inputs<D, G>(p, next.s, next.g, next.c);
-            }
+    run_items<D, G>(
+        p, sh, prefix_out, [&](int s, int g, int c) { return load_item_inputs<D, G>(p, s, g, c); },
+        [&](int s, int g, int c, int n, int64_t slot, const ItemInputs<D>& in, auto prefetch) {
+            decode_item<D, G>(p, sh, st, s, g, c, n, slot, in, prefetch);
         });
-        cur = next;
-        in = in_next;
-    }
-}
-
-template <int D, int G>
-hipError_t launch_typed(const DecodeKernelArgs& kp, int32_t* prefix, hipStream_t stream) {
-    const DecodeArgs& a = kp.a;
-    if (!kp.persistent) {
-        const int64_t blocks = (int64_t)kp.max_chunks * a.num_seqs * a.num_kv_heads;
-        hipLaunchKernelGGL((decode_kernel<D, G>), dim3((unsigned)blocks), dim3(kDecodeThreads), 0, stream, kp, prefix);
-    } else {
-        const size_t lds = sizeof(int32_t) * (size_t)(a.num_seqs + 1);
-        int per_cu = 0;
-        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, G>, kDecodeThreads, lds);
-        if (e != hipSuccess) return e;
-        if (per_cu < 1) per_cu = 1;
-        const int64_t direct = (int64_t)a.num_seqs * kp.max_chunks;
-        const int64_t items = (kp.max_partials < direct ? kp.max_partials : direct) * a.num_kv_heads;
-        int64_t blocks = (items + kXcds - 1) / kXcds * kXcds;
-        int64_t resident = (int64_t)per_cu * device_cu_count() / kXcds * kXcds;
-        if (resident < kXcds) resident = kXcds;
-        if (blocks > resident) blocks = resident;
-        hipLaunchKernelGGL((decode_kernel<D, G>), dim3((unsigned)blocks), dim3(kDecodeThreads), lds, stream, kp, prefix);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || kp.max_chunks < 2) return e;  // no sequence has two chunks: nothing to merge
-    hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3((unsigned)(a.num_seqs * a.num_kv_heads)),
-                       dim3(kDecodeThreads), 0, stream, kp, (const int32_t*)prefix);
-    return hipGetLastError();
-}
-
-int ilog2(int x) {
-    int r = 0;
-    while ((1 << r) < x) ++r;
-    return r;
 }
 
 }  // namespace
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                       int32_t max_seq_len, int64_t total_kv_tokens) {
+                       int32_t max_seq_len, int64_t total_kv_tokens, int32_t tile_keys) {
     DecodePlan pl{};
     const int64_t bound_tokens = (int64_t)num_seqs * max_seq_len;
     int64_t total = total_kv_tokens > 0 ? total_kv_tokens : bound_tokens;
     if (total > bound_tokens) total = bound_tokens;
-    // chunk: the power of two in [256, kMaxChunk] with the least estimated
-    // time, counted in tile times: rounds of resident workgroups (one per CU
-    // at D = 128, two at D = 64, on a 256-CU part) times the round's length,
-    // a load round trip (about 12 tiles) plus the tiles each wave streams.
-    // The item count is a bound (each sequence adds at most one partial chunk).
+    // chunk: the power of two in [16 tiles, 512 tiles] with the least
+    // estimated time, counted in tile times (a tile of either cache format
+    // moves about 8 KB per wave at D = 128): rounds of resident workgroups
+    // (one per CU at D = 128, two at D = 64, on a 256-CU part) times the
+    // round's length, a load round trip (about 12 tiles) plus the tiles each
+    // wave streams.  The item count is a bound (each sequence adds at most one
+    // partial chunk).
     const int64_t slots = (int64_t)kPlanCus * (head_dim == 64 ? 2 : 1);
-    int chunk = kDecodeWaves * 4 * kTileKeys;
+    const int max_chunk = kMaxTilesPerWave * tile_keys * kDecodeWaves;
+    int chunk = kDecodeWaves * 4 * tile_keys;
     int64_t best = -1;
-    for (int c = chunk; c <= kMaxChunk; c *= 2) {
+    for (int c = chunk; c <= max_chunk; c *= 2) {
         const int64_t items = ((total + c - 1) / c + num_seqs) * num_kv_heads;
-        const int64_t cost = (items + slots - 1) / slots * (kRoundTripTiles + c / (kDecodeWaves * kTileKeys));
+        const int64_t cost = (items + slots - 1) / slots * (kRoundTripTiles + c / (kDecodeWaves * tile_keys));
         if (best < 0 || cost < best) {
             best = cost;
             chunk = c;
@@ -760,17 +458,17 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     const int G = a.num_q_heads / a.num_kv_heads;
     if (a.head_dim == 128) {
         switch (G) {
-            case 1: return launch_typed<128, 1>(kp, prefix, stream);
-            case 2: return launch_typed<128, 2>(kp, prefix, stream);
-            case 4: return launch_typed<128, 4>(kp, prefix, stream);
-            default: return launch_typed<128, 8>(kp, prefix, stream);
+            case 1: return launch_split<128, 1>(decode_kernel<128, 1>, kp, prefix, stream);
+            case 2: return launch_split<128, 2>(decode_kernel<128, 2>, kp, prefix, stream);
+            case 4: return launch_split<128, 4>(decode_kernel<128, 4>, kp, prefix, stream);
+            default: return launch_split<128, 8>(decode_kernel<128, 8>, kp, prefix, stream);
         }
     }
     switch (G) {
-        case 1: return launch_typed<64, 1>(kp, prefix, stream);
-        case 2: return launch_typed<64, 2>(kp, prefix, stream);
-        case 4: return launch_typed<64, 4>(kp, prefix, stream);
-        default: return launch_typed<64, 8>(kp, prefix, stream);
+        case 1: return launch_split<64, 1>(decode_kernel<64, 1>, kp, prefix, stream);
+        case 2: return launch_split<64, 2>(decode_kernel<64, 2>, kp, prefix, stream);
+        case 4: return launch_split<64, 4>(decode_kernel<64, 4>, kp, prefix, stream);
+        default: return launch_split<64, 8>(decode_kernel<64, 8>, kp, prefix, stream);
     }
 }
 

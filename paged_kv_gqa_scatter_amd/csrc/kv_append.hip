@@ -58,6 +58,71 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendArgs a)
     store16(a.v_pool + dst, vv);
 }
 
+// Symmetric INT8 quantisation of one row held by `kPieces` consecutive lanes,
+// 8 values each: scale = max|x| / 127 and code = x / scale rounded to the
+// nearest integer, ties to even, in fp32 with IEEE division (an all-zero row
+// has scale 0 and codes 0).  Returns this lane's 8 codes; *scale gets the
+// row's scale on every lane of the row.
+template <int kPieces>
+__device__ __forceinline__ u32x2 quantize_piece(u32x4 x, float* scale) {
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_lo(x[i]);
+        f[2 * i + 1] = bf16_hi(x[i]);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+    for (int off = kPieces / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+    const float sc = amax / 127.f;
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float c = sc > 0.f ? fminf(fmaxf(rintf(f[i] / sc), -127.f), 127.f) : 0.f;
+        w[i / 4] |= ((uint32_t)(int32_t)c & 0xFFu) << (8 * (i % 4));
+    }
+    *scale = sc;
+    return u32x2{w[0], w[1]};
+}
+
+// kv_append into an INT8 cache ("从零搭建AI工程能力：手写KV Cache与动态批处理实战"
+// section 3.2): the placement of kv_append_kernel, each (token, KV head) row
+// quantised on the way in.  A thread holds one 16-byte piece (8 values) of K
+// and of V; the D / 8 lanes of a row find its maximum with a butterfly.
+template <int D>
+__global__ __launch_bounds__(kAppendThreads) void kv_append_int8_kernel(AppendArgs a) {
+    constexpr int kPieces = D / 8;
+    const int64_t idx = (int64_t)blockIdx.x * kAppendThreads + threadIdx.x;
+    const int64_t total = (int64_t)a.total_new_tokens * a.num_kv_heads * kPieces;
+    if (idx >= total) return;  // whole rows only: a row's lanes all stay or all leave
+    const int piece = (int)(idx % kPieces);
+    const int64_t row_head = idx / kPieces;
+    const int g = (int)(row_head % a.num_kv_heads);
+    const int t = (int)(row_head / a.num_kv_heads);
+
+    const int64_t src = ((int64_t)t * a.num_kv_heads + g) * D + piece * 8;
+    float k_scale, v_scale;
+    const u32x2 kq = quantize_piece<kPieces>(load16(a.k_new + src), &k_scale);
+    const u32x2 vq = quantize_piece<kPieces>(load16(a.v_new + src), &v_scale);
+
+    const int s = owner_seq(a.cu_new_lens, a.num_seqs, a.total_new_tokens, t);
+    const int64_t pos = (int64_t)a.ctx_lens[s] + (t - a.cu_new_lens[s]);
+    const int64_t lblock = pos / a.block_size;
+    if (pos < 0 || lblock >= a.max_blocks_per_seq) return;  // precondition broken: skip
+    const int blk = a.block_table[(int64_t)s * a.max_blocks_per_seq + lblock];
+    if (blk < 0 || blk >= a.num_blocks) return;
+    const int slot = (int)(pos & (a.block_size - 1));
+    const int64_t row = ((int64_t)blk * a.num_kv_heads + g) * a.block_size + slot;
+    *reinterpret_cast<u32x2*>(a.k_codes + row * D + piece * 8) = kq;
+    *reinterpret_cast<u32x2*>(a.v_codes + row * D + piece * 8) = vq;
+    if (piece == 0) {
+        a.k_scales[row] = k_scale;
+        a.v_scales[row] = v_scale;
+    }
+}
+
 // Copy-on-write: block src[p] -> dst[p] of both pools, one 16-byte piece per
 // thread; blockIdx.y is the pair.
 __global__ __launch_bounds__(kAppendThreads) void copy_blocks_kernel(CopyBlocksArgs a) {
@@ -83,10 +148,16 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream) {
     const int64_t total = (int64_t)a.total_new_tokens * a.num_kv_heads * (a.head_dim / 8);
     if (total == 0) return hipSuccess;
     const int64_t blocks = (total + kAppendThreads - 1) / kAppendThreads;
-    if (a.head_dim == 128)
+    if (a.k_codes) {
+        if (a.head_dim == 128)
+            hipLaunchKernelGGL(kv_append_int8_kernel<128>, dim3((unsigned)blocks), dim3(kAppendThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL(kv_append_int8_kernel<64>, dim3((unsigned)blocks), dim3(kAppendThreads), 0, stream, a);
+    } else if (a.head_dim == 128) {
         hipLaunchKernelGGL(kv_append_kernel<128>, dim3((unsigned)blocks), dim3(kAppendThreads), 0, stream, a);
-    else
+    } else {
         hipLaunchKernelGGL(kv_append_kernel<64>, dim3((unsigned)blocks), dim3(kAppendThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

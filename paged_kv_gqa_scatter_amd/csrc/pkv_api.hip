@@ -7,6 +7,7 @@
 
 #include "../../include/pkv.h"
 #include "../../include/pkv_blocks.h"
+#include "../../include/pkv_int8.h"
 #include "pkv_launch.h"
 
 namespace pkv {
@@ -90,6 +91,31 @@ int32_t pkv_kv_append(uint16_t* k_pool, uint16_t* v_pool, const uint16_t* k_new,
     return hip_status(launch_kv_append(a, static_cast<hipStream_t>(stream)));
 }
 
+int32_t pkv_kv_append_int8(int8_t* k_codes, int8_t* v_codes, float* k_scales, float* v_scales, const uint16_t* k_new,
+                           const uint16_t* v_new, const int32_t* cu_new_lens, const int32_t* ctx_lens,
+                           const int32_t* block_table, int32_t max_blocks_per_seq, int32_t num_seqs,
+                           int32_t total_new_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, void* stream) {
+    if (num_seqs < 0 || total_new_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0 || max_blocks_per_seq < 0)
+        return PKV_ERR_BAD_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return PKV_ERR_BAD_SHAPE;
+    if (!pow2_in(block_size, 32, 256)) return PKV_ERR_BAD_SHAPE;
+    if (total_new_tokens > 0 && (num_seqs == 0 || num_blocks == 0 || max_blocks_per_seq == 0))
+        return PKV_ERR_BAD_SHAPE;
+    if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PKV_ERR_BAD_SHAPE;
+    if (total_new_tokens == 0) return PKV_OK;
+    if (!k_codes || !v_codes || !k_scales || !v_scales || !k_new || !v_new || !cu_new_lens || !ctx_lens ||
+        !block_table)
+        return PKV_ERR_NULL_POINTER;
+    if (!aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_scales) || !aligned16(v_scales) ||
+        !aligned16(k_new) || !aligned16(v_new))
+        return PKV_ERR_MISALIGNED;
+    AppendArgs a{nullptr, nullptr, k_new, v_new, cu_new_lens, ctx_lens, block_table, max_blocks_per_seq,
+                 num_seqs, total_new_tokens, num_kv_heads, head_dim, block_size, num_blocks,
+                 k_codes, v_codes, k_scales, v_scales};
+    return hip_status(launch_kv_append(a, static_cast<hipStream_t>(stream)));
+}
+
 int32_t pkv_copy_blocks(uint16_t* k_pool, uint16_t* v_pool, const int32_t* src_ids, const int32_t* dst_ids,
                         int32_t n_pairs, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                         int32_t num_blocks, void* stream) {
@@ -125,16 +151,27 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
                                   int32_t max_seq_len, int64_t total_kv_tokens) {
     if (num_seqs < 0 || num_seqs > kMaxDecodeSeqs || max_seq_len < 0) return 0;
     if (check_heads(num_q_heads, num_kv_heads, head_dim, 16) != PKV_OK) return 0;
-    return plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, total_kv_tokens).bytes;
+    return plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, total_kv_tokens, kDecodeTileKeys)
+        .bytes;
+}
+
+size_t pkv_decode_int8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t max_seq_len, int64_t total_kv_tokens) {
+    if (num_seqs < 0 || num_seqs > kMaxDecodeSeqs || max_seq_len < 0) return 0;
+    if (check_heads(num_q_heads, num_kv_heads, head_dim, 32) != PKV_OK) return 0;
+    return plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, total_kv_tokens,
+                       kDecodeInt8TileKeys)
+        .bytes;
 }
 
 }  // extern "C"
 
 namespace {
 
-// Validation shared by the two decode entry points; on PKV_OK, `a` and `pl`
-// describe the launch (nothing to launch when num_seqs == 0).
-int32_t check_decode(DecodeArgs& a, DecodePlan& pl) {
+// Validation shared by the decode entry points; on PKV_OK, `a` and `pl`
+// describe the launch (nothing to launch when num_seqs == 0).  k / v are the
+// cache arrays of the call (bf16 pools or INT8 codes); tile_keys picks the plan.
+int32_t check_decode(DecodeArgs& a, DecodePlan& pl, const void* k, const void* v, int32_t tile_keys) {
     int32_t st = check_heads(a.num_q_heads, a.num_kv_heads, a.head_dim, a.block_size);
     if (st != PKV_OK) return st;
     if (a.num_seqs < 0 || a.num_seqs > kMaxDecodeSeqs || a.max_seq_len < 0 || a.num_blocks < 0 ||
@@ -143,11 +180,11 @@ int32_t check_decode(DecodeArgs& a, DecodePlan& pl) {
     if ((int64_t)a.max_seq_len > (int64_t)a.max_blocks_per_seq * a.block_size) return PKV_ERR_BAD_SHAPE;
     if (a.num_seqs == 0) return PKV_OK;
     if (!a.out || !a.q || !a.block_table || !a.seq_lens) return PKV_ERR_NULL_POINTER;
-    if (a.max_seq_len > 0 && (!a.k_pool || !a.v_pool)) return PKV_ERR_NULL_POINTER;
-    if (!aligned16(a.out) || !aligned16(a.q) || !aligned16(a.k_pool) || !aligned16(a.v_pool) ||
-        !aligned16(a.workspace))
+    if (a.max_seq_len > 0 && (!k || !v)) return PKV_ERR_NULL_POINTER;
+    if (!aligned16(a.out) || !aligned16(a.q) || !aligned16(k) || !aligned16(v) || !aligned16(a.workspace))
         return PKV_ERR_MISALIGNED;
-    pl = plan_decode(a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim, a.max_seq_len, a.total_kv_tokens);
+    pl = plan_decode(a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim, a.max_seq_len, a.total_kv_tokens,
+                     tile_keys);
     if (!a.workspace || a.workspace_bytes < pl.bytes) return PKV_ERR_WORKSPACE;
     if (a.total_kv_tokens <= 0) a.total_kv_tokens = (int64_t)a.num_seqs * a.max_seq_len;
     return PKV_OK;
@@ -166,7 +203,7 @@ int32_t pkv_paged_gqa_decode(uint16_t* out, const uint16_t* q, const uint16_t* k
                  num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, workspace,
                  workspace_bytes};
     DecodePlan pl{};
-    const int32_t st = check_decode(a, pl);
+    const int32_t st = check_decode(a, pl, k_pool, v_pool, kDecodeTileKeys);
     if (st != PKV_OK || num_seqs == 0) return st;
     return hip_status(launch_decode(a, pl, static_cast<hipStream_t>(stream)));
 }
@@ -181,11 +218,29 @@ int32_t pkv_paged_gqa_decode_append(uint16_t* out, const uint16_t* q, const uint
                  num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, workspace,
                  workspace_bytes, k_new, v_new, k_pool, v_pool};
     DecodePlan pl{};
-    const int32_t st = check_decode(a, pl);
+    const int32_t st = check_decode(a, pl, k_pool, v_pool, kDecodeTileKeys);
     if (st != PKV_OK || num_seqs == 0) return st;
     if (!k_new || !v_new) return PKV_ERR_NULL_POINTER;
     if (!aligned16(k_new) || !aligned16(v_new)) return PKV_ERR_MISALIGNED;
     return hip_status(launch_decode(a, pl, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pkv_paged_gqa_decode_int8(uint16_t* out, const uint16_t* q, const int8_t* k_codes, const int8_t* v_codes,
+                                  const float* k_scales, const float* v_scales, const int32_t* block_table,
+                                  int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                  int64_t total_kv_tokens, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                  float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    if (block_size < 32) return PKV_ERR_BAD_SHAPE;  // a 32-key tile lies in one block
+    DecodeArgs a{out, q, nullptr, nullptr, block_table, max_blocks_per_seq, seq_lens, max_seq_len, total_kv_tokens,
+                 num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, workspace,
+                 workspace_bytes, nullptr, nullptr, nullptr, nullptr, k_codes, v_codes, k_scales, v_scales};
+    DecodePlan pl{};
+    const int32_t st = check_decode(a, pl, k_codes, v_codes, kDecodeInt8TileKeys);
+    if (st != PKV_OK || num_seqs == 0) return st;
+    if (max_seq_len > 0 && (!k_scales || !v_scales)) return PKV_ERR_NULL_POINTER;
+    if (!aligned16(k_scales) || !aligned16(v_scales)) return PKV_ERR_MISALIGNED;
+    return hip_status(launch_decode_int8(a, pl, static_cast<hipStream_t>(stream)));
 }
 
 int32_t pkv_paged_gqa_prefill(uint16_t* out, const uint16_t* q, const int32_t* cu_q_lens, int32_t total_q_tokens,

@@ -23,6 +23,13 @@ struct AppendArgs {
     int32_t head_dim;
     int32_t block_size;
     int32_t num_blocks;
+    // INT8 cache (else null): codes [num_blocks][num_kv_heads][block_size][head_dim]
+    // and one fp32 scale per slot [num_blocks][num_kv_heads][block_size];
+    // k_pool / v_pool are then unused
+    int8_t* k_codes;
+    int8_t* v_codes;
+    float* k_scales;
+    float* v_scales;
 };
 
 struct DecodeArgs {
@@ -51,6 +58,11 @@ struct DecodeArgs {
     const uint16_t* v_new;
     uint16_t* k_pool_w;
     uint16_t* v_pool_w;
+    // INT8 cache (decode_int8 only): codes and per-slot scales as in AppendArgs
+    const int8_t* k_codes;
+    const int8_t* v_codes;
+    const float* k_scales;
+    const float* v_scales;
 };
 
 struct PrefillArgs {
@@ -76,8 +88,11 @@ struct PrefillArgs {
 
 // Decode split plan: keys per split and workspace layout, a pure function of
 // host-known shapes so that the size query and the launch always agree.
+// tile_keys: keys per tile of the kernel (kDecodeTileKeys / kDecodeInt8TileKeys).
+constexpr int32_t kDecodeTileKeys = 16;
+constexpr int32_t kDecodeInt8TileKeys = 32;
 struct DecodePlan {
-    int32_t chunk;            // keys per work item (multiple of 256)
+    int32_t chunk;            // keys per work item (a multiple of 16 tiles)
     int32_t max_chunks;       // chunks of the longest sequence
     int32_t persistent;       // 1: persistent grid over a compact item list
 
@@ -88,7 +103,7 @@ struct DecodePlan {
     size_t bytes;
 };
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                       int32_t max_seq_len, int64_t total_kv_tokens);
+                       int32_t max_seq_len, int64_t total_kv_tokens, int32_t tile_keys);
 
 // Whole-block copies of both pools (copy-on-write of a shared block).
 constexpr int kCopyPairsPerLaunch = 32;
@@ -104,6 +119,7 @@ struct CopyBlocksArgs {
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
+hipError_t launch_decode_int8(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 // Number of compute units of the current device (cached per device).

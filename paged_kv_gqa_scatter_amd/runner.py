@@ -13,8 +13,9 @@ from typing import Dict, Optional
 import numpy as np
 import torch
 
-from . import kv_append, paged_gqa_decode, paged_gqa_decode_append, paged_gqa_prefill, decode_workspace_bytes
-from .workloads import NAN_SENTINEL, AppendBatch, Case, DecodeBatch, Deferred, PrefillBatch
+from . import (decode_int8_workspace_bytes, decode_workspace_bytes, kv_append, kv_append_int8, paged_gqa_decode,
+               paged_gqa_decode_append, paged_gqa_decode_int8, paged_gqa_prefill)
+from .workloads import INT8_CODE_SENTINEL, NAN_SENTINEL, AppendBatch, Case, DecodeBatch, Deferred, PrefillBatch
 
 
 _device_gen = {}
@@ -196,3 +197,46 @@ class DeviceCase:
     def pools_numpy(self, pool: int = 0):
         k, v = self.pools[pool]
         return (k.view(torch.int16).cpu().numpy().view(np.uint16), v.view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+class Int8DeviceCase(DeviceCase):
+    """The same case over an INT8 KV cache (include/pkv_int8.h): appends
+    quantise, decodes read codes and scales.  Pools are (k_codes, v_codes,
+    k_scales, v_scales); unwritten codes hold -128 and unwritten scales NaN.
+    Decode steps only (there is no INT8 prefill)."""
+
+    def __init__(self, case: Case, device: str = "cuda", pools: int = 1):
+        if any(st.prefill is not None for st in case.steps):
+            raise ValueError("the INT8 cache has decode steps only")
+        super().__init__(case, device, pools=0)
+        shape = (case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim)
+        for _ in range(pools):
+            codes = [torch.full(shape, INT8_CODE_SENTINEL, dtype=torch.int8, device=self.device) for _ in range(2)]
+            scales = [torch.full(shape[:3], float("nan"), dtype=torch.float32, device=self.device) for _ in range(2)]
+            self.pools.append((codes[0], codes[1], scales[0], scales[1]))
+
+    def _decode(self, b: DecodeBatch) -> DevDecode:
+        dd = super()._decode(b)
+        c = self.case
+        S = b.seq_lens.shape[0]
+        ws = decode_int8_workspace_bytes(S, c.num_q_heads, c.num_kv_heads, c.head_dim, dd.max_seq_len,
+                                         dd.total_kv_tokens) if S else 16
+        dd.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=self.device)
+        return dd
+
+    def append(self, a: DevAppend, pool: int = 0):
+        kv_append_int8(*self.pools[pool], a.k_new, a.v_new, a.cu_new_lens, a.ctx_lens, a.block_table)
+
+    def decode(self, dd: DevDecode, pool: int = 0):
+        return paged_gqa_decode_int8(dd.q, *self.pools[pool], dd.block_table, dd.seq_lens, float(self.case.scale),
+                                     max_seq_len=dd.max_seq_len, total_kv_tokens=dd.total_kv_tokens, out=dd.out,
+                                     workspace=dd.workspace)
+
+    def decode_append(self, a: DevAppend, dd: DevDecode, pool: int = 0):
+        raise NotImplementedError("the INT8 cache appends and decodes in two calls")
+
+    def prefill(self, pp: DevPrefill, pool: int = 0):
+        raise NotImplementedError("the INT8 cache has decode steps only")
+
+    def pools_numpy(self, pool: int = 0):
+        return tuple(t.cpu().numpy() for t in self.pools[pool])

@@ -353,6 +353,13 @@ def decode_unique_kv_bytes(case: Case, batch: DecodeBatch) -> int:
     return sum(rows_read.values()) * case.num_kv_heads * case.head_dim * 2 * 2
 
 
+def decode_unique_int8_kv_bytes(case: Case, batch: DecodeBatch) -> int:
+    """The same rows over an INT8 cache: D code bytes plus one fp32 scale per
+    row, for K and for V."""
+    rows = decode_unique_kv_bytes(case, batch) // (case.head_dim * 2 * 2)
+    return rows * (case.head_dim + 4) * 2
+
+
 def decode_logical_kv_bytes(case: Case, batch: DecodeBatch) -> int:
     return int(batch.seq_lens.astype(np.int64).sum()) * case.num_kv_heads * case.head_dim * 2 * 2
 

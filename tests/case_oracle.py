@@ -57,6 +57,33 @@ def oracle_outputs(case, orc):
     return outs, (K, V)
 
 
+def int8_empty_pools(case):
+    """Host INT8 cache of a case: codes hold -128, scales NaN."""
+    from paged_kv_gqa_scatter_amd.workloads import INT8_CODE_SENTINEL
+    shape = (case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim)
+    codes = [np.full(shape, INT8_CODE_SENTINEL, np.int8) for _ in range(2)]
+    scales = [np.full(shape[:3], np.nan, np.float32) for _ in range(2)]
+    return codes[0], codes[1], scales[0], scales[1]
+
+
+def oracle_int8(case, orc, upto_step=None, decode=True):
+    """The case over an INT8 cache: the host cache after the fills and the
+    appends of steps [0, upto_step), and (decode=True) every decode step's
+    output, each computed after its step's append."""
+    pools = int8_empty_pools(case)
+    for f in case.fills:
+        orc.kv_append_int8(*pools, f.k_new, f.v_new, f.cu_new_lens, f.ctx_lens, f.block_table)
+    outs = []
+    n = len(case.steps) if upto_step is None else upto_step
+    for st in case.steps[:n]:
+        a = st.append
+        orc.kv_append_int8(*pools, a.k_new, a.v_new, a.cu_new_lens, a.ctx_lens, a.block_table)
+        if decode and st.decode is not None:
+            d = st.decode
+            outs.append(orc.decode_int8(d.q, *pools, d.block_table, d.seq_lens, case.scale))
+    return outs, pools
+
+
 def compare(gpu: np.ndarray, ref: np.ndarray, what: str):
     """Max abs error and relative L2 error over the whole tensor."""
     gpu = np.asarray(gpu, np.float64)

@@ -532,8 +532,57 @@ def pin_int8_append_matches_indexing(orc):
     assert np.array_equal(ks, eks, equal_nan=True) and np.array_equal(vs, evs, equal_nan=True)
 
 
+def int8_decode_bound(q, seq_lens, block_table, bf16_pools, int8_pools, scale):
+    """How far decode over the INT8 cache may lie from decode over the bf16
+    cache it was quantised from, per output row (s, h): with every score
+    moved by at most Delta = scale * max_k sum_d |q_d| |k_d - k^_d| and every
+    value by at most eps_v = max |v - v^|, the softmax weights change by a
+    factor within exp(+-2 Delta), so |O^ - O| <= eps_v + (exp(2 Delta) - 1) max|v|.
+    Returns fp64 [S][Hq]."""
+    K, V = bf16_pools
+    kc, vc, ks, vs = int8_pools
+    S, Hq, D = q.shape
+    Hkv, B = K.shape[1], K.shape[2]
+    G = Hq // Hkv
+    qf = bf16_to_f64(q)
+    out = np.zeros((S, Hq))
+    for s in range(S):
+        L = int(seq_lens[s])
+        if L == 0:
+            continue
+        pos = np.arange(L)
+        blk, slot = block_table[s][pos // B], pos % B
+        Kb, Vb = bf16_to_f64(K[blk, :, slot, :]), bf16_to_f64(V[blk, :, slot, :])  # [L][Hkv][D]
+        Kq = kc[blk, :, slot, :].astype(np.float64) * ks[blk, :, slot].astype(np.float64)[..., None]
+        Vq = vc[blk, :, slot, :].astype(np.float64) * vs[blk, :, slot].astype(np.float64)[..., None]
+        for g in range(Hkv):
+            delta = float(scale) * (np.abs(Kb[:, g] - Kq[:, g]) @ np.abs(qf[s, g * G:(g + 1) * G]).T).max(axis=0)
+            eps_v = np.abs(Vb[:, g] - Vq[:, g]).max()
+            out[s, g * G:(g + 1) * G] = eps_v + np.expm1(2 * delta) * np.abs(Vb[:, g]).max()
+    return out
+
+
+def pin_int8_error_within_bound(orc):
+    """Decode over the INT8 cache (rows quantised by the oracle's append)
+    stays within the quantisation bound of decode over the bf16 cache, and
+    the bound is not vacuous."""
+    rng = np.random.default_rng(95)
+    t = Tiny(rng, 3, 8, 2, 64, 32, [70, 1, 33], [1, 1, 1])
+    kc, vc, ks, vs = int8_pools(t.kp.shape)
+    cu = np.concatenate([[0], np.cumsum(t.seq_lens)]).astype(np.int32)
+    orc.kv_append_int8(kc, vc, ks, vs, np.concatenate(t.k), np.concatenate(t.v), cu, np.zeros(3, np.int32), t.table)
+    q = t.q.reshape(3, t.hq, t.d)
+    exact = orc.decode(q, t.kp, t.vp, t.table, t.seq_lens, t.scale)
+    quant = orc.decode_int8(q, kc, vc, ks, vs, t.table, t.seq_lens, t.scale)
+    bound = int8_decode_bound(q, t.seq_lens, t.table, (t.kp, t.vp), (kc, vc, ks, vs), t.scale)
+    err = np.abs(quant - exact).max(axis=2)
+    assert (err <= bound + 1e-12).all(), f"worst ratio {np.max(err / bound)}"
+    assert 0 < err.max() and bound.max() < 1.0, (err.max(), bound.max())  # well below max|v| (about 3)
+
+
 ALL_PINS = [pin_all_golden, pin_vs_sdpa, pin_vs_dense, pin_constant_v, pin_scale_zero_mean, pin_single_key,
             pin_empty_sequence, pin_block_permutation, pin_block_size_16_vs_256, pin_decode_is_last_prefill_row,
             pin_chunked_equals_unchunked, pin_gqa_is_expanded_mha, pin_head_permutation_in_group,
             pin_append_matches_indexing, pin_append_rejects_duplicate_slot, pin_int8_quantizer_bounds,
-            pin_int8_quantizer_symmetries, pin_int8_attention_vs_sdpa, pin_int8_append_matches_indexing]
+            pin_int8_quantizer_symmetries, pin_int8_attention_vs_sdpa, pin_int8_append_matches_indexing,
+            pin_int8_error_within_bound]

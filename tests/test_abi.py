@@ -12,6 +12,7 @@ import paged_kv_gqa_scatter_amd as pkv
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pkv.h")
 BLOCKS_HEADER = os.path.join(ROOT, "include", "pkv_blocks.h")
+INT8_HEADER = os.path.join(ROOT, "include", "pkv_int8.h")
 
 
 @pytest.fixture(scope="module")
@@ -38,8 +39,12 @@ def test_block_header_declares_its_functions():
     assert set(declared_functions(BLOCKS_HEADER)) == set(pkv.BLOCK_EXPORTS)
 
 
+def test_int8_header_declares_its_functions():
+    assert set(declared_functions(INT8_HEADER)) == set(pkv.INT8_EXPORTS)
+
+
 def test_every_declared_symbol_is_exported(lib):
-    for name in declared_functions() + declared_functions(BLOCKS_HEADER):
+    for name in declared_functions() + declared_functions(BLOCKS_HEADER) + declared_functions(INT8_HEADER):
         assert hasattr(lib, name), name
 
 
@@ -143,3 +148,53 @@ def test_prefill_rejects(lib):
     assert f(*prefill_args(cu=None)) == 1
     assert f(*prefill_args(q=A16 + 4)) == 3
     assert f(*prefill_args(T=0)) == 0
+
+
+def append_int8_args(**kw):
+    a = dict(kc=A16, vc=A16, ks=A16, vs=A16, k_new=A16, v_new=A16, cu=A16, ctx=A16, table=A16, mbs=4, S=2, T=3,
+             hkv=8, d=128, bs=256, nb=10, stream=None)
+    a.update(kw)
+    return tuple(a[k] for k in ("kc", "vc", "ks", "vs", "k_new", "v_new", "cu", "ctx", "table", "mbs", "S", "T",
+                                "hkv", "d", "bs", "nb", "stream"))
+
+
+def test_append_int8_rejects(lib):
+    f = lib.pkv_kv_append_int8
+    assert f(*append_int8_args(d=96)) == 2
+    assert f(*append_int8_args(bs=16)) == 2     # INT8 tiles are 32 keys of one block
+    assert f(*append_int8_args(bs=48)) == 2
+    assert f(*append_int8_args(S=0)) == 2
+    assert f(*append_int8_args(ks=None)) == 1
+    assert f(*append_int8_args(v_new=None)) == 1
+    assert f(*append_int8_args(vs=A16 + 4)) == 3
+    assert f(*append_int8_args(kc=A16 + 8)) == 3
+    assert f(*append_int8_args(T=0, kc=None)) == 0
+
+
+def decode_int8_args(**kw):
+    a = dict(out=A16, q=A16, kc=A16, vc=A16, ks=A16, vs=A16, table=A16, mbs=9, lens=A16, maxlen=2049, total=0, S=8,
+             hq=32, hkv=8, d=128, bs=256, nb=50, scale=0.088, ws=A16, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return tuple(a[k] for k in ("out", "q", "kc", "vc", "ks", "vs", "table", "mbs", "lens", "maxlen", "total", "S",
+                                "hq", "hkv", "d", "bs", "nb", "scale", "ws", "wsb", "stream"))
+
+
+def test_decode_int8_rejects(lib):
+    f = lib.pkv_paged_gqa_decode_int8
+    assert f(*decode_int8_args(hq=30)) == 2
+    assert f(*decode_int8_args(bs=16, mbs=200)) == 2
+    assert f(*decode_int8_args(d=256)) == 2
+    assert f(*decode_int8_args(maxlen=9 * 256 + 1)) == 2
+    assert f(*decode_int8_args(kc=None)) == 1
+    assert f(*decode_int8_args(vs=None)) == 1
+    assert f(*decode_int8_args(ks=A16 + 4)) == 3
+    assert f(*decode_int8_args(ws=None)) == 4
+    assert f(*decode_int8_args(wsb=16)) == 4
+    assert f(*decode_int8_args(S=0)) == 0
+
+
+def test_decode_int8_workspace_bytes(lib):
+    f = lib.pkv_decode_int8_workspace_bytes
+    assert f(8, 32, 8, 96, 2049, 0) == 0
+    assert f(8, 32, 8, 128, 2049, 0) > 0
+    assert f(272, 32, 8, 128, 32769, 1_830_000) < f(272, 32, 8, 128, 32769, 0)
