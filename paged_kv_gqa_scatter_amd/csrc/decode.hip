@@ -398,8 +398,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeKernelArgs
 
 }  // namespace
 
+int32_t decode_wgs_per_cu(int32_t head_dim) { return head_dim == 64 ? 2 : 1; }  // LDS: 133..148 KB / 67..74 KB
+
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                       int32_t max_seq_len, int64_t total_kv_tokens, int32_t tile_keys) {
+                       int32_t max_seq_len, int64_t total_kv_tokens, int32_t tile_keys, int32_t wgs_per_cu) {
     DecodePlan pl{};
     const int64_t bound_tokens = (int64_t)num_seqs * max_seq_len;
     int64_t total = total_kv_tokens > 0 ? total_kv_tokens : bound_tokens;
@@ -407,11 +409,10 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
     // chunk: the power of two in [16 tiles, 512 tiles] with the least
     // estimated time, counted in tile times (a tile of either cache format
     // moves about 8 KB per wave at D = 128): rounds of resident workgroups
-    // (one per CU at D = 128, two at D = 64, on a 256-CU part) times the
-    // round's length, a load round trip (about 12 tiles) plus the tiles each
-    // wave streams.  The item count is a bound (each sequence adds at most one
-    // partial chunk).
-    const int64_t slots = (int64_t)kPlanCus * (head_dim == 64 ? 2 : 1);
+    // (wgs_per_cu on each of a 256-CU part's CUs) times the round's length, a
+    // load round trip (about 12 tiles) plus the tiles each wave streams.  The
+    // item count is a bound (each sequence adds at most one partial chunk).
+    const int64_t slots = (int64_t)kPlanCus * wgs_per_cu;
     const int max_chunk = kMaxTilesPerWave * tile_keys * kDecodeWaves;
     int chunk = kDecodeWaves * 4 * tile_keys;
     int64_t best = -1;

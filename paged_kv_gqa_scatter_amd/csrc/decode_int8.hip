@@ -88,7 +88,7 @@ __device__ __forceinline__ Int8Lanes<D> int8_lanes(int lane) {
     return tl;
 }
 
-// The four LDS stages of the block's waves: codes and the scale rows.
+// The LDS stages of the block's waves (a ring of R): codes and the scale rows.
 template <int D>
 struct Int8Stages {
     int8_t* k[kStages];
@@ -161,17 +161,18 @@ __device__ __forceinline__ u32x4 codes_to_bf16(uint32_t lo, uint32_t hi) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8_8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Tile t from stage kS: wait for it, refill the stage freed by tile t - 1
-// with tile t + 3, then S^T, softmax, O^T.
-template <int D, int kS>
+// Tile t from stage kS of a ring of R: wait for it, refill the stage freed by
+// tile t - 1 with tile t + R - 1, then S^T, softmax, O^T.
+template <int D, int R, int kS>
 __device__ __forceinline__ void tile_step8(const Int8WaveItem<D>& w, int t, WaveState<D>& ws) {
     using T = Int8Lanes<D>;
     constexpr int kDma = T::kDma;
-    const int after = min(kStages - 2, w.n_tiles - 1 - t);  // tiles issued after t
+    static_assert(R == 2 || R == 4, "ring depth");
+    const int after = min(R - 2, w.n_tiles - 1 - t);  // tiles issued after t
     if (after >= 2) wait_vmcnt<2 * kDma>();
     else if (after == 1) wait_vmcnt<kDma>();
     else wait_vmcnt<0>();
-    if (t + kStages - 1 < w.n_tiles) issue8(w, t + kStages - 1, (kS + kStages - 1) % kStages);
+    if (t + R - 1 < w.n_tiles) issue8(w, t + R - 1, (kS + R - 1) % R);
 
     // every LDS read of the tile goes out before the first MFMA waits on one
     const int8_t* sk = w.st.k[kS] + w.wave * kTile8 * D;
@@ -257,16 +258,18 @@ __device__ __forceinline__ void tile_step8(const Int8WaveItem<D>& w, int t, Wave
                                                              as_bf16x8_8(pk), ws.acc[db], 0, 0, 0);
 }
 
-template <int D>
+template <int D, int R>
 __device__ __forceinline__ void wave_tiles8(const Int8WaveItem<D>& w, WaveState<D>& ws) {
 #pragma unroll
-    for (int t = 0; t < kStages - 1; ++t)
+    for (int t = 0; t < R - 1; ++t)
         if (t < w.n_tiles) issue8(w, t, t);
-    for (int t = 0; t < w.n_tiles; t += kStages) {
-        tile_step8<D, 0>(w, t, ws);
-        if (t + 1 < w.n_tiles) tile_step8<D, 1>(w, t + 1, ws);
-        if (t + 2 < w.n_tiles) tile_step8<D, 2>(w, t + 2, ws);
-        if (t + 3 < w.n_tiles) tile_step8<D, 3>(w, t + 3, ws);
+    for (int t = 0; t < w.n_tiles; t += R) {
+        tile_step8<D, R, 0>(w, t, ws);
+        if (t + 1 < w.n_tiles) tile_step8<D, R, 1>(w, t + 1, ws);
+        if constexpr (R == 4) {
+            if (t + 2 < w.n_tiles) tile_step8<D, R, 2>(w, t + 2, ws);
+            if (t + 3 < w.n_tiles) tile_step8<D, R, 3>(w, t + 3, ws);
+        }
     }
 }
 
@@ -302,7 +305,7 @@ __device__ __forceinline__ Int8Inputs<D> load_int8_inputs(const DecodeKernelArgs
     return in;
 }
 
-template <int D, int G, typename Prefetch>
+template <int D, int G, int R, typename Prefetch>
 __device__ __forceinline__ void decode_int8_item(const DecodeKernelArgs& p, DecodeShared<D, G>& sh,
                                                  const Int8Stages<D>& st, int s, int g, int c, int nchunks,
                                                  int64_t slot, const Int8Inputs<D>& in, Prefetch prefetch) {
@@ -337,43 +340,31 @@ __device__ __forceinline__ void decode_int8_item(const DecodeKernelArgs& p, Deco
     ws.l = 0.f;
     wait_all_vm();  // the item's inputs are in
     prefetch();     // the next item's inputs travel with this item's first tiles
-    wave_tiles8<D>(w, ws);
+    wave_tiles8<D, R>(w, ws);
     finish_item<D, G>(p, sh, ws, s, g, nchunks, slot);
 }
 
-template <int D, int G>
+// R: LDS ring depth per wave.  R = 4 keeps three tiles in flight per wave
+// (132 KB of stages at D = 128: one workgroup per CU); R = 2 keeps one (66 KB:
+// two workgroups per CU, so two waves share each SIMD and hide each other's
+// stalls: the long-context decode runs about 1.4x faster than with R = 4).
+template <int D, int G, int R>
 __global__ __launch_bounds__(kDecodeThreads) void decode_int8_kernel(DecodeKernelArgs p, int32_t* prefix_out) {
     __shared__ DecodeShared<D, G> sh;
-    __shared__ __attribute__((aligned(16))) int8_t sK0[kDecodeWaves * kTile8 * D];
-    __shared__ __attribute__((aligned(16))) int8_t sK1[kDecodeWaves * kTile8 * D];
-    __shared__ __attribute__((aligned(16))) int8_t sK2[kDecodeWaves * kTile8 * D];
-    __shared__ __attribute__((aligned(16))) int8_t sK3[kDecodeWaves * kTile8 * D];
-    __shared__ __attribute__((aligned(16))) int8_t sV0[kDecodeWaves * kTile8 * D];
-    __shared__ __attribute__((aligned(16))) int8_t sV1[kDecodeWaves * kTile8 * D];
-    __shared__ __attribute__((aligned(16))) int8_t sV2[kDecodeWaves * kTile8 * D];
-    __shared__ __attribute__((aligned(16))) int8_t sV3[kDecodeWaves * kTile8 * D];
-    __shared__ __attribute__((aligned(16))) float sS0[kDecodeWaves * 2 * kTile8];
-    __shared__ __attribute__((aligned(16))) float sS1[kDecodeWaves * 2 * kTile8];
-    __shared__ __attribute__((aligned(16))) float sS2[kDecodeWaves * 2 * kTile8];
-    __shared__ __attribute__((aligned(16))) float sS3[kDecodeWaves * 2 * kTile8];
-    static_assert(kStages == 4, "four stage arrays");
+    __shared__ __attribute__((aligned(16))) int8_t sK[R][kDecodeWaves * kTile8 * D];
+    __shared__ __attribute__((aligned(16))) int8_t sV[R][kDecodeWaves * kTile8 * D];
+    __shared__ __attribute__((aligned(16))) float sS[R][kDecodeWaves * 2 * kTile8];
     Int8Stages<D> st;
-    st.k[0] = sK0;
-    st.k[1] = sK1;
-    st.k[2] = sK2;
-    st.k[3] = sK3;
-    st.v[0] = sV0;
-    st.v[1] = sV1;
-    st.v[2] = sV2;
-    st.v[3] = sV3;
-    st.sc[0] = sS0;
-    st.sc[1] = sS1;
-    st.sc[2] = sS2;
-    st.sc[3] = sS3;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        st.k[i] = sK[i];
+        st.v[i] = sV[i];
+        st.sc[i] = sS[i];
+    }
     run_items<D, G>(
         p, sh, prefix_out, [&](int s, int g, int c) { return load_int8_inputs<D, G>(p, s, g, c); },
         [&](int s, int g, int c, int n, int64_t slot, const Int8Inputs<D>& in, auto prefetch) {
-            decode_int8_item<D, G>(p, sh, st, s, g, c, n, slot, in, prefetch);
+            decode_int8_item<D, G, R>(p, sh, st, s, g, c, n, slot, in, prefetch);
         });
 }
 
@@ -396,18 +387,26 @@ hipError_t launch_decode_int8(const DecodeArgs& a, const DecodePlan& pl, hipStre
     const int G = a.num_q_heads / a.num_kv_heads;
     if (a.head_dim == 128) {
         switch (G) {
-            case 1: return launch_split<128, 1>(decode_int8_kernel<128, 1>, kp, prefix, stream);
-            case 2: return launch_split<128, 2>(decode_int8_kernel<128, 2>, kp, prefix, stream);
-            case 4: return launch_split<128, 4>(decode_int8_kernel<128, 4>, kp, prefix, stream);
-            default: return launch_split<128, 8>(decode_int8_kernel<128, 8>, kp, prefix, stream);
+            case 1: return launch_split<128, 1>(decode_int8_kernel<128, 1, 2>, kp, prefix, stream);
+            case 2: return launch_split<128, 2>(decode_int8_kernel<128, 2, 2>, kp, prefix, stream);
+            case 4: return launch_split<128, 4>(decode_int8_kernel<128, 4, 2>, kp, prefix, stream);
+            default: return launch_split<128, 8>(decode_int8_kernel<128, 8, 4>, kp, prefix, stream);
         }
     }
     switch (G) {
-        case 1: return launch_split<64, 1>(decode_int8_kernel<64, 1>, kp, prefix, stream);
-        case 2: return launch_split<64, 2>(decode_int8_kernel<64, 2>, kp, prefix, stream);
-        case 4: return launch_split<64, 4>(decode_int8_kernel<64, 4>, kp, prefix, stream);
-        default: return launch_split<64, 8>(decode_int8_kernel<64, 8>, kp, prefix, stream);
+        case 1: return launch_split<64, 1>(decode_int8_kernel<64, 1, 2>, kp, prefix, stream);
+        case 2: return launch_split<64, 2>(decode_int8_kernel<64, 2, 2>, kp, prefix, stream);
+        case 4: return launch_split<64, 4>(decode_int8_kernel<64, 4, 2>, kp, prefix, stream);
+        default: return launch_split<64, 8>(decode_int8_kernel<64, 8, 2>, kp, prefix, stream);
     }
+}
+
+int32_t decode_int8_wgs_per_cu(int32_t head_dim, int32_t group) {
+    // workgroups that fit one CU (LDS, then 512 VGPRs per SIMD lane): ring 2
+    // at D = 128 (two; ring 4 and one for G = 8, whose merge buffer is
+    // larger), ring 2 at D = 64 (three)
+    if (head_dim == 128) return group == 8 ? 1 : 2;
+    return 3;
 }
 
 }  // namespace pkv

@@ -102,8 +102,11 @@ struct DecodePlan {
     size_t o_offset;          // float [max_partials][num_q_heads][head_dim]
     size_t bytes;
 };
+// wgs_per_cu: workgroups of the kernel resident on one CU.
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                       int32_t max_seq_len, int64_t total_kv_tokens, int32_t tile_keys);
+                       int32_t max_seq_len, int64_t total_kv_tokens, int32_t tile_keys, int32_t wgs_per_cu);
+int32_t decode_wgs_per_cu(int32_t head_dim);
+int32_t decode_int8_wgs_per_cu(int32_t head_dim, int32_t group);
 
 // Whole-block copies of both pools (copy-on-write of a shared block).
 constexpr int kCopyPairsPerLaunch = 32;
