@@ -200,16 +200,17 @@ __device__ __forceinline__ void put_new_row(const WaveItem<D>& w, int t, int kS)
     }
 }
 
-// Tile t from stage kS: wait for it, refill the stage freed by tile t - 1
-// with tile t + 3, then S^T, softmax, O^T.
-template <int D, int kS>
+// Tile t from stage kS of a ring of R: wait for it, refill the stage freed
+// by tile t - 1 with tile t + R - 1, then S^T, softmax, O^T.
+template <int D, int R, int kS>
 __device__ __forceinline__ void tile_step(const WaveItem<D>& w, int t, WaveState<D>& ws) {
     constexpr int kDma = TileLanes<D>::kDma;
-    const int after = min(kStages - 2, w.n_tiles - 1 - t);  // tiles issued after t
+    static_assert(R == 2 || R == 4, "ring depth");
+    const int after = min(R - 2, w.n_tiles - 1 - t);  // tiles issued after t
     if (after >= 2) wait_vmcnt<2 * kDma>();
     else if (after == 1) wait_vmcnt<kDma>();
     else wait_vmcnt<0>();
-    if (t + kStages - 1 < w.n_tiles) issue(w, t + kStages - 1, (kS + kStages - 1) % kStages);
+    if (t + R - 1 < w.n_tiles) issue(w, t + R - 1, (kS + R - 1) % R);
     if (w.append && w.kend == w.L && tile_key(w, t) + kTileKeys >= w.kend) put_new_row<D>(w, t, kS);
 
     // every LDS read of the tile goes out before the first MFMA waits on one
@@ -262,16 +263,18 @@ __device__ __forceinline__ void tile_step(const WaveItem<D>& w, int t, WaveState
         ws.acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(vf[db]), as_s16x4(pk), ws.acc[db], 0, 0, 0);
 }
 
-template <int D>
+template <int D, int R>
 __device__ __forceinline__ void wave_tiles(const WaveItem<D>& w, WaveState<D>& ws) {
 #pragma unroll
-    for (int t = 0; t < kStages - 1; ++t)
+    for (int t = 0; t < R - 1; ++t)
         if (t < w.n_tiles) issue(w, t, t);
-    for (int t = 0; t < w.n_tiles; t += kStages) {
-        tile_step<D, 0>(w, t, ws);
-        if (t + 1 < w.n_tiles) tile_step<D, 1>(w, t + 1, ws);
-        if (t + 2 < w.n_tiles) tile_step<D, 2>(w, t + 2, ws);
-        if (t + 3 < w.n_tiles) tile_step<D, 3>(w, t + 3, ws);
+    for (int t = 0; t < w.n_tiles; t += R) {
+        tile_step<D, R, 0>(w, t, ws);
+        if (t + 1 < w.n_tiles) tile_step<D, R, 1>(w, t + 1, ws);
+        if constexpr (R == 4) {
+            if (t + 2 < w.n_tiles) tile_step<D, R, 2>(w, t + 2, ws);
+            if (t + 3 < w.n_tiles) tile_step<D, R, 3>(w, t + 3, ws);
+        }
     }
 }
 
@@ -319,7 +322,7 @@ __device__ __forceinline__ ItemInputs<D> load_item_inputs(const DecodeKernelArgs
 
 
 // One work item: chunk c of sequence s, KV head g; `slot` is its partial slot.
-template <int D, int G, typename Prefetch>
+template <int D, int G, int R, typename Prefetch>
 __device__ __forceinline__ void decode_item(const DecodeKernelArgs& p, DecodeShared<D, G>& sh, const Stages<D>& st,
                                             int s, int g, int c, int nchunks, int64_t slot,
                                             const ItemInputs<D>& in, Prefetch prefetch) {
@@ -362,43 +365,35 @@ __device__ __forceinline__ void decode_item(const DecodeKernelArgs& p, DecodeSha
     // in issue order, they retire with the first tile, so the next item
     // starts without a round trip of its own
     prefetch();
-    wave_tiles<D>(w, ws);
+    wave_tiles<D, R>(w, ws);
 
     finish_item<D, G>(p, sh, ws, s, g, nchunks, slot);
 }
 
-template <int D, int G>
+// R: LDS ring depth per wave.  R = 4 keeps three tiles in flight per wave
+// (128 KB of stages at D = 128: one workgroup per CU); R = 2 keeps one (64 KB:
+// two workgroups per CU, two waves per SIMD hiding each other's stalls), which
+// pays when there is more work than one pass over the chip.
+template <int D, int G, int R>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeKernelArgs p, int32_t* prefix_out) {
     __shared__ DecodeShared<D, G> sh;
-    __shared__ __attribute__((aligned(16))) uint16_t sK0[kDecodeWaves * kTileKeys * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sK1[kDecodeWaves * kTileKeys * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sK2[kDecodeWaves * kTileKeys * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sK3[kDecodeWaves * kTileKeys * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sV0[kDecodeWaves * kTileKeys * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sV1[kDecodeWaves * kTileKeys * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sV2[kDecodeWaves * kTileKeys * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sV3[kDecodeWaves * kTileKeys * D];
-    static_assert(kStages == 4, "four stage arrays");
+    __shared__ __attribute__((aligned(16))) uint16_t sK[R][kDecodeWaves * kTileKeys * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[R][kDecodeWaves * kTileKeys * D];
     Stages<D> st;
-    st.k[0] = sK0;
-    st.k[1] = sK1;
-    st.k[2] = sK2;
-    st.k[3] = sK3;
-    st.v[0] = sV0;
-    st.v[1] = sV1;
-    st.v[2] = sV2;
-    st.v[3] = sV3;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        st.k[i] = sK[i];
+        st.v[i] = sV[i];
+    }
 
     run_items<D, G>(
         p, sh, prefix_out, [&](int s, int g, int c) { return load_item_inputs<D, G>(p, s, g, c); },
         [&](int s, int g, int c, int n, int64_t slot, const ItemInputs<D>& in, auto prefetch) {
-            decode_item<D, G>(p, sh, st, s, g, c, n, slot, in, prefetch);
+            decode_item<D, G, R>(p, sh, st, s, g, c, n, slot, in, prefetch);
         });
 }
 
 }  // namespace
-
-int32_t decode_wgs_per_cu(int32_t head_dim) { return head_dim == 64 ? 2 : 1; }  // LDS: 133..148 KB / 67..74 KB
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t max_seq_len, int64_t total_kv_tokens, int32_t tile_keys, int32_t wgs_per_cu) {
@@ -424,7 +419,9 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
             chunk = c;
         }
     }
+    pl.ring = 4;
     pl.chunk = chunk;
+    pl.items = ((total + chunk - 1) / chunk + num_seqs) * num_kv_heads;
     pl.max_chunks = (max_seq_len + chunk - 1) / chunk;
     const int64_t direct_items = (int64_t)num_seqs * pl.max_chunks;
     const int64_t real_items = (total + chunk - 1) / chunk + num_seqs;  // bound on chunks actually present
@@ -439,6 +436,20 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
     pl.lse_offset = align(sizeof(int32_t) * (size_t)(num_seqs + 1));
     pl.o_offset = align(pl.lse_offset + sizeof(float) * (size_t)pl.max_partials * num_q_heads);
     pl.bytes = pl.o_offset + sizeof(float) * (size_t)pl.max_partials * num_q_heads * head_dim;
+    return pl;
+}
+
+DecodePlan plan_decode_bf16(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t max_seq_len, int64_t total_kv_tokens) {
+    // ring 4: one workgroup per CU at D = 128 (133..148 KB of LDS), two at
+    // D = 64.  When the items outnumber one pass over the CUs, ring 2 at
+    // D = 128 and G <= 4 (66..74 KB: two per CU) hides more stalls.
+    DecodePlan pl = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, total_kv_tokens,
+                                kTileKeys, head_dim == 64 ? 2 : 1);
+    if (head_dim == 128 && num_q_heads <= 4 * num_kv_heads && pl.items > kPlanCus) {
+        pl = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, total_kv_tokens, kTileKeys, 2);
+        pl.ring = 2;
+    }
     return pl;
 }
 
@@ -458,18 +469,25 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     kp.qk_scale_log2 = a.scale * kLog2e;
     const int G = a.num_q_heads / a.num_kv_heads;
     if (a.head_dim == 128) {
+        if (pl.ring == 2) {
+            switch (G) {
+                case 1: return launch_split<128, 1>(decode_kernel<128, 1, 2>, kp, prefix, stream);
+                case 2: return launch_split<128, 2>(decode_kernel<128, 2, 2>, kp, prefix, stream);
+                default: return launch_split<128, 4>(decode_kernel<128, 4, 2>, kp, prefix, stream);
+            }
+        }
         switch (G) {
-            case 1: return launch_split<128, 1>(decode_kernel<128, 1>, kp, prefix, stream);
-            case 2: return launch_split<128, 2>(decode_kernel<128, 2>, kp, prefix, stream);
-            case 4: return launch_split<128, 4>(decode_kernel<128, 4>, kp, prefix, stream);
-            default: return launch_split<128, 8>(decode_kernel<128, 8>, kp, prefix, stream);
+            case 1: return launch_split<128, 1>(decode_kernel<128, 1, 4>, kp, prefix, stream);
+            case 2: return launch_split<128, 2>(decode_kernel<128, 2, 4>, kp, prefix, stream);
+            case 4: return launch_split<128, 4>(decode_kernel<128, 4, 4>, kp, prefix, stream);
+            default: return launch_split<128, 8>(decode_kernel<128, 8, 4>, kp, prefix, stream);
         }
     }
     switch (G) {
-        case 1: return launch_split<64, 1>(decode_kernel<64, 1>, kp, prefix, stream);
-        case 2: return launch_split<64, 2>(decode_kernel<64, 2>, kp, prefix, stream);
-        case 4: return launch_split<64, 4>(decode_kernel<64, 4>, kp, prefix, stream);
-        default: return launch_split<64, 8>(decode_kernel<64, 8>, kp, prefix, stream);
+        case 1: return launch_split<64, 1>(decode_kernel<64, 1, 4>, kp, prefix, stream);
+        case 2: return launch_split<64, 2>(decode_kernel<64, 2, 4>, kp, prefix, stream);
+        case 4: return launch_split<64, 4>(decode_kernel<64, 4, 4>, kp, prefix, stream);
+        default: return launch_split<64, 8>(decode_kernel<64, 8, 4>, kp, prefix, stream);
     }
 }
 

@@ -384,7 +384,7 @@ hipError_t launch_decode_int8(const DecodeArgs& a, const DecodePlan& pl, hipStre
     kp.lse = reinterpret_cast<float*>(ws + pl.lse_offset);
     kp.part = reinterpret_cast<float*>(ws + pl.o_offset);
     kp.qk_scale_log2 = a.scale * kLog2e;
-    const int G = a.num_q_heads / a.num_kv_heads;
+    const int G = a.num_q_heads / a.num_kv_heads;  // the ring depth follows from (D, G): plan_decode_int8
     if (a.head_dim == 128) {
         switch (G) {
             case 1: return launch_split<128, 1>(decode_int8_kernel<128, 1, 2>, kp, prefix, stream);
@@ -401,12 +401,18 @@ hipError_t launch_decode_int8(const DecodeArgs& a, const DecodePlan& pl, hipStre
     }
 }
 
-int32_t decode_int8_wgs_per_cu(int32_t head_dim, int32_t group) {
+DecodePlan plan_decode_int8(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t max_seq_len, int64_t total_kv_tokens) {
     // workgroups that fit one CU (LDS, then 512 VGPRs per SIMD lane): ring 2
     // at D = 128 (two; ring 4 and one for G = 8, whose merge buffer is
     // larger), ring 2 at D = 64 (three)
-    if (head_dim == 128) return group == 8 ? 1 : 2;
-    return 3;
+    const int group = num_q_heads / num_kv_heads;
+    const int ring = head_dim == 128 && group == 8 ? 4 : 2;
+    const int wgs = head_dim == 128 ? (group == 8 ? 1 : 2) : 3;
+    DecodePlan pl = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, total_kv_tokens,
+                                kTile8, wgs);
+    pl.ring = ring;
+    return pl;
 }
 
 }  // namespace pkv

@@ -151,18 +151,14 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
                                   int32_t max_seq_len, int64_t total_kv_tokens) {
     if (num_seqs < 0 || num_seqs > kMaxDecodeSeqs || max_seq_len < 0) return 0;
     if (check_heads(num_q_heads, num_kv_heads, head_dim, 16) != PKV_OK) return 0;
-    return plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, total_kv_tokens, kDecodeTileKeys,
-                       decode_wgs_per_cu(head_dim))
-        .bytes;
+    return plan_decode_bf16(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, total_kv_tokens).bytes;
 }
 
 size_t pkv_decode_int8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t max_seq_len, int64_t total_kv_tokens) {
     if (num_seqs < 0 || num_seqs > kMaxDecodeSeqs || max_seq_len < 0) return 0;
     if (check_heads(num_q_heads, num_kv_heads, head_dim, 32) != PKV_OK) return 0;
-    return plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, total_kv_tokens,
-                       kDecodeInt8TileKeys, decode_int8_wgs_per_cu(head_dim, num_q_heads / num_kv_heads))
-        .bytes;
+    return plan_decode_int8(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, total_kv_tokens).bytes;
 }
 
 }  // extern "C"
@@ -184,11 +180,11 @@ int32_t check_decode(DecodeArgs& a, DecodePlan& pl, const void* k, const void* v
     if (a.max_seq_len > 0 && (!k || !v)) return PKV_ERR_NULL_POINTER;
     if (!aligned16(a.out) || !aligned16(a.q) || !aligned16(k) || !aligned16(v) || !aligned16(a.workspace))
         return PKV_ERR_MISALIGNED;
-    const int32_t wgs = tile_keys == kDecodeInt8TileKeys
-                            ? decode_int8_wgs_per_cu(a.head_dim, a.num_q_heads / a.num_kv_heads)
-                            : decode_wgs_per_cu(a.head_dim);
-    pl = plan_decode(a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim, a.max_seq_len, a.total_kv_tokens,
-                     tile_keys, wgs);
+    pl = tile_keys == kDecodeInt8TileKeys
+             ? plan_decode_int8(a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim, a.max_seq_len,
+                                a.total_kv_tokens)
+             : plan_decode_bf16(a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim, a.max_seq_len,
+                                a.total_kv_tokens);
     if (!a.workspace || a.workspace_bytes < pl.bytes) return PKV_ERR_WORKSPACE;
     if (a.total_kv_tokens <= 0) a.total_kv_tokens = (int64_t)a.num_seqs * a.max_seq_len;
     return PKV_OK;

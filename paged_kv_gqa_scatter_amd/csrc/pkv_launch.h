@@ -92,21 +92,28 @@ struct PrefillArgs {
 constexpr int32_t kDecodeTileKeys = 16;
 constexpr int32_t kDecodeInt8TileKeys = 32;
 struct DecodePlan {
+    int32_t ring;             // LDS stages per wave of the split kernel (2 or 4)
     int32_t chunk;            // keys per work item (a multiple of 16 tiles)
     int32_t max_chunks;       // chunks of the longest sequence
     int32_t persistent;       // 1: persistent grid over a compact item list
 
+    int64_t items;            // bound on (chunk, KV head) work items
     int64_t max_partials;     // (sequence, split) slots the workspace holds
     size_t prefix_offset;     // int32 [num_seqs + 1] chunk prefix (persistent grid)
     size_t lse_offset;        // float [max_partials][num_q_heads]
     size_t o_offset;          // float [max_partials][num_q_heads][head_dim]
     size_t bytes;
 };
-// wgs_per_cu: workgroups of the kernel resident on one CU.
+// plan_decode: the split of a kernel whose tiles hold tile_keys keys and of
+// which wgs_per_cu workgroups are resident on one CU; the plan of each cache
+// format (which also picks its ring depth) comes from plan_decode_bf16 /
+// plan_decode_int8.
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t max_seq_len, int64_t total_kv_tokens, int32_t tile_keys, int32_t wgs_per_cu);
-int32_t decode_wgs_per_cu(int32_t head_dim);
-int32_t decode_int8_wgs_per_cu(int32_t head_dim, int32_t group);
+DecodePlan plan_decode_bf16(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t max_seq_len, int64_t total_kv_tokens);
+DecodePlan plan_decode_int8(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t max_seq_len, int64_t total_kv_tokens);
 
 // Whole-block copies of both pools (copy-on-write of a shared block).
 constexpr int kCopyPairsPerLaunch = 32;
