@@ -62,6 +62,7 @@ class Oracle:
         self.lib.oracle_quantize_int8.restype = None
         self.lib.oracle_kv_append_int8.restype = ctypes.c_int
         self.lib.oracle_attention_rows_int8.restype = ctypes.c_int
+        self.lib.oracle_qkv_project_append.restype = ctypes.c_int
 
     @staticmethod
     def _check(rc):
@@ -185,6 +186,28 @@ class Oracle:
         out = self.attention_rows_int8(items, q.reshape(S, Hq, D), cu, k_codes, v_codes, k_scales, v_scales,
                                        block_table, seq_lens, Hq, scale, num_threads)
         return out.reshape(S, Hq, D)
+
+    # ---- fused QKV projection with the paged append of k and v
+
+    def qkv_project_append(self, k_pool, v_pool, x, w, cu_new_lens, ctx_lens, block_table, num_q_heads):
+        """``x [T][d_model]`` and the merged weight ``w [(Hq + 2 Hkv) D][d_model]``
+        (uint16 bf16 bits): returns q ``[T][Hq][D]`` and writes the k and v rows
+        into the host pools (in place)."""
+        NB, Hkv, B, D = k_pool.shape
+        for a in (k_pool, v_pool, x, w):
+            assert a.dtype == np.uint16 and a.flags.c_contiguous
+        T, dm = x.shape
+        assert w.shape == ((num_q_heads + 2 * Hkv) * D, dm)
+        cu = np.ascontiguousarray(cu_new_lens, dtype=np.int32)
+        ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+        tab = np.ascontiguousarray(block_table, dtype=np.int32)
+        assert T >= cu[-1]
+        q = np.zeros((T, num_q_heads, D), np.uint16)
+        rc = self.lib.oracle_qkv_project_append(_p(q, _U16P), _p(k_pool, _U16P), _p(v_pool, _U16P), _p(x, _U16P),
+                                                _p(w, _U16P), _p(cu, _I32P), _p(ctx, _I32P), _p(tab, _I32P),
+                                                tab.shape[1], ctx.shape[0], dm, num_q_heads, Hkv, D, B, NB)
+        self._check(rc)
+        return q
 
     # decode is the one-row-per-sequence case of the same definition
     def decode(self, q, k_pool, v_pool, block_table, seq_lens, scale, num_threads: int = 0):

@@ -51,6 +51,18 @@
  *    decision; attention then reads the dequantised values code * scale,
  *    which are exact in fp64.
  *
+ *  - oracle_qkv_project_append: the fused QKV projection of "扔掉 vLLM！从零构建
+ *    Qwen3-8B 推理引擎" section 4.4.3 (the q, k and v linear projections as one
+ *    matmul against the merged weight, whose output is cut into q, k and v),
+ *    with the k and v parts placed in the paged cache as oracle_kv_append
+ *    places new rows.  The page stops at the three slices; storing k and v in
+ *    the cache straight from the projection is this repository's reading of
+ *    the fused step (the slices would be appended next anyway).  No bias and
+ *    no position encoding: the page's projection has neither.  Each output is
+ *    the dot product of a new row with a row of the merged weight, summed in
+ *    fp64 (bf16 products are exact in fp64) and rounded once to bf16, to
+ *    nearest with ties to even.
+ *
  * bf16 inputs are widened exactly: the 16 bits become the top half of an IEEE
  * binary32 word, which is then converted to double.
  */
@@ -193,6 +205,76 @@ int oracle_kv_append_int8(int8_t* k_codes, int8_t* v_codes, float* k_scales, flo
             oracle_quantize_int8(v_codes + row * head_dim, v_scales + row, v_new + src, head_dim);
         }
     }
+    free(written);
+    return rc;
+}
+
+/*
+ * A double rounded once to bf16, to nearest with ties to even (bf16 keeps 8
+ * significant bits; below 2^-126 its spacing stays 2^-133; past the largest
+ * finite value it is infinite).
+ */
+static uint16_t double_to_bf16(double v) {
+    if (v != v) return 0x7FC0;
+    const uint16_t sign = signbit(v) ? 0x8000 : 0;
+    const double a = fabs(v);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);                       /* a = m 2^e, m in [0.5, 1): spacing 2^(e - 8) */
+    int q = e - 8;
+    if (q < -133) q = -133;
+    const double r = ldexp(nearbyint(ldexp(a, -q)), q);
+    if (r >= 0x1p128) return sign | 0x7F80;
+    const float f = (float)r;           /* exact: r has at most 8 significant bits */
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    return sign | (uint16_t)(bits >> 16);
+}
+
+int oracle_qkv_project_append(uint16_t* q_out, uint16_t* k_pool, uint16_t* v_pool,
+                              const uint16_t* x, const uint16_t* w,
+                              const int32_t* cu_new_lens, const int32_t* ctx_lens,
+                              const int32_t* block_table, int max_blocks_per_seq,
+                              int num_seqs, int d_model, int num_q_heads, int num_kv_heads,
+                              int head_dim, int block_size, int num_blocks) {
+    if (num_seqs < 0 || d_model <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || num_blocks < 0)
+        return ORACLE_ERR_ARGS;
+    const int total = num_seqs > 0 ? cu_new_lens[num_seqs] : 0;
+    const int nq = num_q_heads * head_dim, nkv = num_kv_heads * head_dim;
+    const int n_out = nq + 2 * nkv;    /* rows of the merged weight: q, then k, then v features */
+    uint16_t* y = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(n_out ? n_out : 1));
+    size_t nslots = (size_t)num_blocks * (size_t)block_size;
+    unsigned char* written = (unsigned char*)calloc(nslots ? nslots : 1, 1);
+    if (!y || !written) {
+        free(y);
+        free(written);
+        return ORACLE_ERR_OOM;
+    }
+    int rc = ORACLE_OK;
+    for (int t = 0; t < total && rc == ORACLE_OK; ++t) {
+        const uint16_t* xt = x + (size_t)t * d_model;
+        for (int n = 0; n < n_out; ++n) {
+            const uint16_t* wn = w + (size_t)n * d_model;
+            double acc = 0.0;
+            for (int k = 0; k < d_model; ++k) acc += bf16_to_double(xt[k]) * bf16_to_double(wn[k]);
+            y[n] = double_to_bf16(acc);
+        }
+        memcpy(q_out + (size_t)t * nq, y, sizeof(uint16_t) * (size_t)nq);
+        int blk;
+        long slot;
+        rc = target_slot(cu_new_lens, ctx_lens, block_table, max_blocks_per_seq, num_seqs, block_size,
+                         num_blocks, t, &blk, &slot);
+        if (rc != ORACLE_OK) break;
+        if (written[(size_t)blk * block_size + slot]) { rc = ORACLE_ERR_DUP_SLOT; break; }
+        written[(size_t)blk * block_size + slot] = 1;
+        for (int g = 0; g < num_kv_heads; ++g) {
+            size_t dst = (((size_t)blk * num_kv_heads + g) * block_size + slot) * head_dim;
+            memcpy(k_pool + dst, y + nq + (size_t)g * head_dim, sizeof(uint16_t) * (size_t)head_dim);
+            memcpy(v_pool + dst, y + nq + nkv + (size_t)g * head_dim, sizeof(uint16_t) * (size_t)head_dim);
+        }
+    }
+    free(y);
     free(written);
     return rc;
 }

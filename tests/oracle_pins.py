@@ -186,8 +186,26 @@ def pin_golden_int8(orc, g, name):
     assert err <= g["tol"], f"{name}: max err {err}"
 
 
+def pin_golden_qkv(orc, g, name):
+    shape = (g["num_blocks"], g["num_kv_heads"], g["block_size"], g["head_dim"])
+    kp = np.full(shape, NAN_SENTINEL, np.uint16)
+    vp = np.full(shape, NAN_SENTINEL, np.uint16)
+    q = orc.qkv_project_append(kp, vp, to_bf16_exact(g["x"]), to_bf16_exact(g["w"]), g["cu_new_lens"],
+                               g["ctx_lens"], np.asarray(g["block_table"], np.int32), g["num_q_heads"])
+    assert np.array_equal(q, to_bf16_exact(g["expected_q"])), f"{name}: q {bf16_to_f64(q).ravel()}"
+    ek = np.full(shape, NAN_SENTINEL, np.uint16)
+    ev = np.full(shape, NAN_SENTINEL, np.uint16)
+    for w in g["expected_writes"]:
+        ek[w["block"], w["kv_head"], w["slot"]] = to_bf16_exact(w["k"])
+        ev[w["block"], w["kv_head"], w["slot"]] = to_bf16_exact(w["v"])
+    assert np.array_equal(kp, ek) and np.array_equal(vp, ev), name
+
+
 def pin_golden(orc, name):
     g = load_golden(name)
+    if g["kind"] == "qkv_project_append":
+        pin_golden_qkv(orc, g, name)
+        return
     if g["kind"] in ("quantize_int8", "int8_append_decode"):
         pin_golden_int8(orc, g, name)
         return
@@ -575,9 +593,106 @@ def pin_int8_error_within_bound(orc):
     exact = orc.decode(q, t.kp, t.vp, t.table, t.seq_lens, t.scale)
     quant = orc.decode_int8(q, kc, vc, ks, vs, t.table, t.seq_lens, t.scale)
     bound = int8_decode_bound(q, t.seq_lens, t.table, (t.kp, t.vp), (kc, vc, ks, vs), t.scale)
-    err = np.abs(quant - exact).max(axis=2)
+    with np.errstate(invalid="ignore"):  # a planted mistake may make either side non-finite
+        err = np.abs(quant - exact).max(axis=2)
     assert (err <= bound + 1e-12).all(), f"worst ratio {np.max(err / bound)}"
     assert 0 < err.max() and bound.max() < 1.0, (err.max(), bound.max())  # well below max|v| (about 3)
+
+
+# ----------------------------------------------------------------------------
+# fused QKV projection + paged append
+# ----------------------------------------------------------------------------
+
+def _qkv_case(rng, hq, hkv, d, bs, ctx_lens, new_lens):
+    """Placement of a few sequences' new rows: table, cu_new_lens, and each
+    packed row's (sequence, position)."""
+    S = len(ctx_lens)
+    ends = [c + n for c, n in zip(ctx_lens, new_lens)]
+    nblk = [-(-e // bs) for e in ends]
+    mbs = max(nblk)
+    nb = sum(nblk) + 2
+    perm = rng.permutation(nb).astype(np.int32)
+    table = np.full((S, mbs), -1, np.int32)
+    o = 0
+    for s in range(S):
+        table[s, :nblk[s]] = perm[o:o + nblk[s]]
+        o += nblk[s]
+    cu = np.concatenate([[0], np.cumsum(new_lens)]).astype(np.int32)
+    where = [(s, ctx_lens[s] + i) for s in range(S) for i in range(new_lens[s])]
+    return table, cu, np.asarray(ctx_lens, np.int32), nb, where
+
+
+def pin_qkv_selection_weights(orc):
+    """With a merged weight whose rows each pick one input feature (scaled by
+    a power of two), the projection is exact: q, k and v are those features,
+    and k / v land at each row's slot (placed here by plain indexing)."""
+    rng = np.random.default_rng(101)
+    hq, hkv, d, bs, dm = 4, 2, 8, 4, 64
+    n_out = (hq + 2 * hkv) * d
+    table, cu, ctx, nb, where = _qkv_case(rng, hq, hkv, d, bs, [3, 0, 6], [2, 5, 1])
+    T = int(cu[-1])
+    x = bf16_normal(rng, (T, dm))
+    pick = rng.permutation(dm)[:n_out] if n_out <= dm else rng.integers(dm, size=n_out)
+    mult = 2.0 ** (np.arange(n_out) % 3)
+    wf = np.zeros((n_out, dm), np.float32)
+    wf[np.arange(n_out), pick] = mult
+    kp = np.full((nb, hkv, bs, d), NAN_SENTINEL, np.uint16)
+    vp = kp.copy()
+    q = orc.qkv_project_append(kp, vp, x, to_bf16_exact(wf), cu, ctx, table, hq)
+    y = to_bf16_exact(bf16_to_f64(x)[:, pick] * mult)  # exact: a power-of-two multiple of a bf16 value
+    assert np.array_equal(q.reshape(T, -1), y[:, :hq * d])
+    ek = np.full_like(kp, NAN_SENTINEL)
+    ev = np.full_like(vp, NAN_SENTINEL)
+    for t, (s, pos) in enumerate(where):
+        ek[table[s][pos // bs], :, pos % bs, :] = y[t, hq * d:(hq + hkv) * d].reshape(hkv, d)
+        ev[table[s][pos // bs], :, pos % bs, :] = y[t, (hq + hkv) * d:].reshape(hkv, d)
+    assert np.array_equal(kp, ek) and np.array_equal(vp, ev)
+
+
+def _assert_nearest_bf16(got_bits, y):
+    """Each got value is the bf16 number nearest to the exact y (ties to the
+    even last bit), checked through the floor of y on the bf16 grid of its
+    binade (a formulation of its own, independent of the oracle's)."""
+    g = bf16_to_f64(got_bits)
+    for a, b in zip(g.ravel(), np.asarray(y, np.float64).ravel()):
+        if b == 0:
+            assert a == 0
+            continue
+        e = math.floor(math.log2(abs(b)))
+        if 2.0 ** e > abs(b):
+            e -= 1
+        sp = 2.0 ** (max(e, -126) - 7)
+        lo = math.floor(b / sp) * sp
+        hi = lo + sp
+        if b - lo < hi - b:
+            want = lo
+        elif hi - b < b - lo:
+            want = hi
+        else:
+            want = lo if int(round(lo / sp)) % 2 == 0 else hi
+        assert a == want, f"got {a}, exact {b}, nearest {want}"
+
+
+def pin_qkv_rounds_the_exact_product_to_nearest(orc):
+    """Random inputs and weights: every output is the bf16 number nearest to
+    the exact dot product (numpy fp64: exact for these few bf16 terms), and
+    k / v sit where kv_append would put those rows."""
+    rng = np.random.default_rng(102)
+    hq, hkv, d, bs, dm = 2, 1, 16, 16, 96
+    table, cu, ctx, nb, where = _qkv_case(rng, hq, hkv, d, bs, [15, 1], [3, 2])
+    T = int(cu[-1])
+    x = bf16_normal(rng, (T, dm))
+    w = bf16_normal(rng, ((hq + 2 * hkv) * d, dm))
+    kp = np.full((nb, hkv, bs, d), NAN_SENTINEL, np.uint16)
+    vp = kp.copy()
+    q = orc.qkv_project_append(kp, vp, x, w, cu, ctx, table, hq)
+    y = bf16_to_f64(x) @ bf16_to_f64(w).T
+    got = np.zeros((T, (hq + 2 * hkv) * d), np.uint16)
+    got[:, :hq * d] = q.reshape(T, -1)
+    for t, (s, pos) in enumerate(where):
+        got[t, hq * d:(hq + hkv) * d] = kp[table[s][pos // bs], :, pos % bs, :].ravel()
+        got[t, (hq + hkv) * d:] = vp[table[s][pos // bs], :, pos % bs, :].ravel()
+    _assert_nearest_bf16(got, y)
 
 
 ALL_PINS = [pin_all_golden, pin_vs_sdpa, pin_vs_dense, pin_constant_v, pin_scale_zero_mean, pin_single_key,
@@ -585,4 +700,4 @@ ALL_PINS = [pin_all_golden, pin_vs_sdpa, pin_vs_dense, pin_constant_v, pin_scale
             pin_chunked_equals_unchunked, pin_gqa_is_expanded_mha, pin_head_permutation_in_group,
             pin_append_matches_indexing, pin_append_rejects_duplicate_slot, pin_int8_quantizer_bounds,
             pin_int8_quantizer_symmetries, pin_int8_attention_vs_sdpa, pin_int8_append_matches_indexing,
-            pin_int8_error_within_bound]
+            pin_int8_error_within_bound, pin_qkv_selection_weights, pin_qkv_rounds_the_exact_product_to_nearest]

@@ -37,6 +37,14 @@ MUTATIONS = {
                                  "(double)pool->codes[row * head_dim + d]"),
     "int8_scale_of_wrong_row": ("(double)pool->scales[row]", "(double)pool->scales[row ^ 1]"),
     "int8_append_v_from_k": ("v_scales + row, v_new + src", "v_scales + row, k_new + src"),
+    "qkv_weight_transposed": ("acc += bf16_to_double(xt[k]) * bf16_to_double(wn[k]);",
+                              "acc += bf16_to_double(xt[k]) * bf16_to_double(w[(size_t)k * n_out + n]);"),
+    "qkv_k_from_q_slice": ("memcpy(k_pool + dst, y + nq + (size_t)g * head_dim",
+                           "memcpy(k_pool + dst, y + (size_t)g * head_dim"),
+    "qkv_v_from_k_slice": ("memcpy(v_pool + dst, y + nq + nkv + (size_t)g * head_dim",
+                           "memcpy(v_pool + dst, y + nq + (size_t)g * head_dim"),
+    "qkv_round_truncates": ("ldexp(nearbyint(ldexp(a, -q)), q)", "ldexp(trunc(ldexp(a, -q)), q)"),
+    "qkv_round_half_away": ("ldexp(nearbyint(ldexp(a, -q)), q)", "ldexp(round(ldexp(a, -q)), q)"),
     "softmax_sum_skips_last": ("for (int j = 0; j < nkeys; ++j) {\n        z[j] = exp",
                                "for (int j = 0; j < nkeys - 1; ++j) {\n        z[j] = exp"),
 }
