@@ -30,6 +30,7 @@ BLOCK_EXPORTS = ("pkv_bm_create", "pkv_bm_destroy", "pkv_bm_available", "pkv_bm_
                  "pkv_bm_free_sequence", "pkv_bm_block_table", "pkv_bm_cache_prefix", "pkv_bm_fork",
                  "pkv_copy_blocks")
 INT8_EXPORTS = ("pkv_kv_append_int8", "pkv_decode_int8_workspace_bytes", "pkv_paged_gqa_decode_int8")
+QKV_EXPORTS = ("pkv_qkv_project_append",)
 
 
 class PkvError(RuntimeError):
@@ -84,6 +85,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_paged_gqa_decode_int8.restype = I32
     lib.pkv_paged_gqa_decode_int8.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I64, I32, I32, I32, I32, I32, I32,
                                               F32, P, SZ, P]
+    lib.pkv_qkv_project_append.restype = I32
+    lib.pkv_qkv_project_append.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, I32, P]
     lib.pkv_paged_gqa_prefill.restype = I32
     lib.pkv_paged_gqa_prefill.argtypes = [P, P, P, I32, I32, P, P, P, I32, P, I32, I32, I32, I32, I32, I32, I32,
                                           F32, P]
@@ -322,6 +325,36 @@ def paged_gqa_decode_int8(q, k_codes, v_codes, k_scales, v_scales, block_table, 
                                         _stream())
     _check(st, "paged_gqa_decode_int8")
     return out
+
+
+def qkv_project_append(x, w_qkv, k_pool, v_pool, cu_new_lens, ctx_lens, block_table, num_q_heads: int, *,
+                       q_out=None):
+    """The fused QKV projection (see ``pkv_qkv_project_append``): ``x [T][d_model]``
+    times the merged weight ``w_qkv [(Hq + 2 Hkv) D][d_model]``; returns
+    ``q_out [T][Hq][D]`` and writes the k / v rows into the pools."""
+    NB, Hkv, B, D = _pool_shape(k_pool, v_pool)
+    _bf16(x, "x", 2)
+    _bf16(w_qkv, "w_qkv", 2)
+    T, dm = x.shape
+    if tuple(w_qkv.shape) != ((num_q_heads + 2 * Hkv) * D, dm):
+        raise ValueError("w_qkv must be [(num_q_heads + 2 num_kv_heads) head_dim][d_model]")
+    _i32(cu_new_lens, "cu_new_lens", 1)
+    _i32(ctx_lens, "ctx_lens", 1)
+    _i32(block_table, "block_table", 2)
+    S = ctx_lens.shape[0]
+    if cu_new_lens.shape[0] != S + 1 or block_table.shape[0] != S:
+        raise ValueError("cu_new_lens must have num_seqs+1 entries and block_table num_seqs rows")
+    if q_out is None:
+        q_out = torch.empty((T, num_q_heads, D), dtype=torch.bfloat16, device=x.device)
+    _bf16(q_out, "q_out", 3)
+    if tuple(q_out.shape) != (T, num_q_heads, D):
+        raise ValueError("q_out must be [T][num_q_heads][head_dim]")
+    st = lib().pkv_qkv_project_append(q_out.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), x.data_ptr(),
+                                     w_qkv.data_ptr(), cu_new_lens.data_ptr(), ctx_lens.data_ptr(),
+                                     block_table.data_ptr(), block_table.shape[1], S, T, dm, num_q_heads, Hkv, D, B,
+                                     NB, _stream())
+    _check(st, "qkv_project_append")
+    return q_out
 
 
 def copy_blocks(k_pool, v_pool, src_ids, dst_ids) -> None:

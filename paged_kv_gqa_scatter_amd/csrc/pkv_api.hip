@@ -8,6 +8,7 @@
 #include "../../include/pkv.h"
 #include "../../include/pkv_blocks.h"
 #include "../../include/pkv_int8.h"
+#include "../../include/pkv_qkv.h"
 #include "pkv_launch.h"
 
 namespace pkv {
@@ -114,6 +115,30 @@ int32_t pkv_kv_append_int8(int8_t* k_codes, int8_t* v_codes, float* k_scales, fl
                  num_seqs, total_new_tokens, num_kv_heads, head_dim, block_size, num_blocks,
                  k_codes, v_codes, k_scales, v_scales};
     return hip_status(launch_kv_append(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pkv_qkv_project_append(uint16_t* q_out, uint16_t* k_pool, uint16_t* v_pool, const uint16_t* x,
+                               const uint16_t* w_qkv, const int32_t* cu_new_lens, const int32_t* ctx_lens,
+                               const int32_t* block_table, int32_t max_blocks_per_seq, int32_t num_seqs,
+                               int32_t total_new_tokens, int32_t d_model, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t num_blocks, void* stream) {
+    int32_t st = check_heads(num_q_heads, num_kv_heads, head_dim, block_size);
+    if (st != PKV_OK) return st;
+    if (num_seqs < 0 || total_new_tokens < 0 || num_blocks < 0 || max_blocks_per_seq < 0) return PKV_ERR_BAD_SHAPE;
+    if (d_model <= 0 || d_model % 64 != 0) return PKV_ERR_BAD_SHAPE;
+    if (total_new_tokens > 0 && (num_seqs == 0 || num_blocks == 0 || max_blocks_per_seq == 0))
+        return PKV_ERR_BAD_SHAPE;
+    if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PKV_ERR_BAD_SHAPE;
+    const int64_t n_out = (int64_t)(num_q_heads + 2 * num_kv_heads) * head_dim;
+    if ((int64_t)total_new_tokens * d_model >= (1ll << 30) || n_out * d_model >= (1ll << 30)) return PKV_ERR_BAD_SHAPE;
+    if (total_new_tokens == 0) return PKV_OK;
+    if (!q_out || !k_pool || !v_pool || !x || !w_qkv || !cu_new_lens || !ctx_lens || !block_table)
+        return PKV_ERR_NULL_POINTER;
+    if (!aligned16(q_out) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(x) || !aligned16(w_qkv))
+        return PKV_ERR_MISALIGNED;
+    QkvArgs a{q_out, k_pool, v_pool, x, w_qkv, cu_new_lens, ctx_lens, block_table, max_blocks_per_seq,
+              num_seqs, total_new_tokens, d_model, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks};
+    return hip_status(launch_qkv_append(a, static_cast<hipStream_t>(stream)));
 }
 
 int32_t pkv_copy_blocks(uint16_t* k_pool, uint16_t* v_pool, const int32_t* src_ids, const int32_t* dst_ids,

@@ -86,6 +86,28 @@ struct PrefillArgs {
     float scale;
 };
 
+// Fused QKV projection + paged append: y = x W^T, q part to q_out, k / v
+// parts to the pools at each token's slot.
+struct QkvArgs {
+    uint16_t* q_out;        // [T][Hq * D]
+    uint16_t* k_pool;
+    uint16_t* v_pool;
+    const uint16_t* x;      // [T][d_model]
+    const uint16_t* w;      // [(Hq + 2 Hkv) * D][d_model]
+    const int32_t* cu_new_lens;
+    const int32_t* ctx_lens;
+    const int32_t* block_table;
+    int32_t max_blocks_per_seq;
+    int32_t num_seqs;
+    int32_t total_new_tokens;
+    int32_t d_model;        // a multiple of 64
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+    int32_t num_blocks;
+};
+
 // Decode split plan: keys per split and workspace layout, a pure function of
 // host-known shapes so that the size query and the launch always agree.
 // tile_keys: keys per tile of the kernel (kDecodeTileKeys / kDecodeInt8TileKeys).
@@ -131,6 +153,7 @@ hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
 hipError_t launch_decode_int8(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_qkv_append(const QkvArgs& a, hipStream_t stream);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

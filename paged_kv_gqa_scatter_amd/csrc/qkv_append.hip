@@ -1,0 +1,227 @@
+// qkv_project_append: the fused QKV projection whose epilogue writes k and v
+// straight into the paged cache.
+//
+// "扔掉 vLLM！从零构建 Qwen3-8B 推理引擎" section 4.4.3 computes q, k and v with
+// one matmul against the merged weight W = [W_q; W_k; W_v] and cuts the output
+// into the three parts; the k and v rows are then appended to the cache
+// (section 4.3.1).  Here the two steps are one kernel: Y = X W^T in bf16 on
+// the matrix cores with fp32 accumulation, and each output tile is rounded to
+// bf16 and stored where it belongs -- q rows to q_out, k and v rows to the
+// (block, KV head, slot) their token's position maps to -- so the k/v rows
+// never make a round trip through HBM between a projection and an append.
+//
+// gfx950 design:
+//  * Workgroup = 4 waves = a 128 x 128 tile of Y (tokens x output features);
+//    each wave computes a 64 x 64 quarter as 2 x 2 v_mfma_f32_32x32x16_bf16
+//    tiles.  Both X [T][d_model] and W [N][d_model] are row-major with d_model
+//    contiguous, so both operands are read as rows.
+//  * K steps of 64: the X and W slices of a step (2 x 16 KB) are copied into
+//    LDS with global_load_lds_dwordx4, double-buffered, one barrier per step;
+//    the copy of step k + 1 runs while step k is multiplied.  Each lane's
+//    global offset is fixed for the workgroup (rows past the end repeat the
+//    last row); the step moves the scalar base.  16-byte pieces are
+//    XOR-swizzled per row so that the 16 rows an MFMA operand read touches
+//    fall on distinct banks.
+//  * Tiles are dealt so that each XCD (workgroups go round-robin over 8)
+//    works through a contiguous run of tiles, the token tiles of one feature
+//    tile together: that W slice is then read from HBM once into the XCD's L2.
+//  * Epilogue: a lane holds one feature column and 16 token rows of each
+//    32 x 32 tile; the destination row of every token of the tile (its q_out
+//    row and its cache slot) is computed once per workgroup into LDS.
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kQkvThreads = 256;
+constexpr int kTileM = 128;  // tokens per workgroup
+constexpr int kTileN = 128;  // output features per workgroup
+constexpr int kTileK = 64;   // d_model per step
+constexpr int kRowBytes = kTileK * 2;
+constexpr int kStageBytes = kTileM * kRowBytes;  // one operand's slice of a step
+constexpr int kXcds = 8;
+
+struct QkvKernelArgs {
+    QkvArgs a;
+    int32_t n_out;    // (Hq + 2 Hkv) * D
+    int32_t m_tiles;  // token tiles
+    int32_t tiles;    // token tiles * feature tiles
+    int32_t per_xcd;  // tiles dealt to each XCD
+};
+
+// global_load_lds_dwordx4 with a scalar base: lane l's 16 bytes at
+// base + voff land at LDS byte address lds + 16 l.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Slot of 16-byte piece p of LDS row r (8 pieces per 128-byte row; an
+// involution).  Two rows share a 256-byte bank sweep, so rows 2j and 2j + 1
+// get key j: an operand read (16 consecutive rows, one piece) hits 16
+// distinct bank groups.
+__device__ __forceinline__ int swz(int r, int p) { return p ^ ((r >> 1) & 7); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__global__ __launch_bounds__(kQkvThreads) void qkv_append_kernel(QkvKernelArgs p) {
+    __shared__ __attribute__((aligned(16))) uint8_t sX[2][kStageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t sW[2][kStageBytes];
+    __shared__ int64_t s_dst[kTileM];  // per token of the tile: element offset of (block, head 0, slot), or -1
+
+    const QkvArgs& a = p.a;
+    // tile of this workgroup: a contiguous run of tiles per XCD, token tiles fastest
+    const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+    const int tile = xcd * p.per_xcd + j;
+    if (j >= p.per_xcd || tile >= p.tiles) return;
+    const int m0 = (tile % p.m_tiles) * kTileM;
+    const int n0 = (tile / p.m_tiles) * kTileN;
+    const int T = a.total_new_tokens, K = a.d_model;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    // destination rows of the tile's tokens (where kv_append would write them)
+    if (threadIdx.x < kTileM) {
+        const int t = m0 + threadIdx.x;
+        int64_t dst = -1;
+        if (t < T) {
+            int lo = 0, hi = a.num_seqs - 1;  // the sequence owning row t: last s with cu[s] <= t
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (a.cu_new_lens[mid] <= t) lo = mid; else hi = mid - 1;
+            }
+            const int64_t pos = (int64_t)a.ctx_lens[lo] + (t - a.cu_new_lens[lo]);
+            const int64_t lb = pos / a.block_size;
+            if (pos >= 0 && lb < a.max_blocks_per_seq) {
+                const int blk = a.block_table[(int64_t)lo * a.max_blocks_per_seq + lb];
+                if (blk >= 0 && blk < a.num_blocks)
+                    dst = ((int64_t)blk * a.num_kv_heads * a.block_size + (pos & (a.block_size - 1))) * a.head_dim;
+            }
+        }
+        s_dst[threadIdx.x] = dst;
+    }
+
+    // copy lanes: wave w moves rows [32 w, 32 w + 32) of both slices, 8 rows per load
+    uint32_t xoff[4], woff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 32 * wave + 8 * i + lane / 8;
+        const int piece = swz(r, lane % 8);
+        xoff[i] = (uint32_t)((int64_t)min(m0 + r, T - 1) * K * 2 + piece * 16);
+        woff[i] = (uint32_t)((int64_t)min(n0 + r, p.n_out - 1) * K * 2 + piece * 16);
+    }
+    auto issue = [&](int step, int stage) {
+        const uint16_t* xb = a.x + (int64_t)step * kTileK;
+        const uint16_t* wb = a.w + (int64_t)step * kTileK;
+        const uint32_t lx = lds_addr(sX[stage]) + (uint32_t)(32 * wave * kRowBytes);
+        const uint32_t lw = lds_addr(sW[stage]) + (uint32_t)(32 * wave * kRowBytes);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            dma16(xb, xoff[i], lx + i * 1024);
+            dma16(wb, woff[i], lw + i * 1024);
+        }
+    };
+
+    // operand reads: lane -> row (lane % 32) of a 32-row block, piece 2 s + lane / 32 of step s
+    const int wm = wave & 1, wn = wave >> 1;
+    int aoff[2][4], boff[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int ra = 64 * wm + 32 * t + (lane & 31), rb = 64 * wn + 32 * t + (lane & 31);
+            aoff[t][s] = ra * kRowBytes + swz(ra, 2 * s + (lane >> 5)) * 16;
+            boff[t][s] = rb * kRowBytes + swz(rb, 2 * s + (lane >> 5)) * 16;
+        }
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][jj][e] = 0.f;
+
+    const int steps = K / kTileK;
+    issue(0, 0);
+    for (int st = 0; st < steps; ++st) {
+        const int cur = st & 1;
+        wait_vm_all();     // this wave's copies of step st have landed
+        __syncthreads();   // everyone's have, and nobody still reads the other stage
+        if (st + 1 < steps) issue(st + 1, cur ^ 1);
+        const uint8_t* xs = sX[cur];
+        const uint8_t* ws = sW[cur];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            u32x4 af[2], bfr[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                af[t] = *reinterpret_cast<const u32x4*>(xs + aoff[t][s]);
+                bfr[t] = *reinterpret_cast<const u32x4*>(ws + boff[t][s]);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[i]), as_bf16x8(bfr[jj]),
+                                                                         acc[i][jj], 0, 0, 0);
+        }
+    }
+
+    // epilogue: lane holds column n of each 32 x 32 tile and rows 8 g + 4 (lane / 32) + e
+    const int nq = a.num_q_heads * a.head_dim, nkv = a.num_kv_heads * a.head_dim;
+    const int64_t slot_elems = (int64_t)a.block_size * a.head_dim;  // one (block, head) slab
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int n = n0 + 64 * wn + 32 * jj + (lane & 31);
+        if (n >= p.n_out) continue;
+        uint16_t* base;
+        int64_t col;
+        bool to_cache = false;
+        if (n < nq) {
+            base = a.q_out;
+            col = n;
+        } else {
+            const int f = n < nq + nkv ? n - nq : n - nq - nkv;
+            base = n < nq + nkv ? a.k_pool : a.v_pool;
+            col = (int64_t)(f / a.head_dim) * slot_elems + f % a.head_dim;
+            to_cache = true;
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = 64 * wm + 32 * i + 8 * (e / 4) + 4 * (lane >> 5) + (e & 3);
+                const int t = m0 + r;
+                if (t >= T) continue;
+                const uint16_t v = __builtin_bit_cast(uint16_t, (__bf16)acc[i][jj][e]);
+                if (!to_cache) {
+                    base[(int64_t)t * nq + col] = v;
+                } else {
+                    const int64_t d = s_dst[r];  // + col: the head's slab and the dim
+                    if (d >= 0) base[d + col] = v;
+                }
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_qkv_append(const QkvArgs& a, hipStream_t stream) {
+    if (a.total_new_tokens == 0) return hipSuccess;
+    QkvKernelArgs kp;
+    kp.a = a;
+    kp.n_out = (a.num_q_heads + 2 * a.num_kv_heads) * a.head_dim;
+    kp.m_tiles = (a.total_new_tokens + kTileM - 1) / kTileM;
+    kp.tiles = kp.m_tiles * ((kp.n_out + kTileN - 1) / kTileN);
+    kp.per_xcd = (kp.tiles + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL(qkv_append_kernel, dim3((unsigned)(kp.per_xcd * kXcds)), dim3(kQkvThreads), 0, stream, kp);
+    return hipGetLastError();
+}
+
+}  // namespace pkv

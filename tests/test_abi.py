@@ -13,6 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pkv.h")
 BLOCKS_HEADER = os.path.join(ROOT, "include", "pkv_blocks.h")
 INT8_HEADER = os.path.join(ROOT, "include", "pkv_int8.h")
+QKV_HEADER = os.path.join(ROOT, "include", "pkv_qkv.h")
 
 
 @pytest.fixture(scope="module")
@@ -43,9 +44,14 @@ def test_int8_header_declares_its_functions():
     assert set(declared_functions(INT8_HEADER)) == set(pkv.INT8_EXPORTS)
 
 
+def test_qkv_header_declares_its_functions():
+    assert set(declared_functions(QKV_HEADER)) == set(pkv.QKV_EXPORTS)
+
+
 def test_every_declared_symbol_is_exported(lib):
-    for name in declared_functions() + declared_functions(BLOCKS_HEADER) + declared_functions(INT8_HEADER):
-        assert hasattr(lib, name), name
+    for header in (HEADER, BLOCKS_HEADER, INT8_HEADER, QKV_HEADER):
+        for name in declared_functions(header):
+            assert hasattr(lib, name), name
 
 
 def test_version_and_status_strings(lib):
@@ -198,3 +204,25 @@ def test_decode_int8_workspace_bytes(lib):
     assert f(8, 32, 8, 96, 2049, 0) == 0
     assert f(8, 32, 8, 128, 2049, 0) > 0
     assert f(272, 32, 8, 128, 32769, 1_830_000) < f(272, 32, 8, 128, 32769, 0)
+
+
+def qkv_args(**kw):
+    a = dict(q=A16, kp=A16, vp=A16, x=A16, w=A16, cu=A16, ctx=A16, table=A16, mbs=4, S=2, T=3, dm=4096, hq=32,
+             hkv=8, d=128, bs=256, nb=10, stream=None)
+    a.update(kw)
+    return tuple(a[k] for k in ("q", "kp", "vp", "x", "w", "cu", "ctx", "table", "mbs", "S", "T", "dm", "hq", "hkv",
+                                "d", "bs", "nb", "stream"))
+
+
+def test_qkv_project_append_rejects(lib):
+    f = lib.pkv_qkv_project_append
+    assert f(*qkv_args(dm=4000)) == 2          # d_model not a multiple of 64
+    assert f(*qkv_args(hq=30)) == 2
+    assert f(*qkv_args(d=96)) == 2
+    assert f(*qkv_args(bs=48)) == 2
+    assert f(*qkv_args(T=300000)) == 2         # T * d_model past 2^30
+    assert f(*qkv_args(S=0)) == 2
+    assert f(*qkv_args(w=None)) == 1
+    assert f(*qkv_args(q=None)) == 1
+    assert f(*qkv_args(x=A16 + 2)) == 3
+    assert f(*qkv_args(T=0, x=None)) == 0
