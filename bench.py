@@ -20,7 +20,8 @@ sequences) is reported under ``long_context_decode``, the mixed
 continuous-batching step (64 decodes + two 512-row chunks) under
 ``mixed_step``, and the INT8 KV cache (quantising append, decode over codes
 and per-row scales) on the headline step and the long-context decode under
-``int8_kv_cache``.
+``int8_kv_cache``, and the fused QKV projection with its paged append
+(prefill prompts and decode step shapes) under ``qkv_project_append``.
 
 Kernel durations are measured with HIP events on the stream the kernels run
 on; ``roofline`` relates the decode call to HBM peak, ``prefill.roofline`` the
@@ -60,6 +61,7 @@ def parse():
     ap.add_argument("--no-long", action="store_true", help="skip the long-context decode measurement")
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed continuous-batching step")
     ap.add_argument("--no-int8", action="store_true", help="skip the INT8 KV cache measurements")
+    ap.add_argument("--no-qkv", action="store_true", help="skip the fused QKV projection measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile-pass", action="store_true",
                     help="for counter runs: a few untimed steps of each kernel plus a reference device copy, no JSON")
@@ -391,6 +393,69 @@ def time_int8(args, bf16_step_ms, bf16_long_ms):
     return res
 
 
+def time_qkv(args):
+    """The fused QKV projection + paged append at Qwen3-8B layer shapes
+    (d_model 4096, 32 / 8 heads of 128, merged weight 6144 x 4096): the
+    prefill prompts (4 x U[1024, 4096] tokens; flops 2 T N d_model against
+    the bf16 MFMA peak) and the decode step (8 tokens; the weight and input
+    bytes it must read against HBM peak).  Inputs are N(0, 1) drawn on the
+    device (timing only)."""
+    import torch
+    import paged_kv_gqa_scatter_amd as pkv
+    from paged_kv_gqa_scatter_amd import workloads as W
+
+    res = {}
+    dm, hq, hkv, d = 4096, 32, 8, 128
+    n_out = (hq + 2 * hkv) * d
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0x9C7)
+    w = (torch.randn((n_out, dm), generator=gen, device="cuda") / 64).to(torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    for name, case in (("prefill_prompts", W.config3_prefill(draw_values=False)),
+                       ("decode_step", W.config2_decode(draw_values=False))):
+        a = case.steps[0].append
+        T = int(a.cu_new_lens[-1])
+        x = torch.randn((T, dm), generator=gen, device="cuda").to(torch.bfloat16)
+        shape = (case.num_blocks, hkv, case.block_size, d)
+        kp = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+        vp = torch.zeros_like(kp)
+        q = torch.empty((T, hq, d), dtype=torch.bfloat16, device="cuda")
+        cu, ctx, tab = (torch.from_numpy(np.ascontiguousarray(v)).cuda() for v in (a.cu_new_lens, a.ctx_lens,
+                                                                                    a.block_table))
+        call = lambda: pkv.qkv_project_append(x, w, kp, vp, cu, ctx, tab, hq, q_out=q)
+        t = time.perf_counter()
+        while time.perf_counter() - t < 0.3:
+            call()
+            torch.cuda.synchronize()
+        n = max(10, args.prefill_steps)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            call()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+        flops = 2 * T * n_out * dm
+        nbytes = (n_out * dm + T * dm + T * n_out) * 2
+        r = {"tokens": T, "ms": round(ms, 5), "flops": int(flops), "bytes": int(nbytes)}
+        if name == "prefill_prompts":
+            tfs = flops / (ms * 1e-3) / 1e12
+            r["roofline"] = {"bound": "mfma", "kernel": "qkv_project_append (qkv_append_kernel)",
+                             "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                             "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}
+        else:
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            r["roofline"] = {"bound": "hbm", "kernel": "qkv_project_append (qkv_append_kernel)",
+                             "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        res[name] = r
+        del x, kp, vp, q
+        torch.cuda.empty_cache()
+    res["workload"] = ("qwen3-8b fused QKV projection + paged append: x [T][4096] times the merged weight "
+                       "[6144][4096], q to q_out, k/v rows into 256-token blocks")
+    return res
+
+
 def cpu_baseline(case, dec, kv_bytes, seconds):
     """The fp64 oracle on the same decode step, repeated for about `seconds`."""
     import oracle
@@ -471,6 +536,8 @@ def main():
             line["prefill"]["roofline"]["traffic"] = int(prec["hbm_bytes_per_launch"])
     if not args.no_long:
         line["long_context_decode"] = time_long_decode(args)
+    if not args.no_qkv:
+        line["qkv_project_append"] = time_qkv(args)
     if not args.no_int8:
         line["int8_kv_cache"] = time_int8(args, step_ms, line.get("long_context_decode", {}).get("ms"))
     if not args.no_mixed:

@@ -28,6 +28,8 @@
 //  * Epilogue: a lane holds one feature column and 16 token rows of each
 //    32 x 32 tile; the destination row of every token of the tile (its q_out
 //    row and its cache slot) is computed once per workgroup into LDS.
+//  * Calls with too few tokens to give every CU a 128 x 128 tile (decode
+//    steps) use 32 x 32 tiles with d_model split over the waves instead.
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -35,6 +37,7 @@ namespace pkv {
 namespace {
 
 constexpr int kQkvThreads = 256;
+constexpr int kQkvWaves = kQkvThreads / kWave;
 constexpr int kTileM = 128;  // tokens per workgroup
 constexpr int kTileN = 128;  // output features per workgroup
 constexpr int kTileK = 64;   // d_model per step
@@ -70,6 +73,53 @@ __device__ __forceinline__ int swz(int r, int p) { return p ^ ((r >> 1) & 7); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Element offset of (block, KV head 0, slot) of packed token t in the
+// pools, where kv_append would write it; -1 if t has no valid slot.
+__device__ __forceinline__ int64_t token_dst(const QkvArgs& a, int t) {
+    if (t >= a.total_new_tokens) return -1;
+    int lo = 0, hi = a.num_seqs - 1;  // the sequence owning row t: last s with cu[s] <= t
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.cu_new_lens[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int64_t pos = (int64_t)a.ctx_lens[lo] + (t - a.cu_new_lens[lo]);
+    const int64_t lb = pos / a.block_size;
+    if (pos < 0 || lb >= a.max_blocks_per_seq) return -1;
+    const int blk = a.block_table[(int64_t)lo * a.max_blocks_per_seq + lb];
+    if (blk < 0 || blk >= a.num_blocks) return -1;
+    return ((int64_t)blk * a.num_kv_heads * a.block_size + (pos & (a.block_size - 1))) * a.head_dim;
+}
+
+// Store a 32 x 32 tile of Y as bf16: this lane's column n, rows
+// r0 + 8 j + 4 (lane / 32) + i of the workgroup's tokens (token m0 + row).
+// q columns go to q_out; k / v columns to the token's cache slot (dst[row]).
+__device__ __forceinline__ void store_tile(const QkvArgs& a, int n_out, const f32x16& acc, int m0, int r0, int n,
+                                           const int64_t* dst) {
+    if (n >= n_out) return;
+    const int lane = threadIdx.x & 63;
+    const int nq = a.num_q_heads * a.head_dim, nkv = a.num_kv_heads * a.head_dim;
+    uint16_t* base = a.q_out;
+    int64_t col = n;
+    const bool to_cache = n >= nq;
+    if (to_cache) {
+        const int f = n < nq + nkv ? n - nq : n - nq - nkv;
+        base = n < nq + nkv ? a.k_pool : a.v_pool;
+        col = (int64_t)(f / a.head_dim) * a.block_size * a.head_dim + f % a.head_dim;  // head's slab + dim
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int r = r0 + 8 * (e / 4) + 4 * (lane >> 5) + (e & 3);
+        const int t = m0 + r;
+        if (t >= a.total_new_tokens) continue;
+        const uint16_t v = __builtin_bit_cast(uint16_t, (__bf16)acc[e]);
+        if (!to_cache) {
+            base[(int64_t)t * nq + col] = v;
+        } else if (dst[r] >= 0) {
+            base[dst[r] + col] = v;
+        }
+    }
+}
+
 __global__ __launch_bounds__(kQkvThreads) void qkv_append_kernel(QkvKernelArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t sX[2][kStageBytes];
     __shared__ __attribute__((aligned(16))) uint8_t sW[2][kStageBytes];
@@ -86,25 +136,7 @@ __global__ __launch_bounds__(kQkvThreads) void qkv_append_kernel(QkvKernelArgs p
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
     // destination rows of the tile's tokens (where kv_append would write them)
-    if (threadIdx.x < kTileM) {
-        const int t = m0 + threadIdx.x;
-        int64_t dst = -1;
-        if (t < T) {
-            int lo = 0, hi = a.num_seqs - 1;  // the sequence owning row t: last s with cu[s] <= t
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (a.cu_new_lens[mid] <= t) lo = mid; else hi = mid - 1;
-            }
-            const int64_t pos = (int64_t)a.ctx_lens[lo] + (t - a.cu_new_lens[lo]);
-            const int64_t lb = pos / a.block_size;
-            if (pos >= 0 && lb < a.max_blocks_per_seq) {
-                const int blk = a.block_table[(int64_t)lo * a.max_blocks_per_seq + lb];
-                if (blk >= 0 && blk < a.num_blocks)
-                    dst = ((int64_t)blk * a.num_kv_heads * a.block_size + (pos & (a.block_size - 1))) * a.head_dim;
-            }
-        }
-        s_dst[threadIdx.x] = dst;
-    }
+    if (threadIdx.x < kTileM) s_dst[threadIdx.x] = token_dst(a, m0 + threadIdx.x);
 
     // copy lanes: wave w moves rows [32 w, 32 w + 32) of both slices, 8 rows per load
     uint32_t xoff[4], woff[4];
@@ -173,41 +205,85 @@ __global__ __launch_bounds__(kQkvThreads) void qkv_append_kernel(QkvKernelArgs p
         }
     }
 
-    // epilogue: lane holds column n of each 32 x 32 tile and rows 8 g + 4 (lane / 32) + e
-    const int nq = a.num_q_heads * a.head_dim, nkv = a.num_kv_heads * a.head_dim;
-    const int64_t slot_elems = (int64_t)a.block_size * a.head_dim;  // one (block, head) slab
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-        const int n = n0 + 64 * wn + 32 * jj + (lane & 31);
-        if (n >= p.n_out) continue;
-        uint16_t* base;
-        int64_t col;
-        bool to_cache = false;
-        if (n < nq) {
-            base = a.q_out;
-            col = n;
-        } else {
-            const int f = n < nq + nkv ? n - nq : n - nq - nkv;
-            base = n < nq + nkv ? a.k_pool : a.v_pool;
-            col = (int64_t)(f / a.head_dim) * slot_elems + f % a.head_dim;
-            to_cache = true;
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+            store_tile(a, p.n_out, acc[i][jj], m0, 64 * wm + 32 * i, n0 + 64 * wn + 32 * jj + (lane & 31), s_dst);
+}
+
+// Few tokens (a decode step): the weight stream dominates and 128 x 128 tiles
+// would leave most CUs idle, so a workgroup takes a 32 x 32 tile and its four
+// waves split d_model (wave w: 64-wide steps w, w + 4, ..., three in flight),
+// reducing through LDS at the end.  Operands come straight from global memory: lane (row i,
+// half h) loads 64 contiguous bytes of its X row and of its W row per step
+// (d_model k0 + 32 h .. k0 + 32 h + 31), and MFMA s of the step contracts
+// bytes [16 s, 16 s + 16) of each -- the same order of d_model on both sides.
+__global__ __launch_bounds__(kQkvThreads) void qkv_append_skinny_kernel(QkvKernelArgs p) {
+    __shared__ float s_red[kQkvWaves - 1][16][kWave];
+    __shared__ int64_t s_dst[32];
+
+    const QkvArgs& a = p.a;
+    const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+    const int tile = xcd * p.per_xcd + j;
+    if (j >= p.per_xcd || tile >= p.tiles) return;
+    const int m0 = (tile % p.m_tiles) * 32;
+    const int n0 = (tile / p.m_tiles) * 32;
+    const int T = a.total_new_tokens, K = a.d_model;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (threadIdx.x < 32) s_dst[threadIdx.x] = token_dst(a, m0 + threadIdx.x);
+
+    const int h = lane >> 5;
+    const uint16_t* xr = a.x + (int64_t)min(m0 + (lane & 31), T - 1) * K + 32 * h;
+    const uint16_t* wr = a.w + (int64_t)min(n0 + (lane & 31), p.n_out - 1) * K + 32 * h;
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    // this wave's steps w, w + 4, ..., three in flight (a ring of three
+    // register sets); loads past the last step repeat it and are not used
+    const int steps = K / 64;
+    const int nsw = steps > wave ? (steps - wave + kQkvWaves - 1) / kQkvWaves : 0;
+    u32x4 x0[4], w0[4], x1[4], w1[4], x2[4], w2[4];
+    auto load = [&](u32x4* xv, u32x4* wv, int i) {
+        const int64_t k = (int64_t)(wave + kQkvWaves * min(i, nsw - 1)) * 64;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            xv[c] = load16(xr + k + 8 * c);
+            wv[c] = load16(wr + k + 8 * c);
         }
+    };
+    auto mma = [&](const u32x4* xv, const u32x4* wv) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int r = 64 * wm + 32 * i + 8 * (e / 4) + 4 * (lane >> 5) + (e & 3);
-                const int t = m0 + r;
-                if (t >= T) continue;
-                const uint16_t v = __builtin_bit_cast(uint16_t, (__bf16)acc[i][jj][e]);
-                if (!to_cache) {
-                    base[(int64_t)t * nq + col] = v;
-                } else {
-                    const int64_t d = s_dst[r];  // + col: the head's slab and the dim
-                    if (d >= 0) base[d + col] = v;
-                }
+        for (int c = 0; c < 4; ++c)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xv[c]), as_bf16x8(wv[c]), acc, 0, 0, 0);
+    };
+    if (nsw > 0) {
+        load(x0, w0, 0);
+        load(x1, w1, 1);
+        load(x2, w2, 2);
+        for (int i = 0; i < nsw; i += 3) {
+            mma(x0, w0);
+            if (i + 3 < nsw) load(x0, w0, i + 3);
+            if (i + 1 < nsw) {
+                mma(x1, w1);
+                if (i + 4 < nsw) load(x1, w1, i + 4);
             }
+            if (i + 2 < nsw) {
+                mma(x2, w2);
+                if (i + 5 < nsw) load(x2, w2, i + 5);
+            }
+        }
     }
+    if (wave > 0)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s_red[wave - 1][e][lane] = acc[e];
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < kQkvWaves - 1; ++w)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] += s_red[w][e][lane];
+    store_tile(a, p.n_out, acc, m0, 0, n0 + (lane & 31), s_dst);
 }
 
 }  // namespace
@@ -219,6 +295,14 @@ hipError_t launch_qkv_append(const QkvArgs& a, hipStream_t stream) {
     kp.n_out = (a.num_q_heads + 2 * a.num_kv_heads) * a.head_dim;
     kp.m_tiles = (a.total_new_tokens + kTileM - 1) / kTileM;
     kp.tiles = kp.m_tiles * ((kp.n_out + kTileN - 1) / kTileN);
+    if (kp.tiles < device_cu_count()) {  // too few 128 x 128 tiles to fill the chip: 32 x 32 tiles
+        kp.m_tiles = (a.total_new_tokens + 31) / 32;
+        kp.tiles = kp.m_tiles * ((kp.n_out + 31) / 32);
+        kp.per_xcd = (kp.tiles + kXcds - 1) / kXcds;
+        hipLaunchKernelGGL(qkv_append_skinny_kernel, dim3((unsigned)(kp.per_xcd * kXcds)), dim3(kQkvThreads), 0,
+                           stream, kp);
+        return hipGetLastError();
+    }
     kp.per_xcd = (kp.tiles + kXcds - 1) / kXcds;
     hipLaunchKernelGGL(qkv_append_kernel, dim3((unsigned)(kp.per_xcd * kXcds)), dim3(kQkvThreads), 0, stream, kp);
     return hipGetLastError();

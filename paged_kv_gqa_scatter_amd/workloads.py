@@ -286,24 +286,24 @@ def config1_tiny(seed: int = 1, block_size: int = 16, num_blocks: int = 32, perm
                 np.float32(0.125), [], steps)
 
 
-def config2_decode(seed: int = 2) -> Case:
+def config2_decode(seed: int = 2, draw_values: bool = True) -> Case:
     """Qwen3-8B one-layer decode step: 8 sequences, 32/8 heads, d 128,
     block 256, cached context uniform in [512, 2048]; the step appends one
     token per sequence and decodes over ctx+1 keys."""
     rng = np.random.default_rng(seed)
     ctx = rng.integers(512, 2048, size=8, endpoint=True)
     return build_case("qwen3_8b_decode_8seq_ctx512_2048", rng, hq=32, hkv=8, d=128, bs=256,
-                      ctx_lens=ctx, new_lens=np.ones(8, np.int64), kinds="d" * 8)
+                      ctx_lens=ctx, new_lens=np.ones(8, np.int64), kinds="d" * 8, draw_values=draw_values)
 
 
-def config3_prefill(seed: int = 3) -> Case:
+def config3_prefill(seed: int = 3, draw_values: bool = True) -> Case:
     """Qwen3-8B one-layer causal prefill: 4 prompts of length uniform in
     [1024, 4096], 32/8 heads, d 128, block 256; K/V are written by kv_append
     first, then the prefill attends causally over each whole prompt."""
     rng = np.random.default_rng(seed)
     lens = rng.integers(1024, 4096, size=4, endpoint=True)
     return build_case("qwen3_8b_prefill_4x1024_4096", rng, hq=32, hkv=8, d=128, bs=256,
-                      ctx_lens=np.zeros(4, np.int64), new_lens=lens, kinds="pppp")
+                      ctx_lens=np.zeros(4, np.int64), new_lens=lens, kinds="pppp", draw_values=draw_values)
 
 
 def config4_mixed(seed: int = 4) -> Case:

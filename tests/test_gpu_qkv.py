@@ -160,3 +160,16 @@ def test_qkv_qwen3_prefill_sampled(orc):
     pick |= {127, 128, 255, 256, T - 1}
     _say(f"case qkv qwen3-8b prefill prompts: T {T}, {len(pick)} tokens sampled")
     _compare(orc, x, w, 32, 8, 128, 256, case.num_blocks, cu, a.ctx_lens, a.block_table, sorted(pick), "sampled")
+
+
+def test_qkv_wide_tiles_ragged_tails(orc):
+    # enough tokens for the 128 x 128 tile path (258 tiles), with a ragged
+    # token tail (16400 = 128 * 128 + 16) and a ragged feature tail (n_out 192)
+    rng = np.random.default_rng(41)
+    hq, hkv, d, bs, dm = 1, 1, 64, 16, 128
+    table, cu, ctx, nb = _placement(rng, [3, 0, 9], [8000, 8000, 400], bs)
+    x, w = _inputs(rng, int(cu[-1]), dm, (hq + 2 * hkv) * d)
+    T = int(cu[-1])
+    pick = set(rng.choice(T, 40, replace=False).tolist()) | {0, 127, 128, 7999, 8000, 16383, 16384, T - 1}
+    _say(f"case qkv wide tiles: T {T}, n_out {(hq + 2 * hkv) * d}, {len(pick)} tokens sampled")
+    _compare(orc, x, w, hq, hkv, d, bs, nb, cu, ctx, table, sorted(pick), "wide, ragged tails")
