@@ -68,7 +68,8 @@ def parse():
     ap.add_argument("--copy-mib", type=int, default=256, help="size of the reference copy in --profile-pass")
     ap.add_argument("--profile-warm-s", type=float, default=0.0,
                     help="--profile-pass: run each workload this long before its counted calls (steady clocks)")
-    ap.add_argument("--profile-only", choices=("decode", "prefill", "long", "copy"), default=None,
+    ap.add_argument("--profile-only", choices=("decode", "prefill", "long", "int8", "qkv", "qkvdec", "copy"),
+                    default=None,
                     help="--profile-pass: run only this workload (counter passes per workload)")
     return ap.parse_args()
 
@@ -78,10 +79,13 @@ def profile_pass(args):
     decode_append launch), the prefill kernel and the long-context decode a
     few times each (the long one last, unless --no-long), and one plain
     device-to-device copy of --copy-mib MiB whose counter readings calibrate
-    the byte counters."""
+    the byte counters.  --profile-only also offers the INT8 long-context
+    decode (int8) and the fused QKV projection at the prefill-prompt (qkv)
+    and decode-step (qkvdec) shapes."""
     import torch
+    import paged_kv_gqa_scatter_amd as pkv
     from paged_kv_gqa_scatter_amd import workloads as W
-    from paged_kv_gqa_scatter_amd.runner import DeviceCase
+    from paged_kv_gqa_scatter_amd.runner import DeviceCase, Int8DeviceCase
 
     n = max(1, args.steps)
     only = args.profile_only
@@ -127,6 +131,35 @@ def profile_pass(args):
         torch.cuda.synchronize()
         del lc
         done.append(f"{n} long-context decodes")
+    if only == "int8":
+        ic = Int8DeviceCase(W.config5_prefix_long(draw_values=False))
+        ic.run_fills()
+        ic.append(ic.steps[0]["append"])
+        warm(lambda: ic.decode(ic.steps[0]["decode"]))
+        for _ in range(n):
+            ic.decode(ic.steps[0]["decode"])
+        torch.cuda.synchronize()
+        del ic
+        done.append(f"{n} INT8 long-context decodes")
+    if only in ("qkv", "qkvdec"):
+        case = W.config3_prefill(draw_values=False) if only == "qkv" else W.config2_decode(draw_values=False)
+        a = case.steps[0].append
+        T, dm, hq, hkv, d = int(a.cu_new_lens[-1]), 4096, 32, 8, 128
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(0x9C7)
+        w = (torch.randn(((hq + 2 * hkv) * d, dm), generator=gen, device="cuda") / 64).to(torch.bfloat16)
+        x = torch.randn((T, dm), generator=gen, device="cuda").to(torch.bfloat16)
+        kp = torch.zeros((case.num_blocks, hkv, case.block_size, d), dtype=torch.bfloat16, device="cuda")
+        vp = torch.zeros_like(kp)
+        q = torch.empty((T, hq, d), dtype=torch.bfloat16, device="cuda")
+        cu, ctx, tab = (torch.from_numpy(np.ascontiguousarray(v)).cuda() for v in (a.cu_new_lens, a.ctx_lens,
+                                                                                    a.block_table))
+        call = lambda: pkv.qkv_project_append(x, w, kp, vp, cu, ctx, tab, hq, q_out=q)
+        warm(call)
+        for _ in range(n):
+            call()
+        torch.cuda.synchronize()
+        done.append(f"{n} QKV projections of {T} tokens")
     torch.cuda.empty_cache()
     if only in (None, "copy"):
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda")
@@ -382,6 +415,7 @@ def time_int8(args, bf16_step_ms, bf16_long_ms):
         del dc
         torch.cuda.empty_cache()
         gbs = nbytes / (lms * 1e-3) / 1e9
+        rec = traffic_record("int8_long_decode")
         res["long_context_decode"] = {
             "workload": "the long-context decode (256 seqs on a shared 4096-token prefix + 16 x 32768) over an "
                         "INT8 cache",
@@ -389,7 +423,8 @@ def time_int8(args, bf16_step_ms, bf16_long_ms):
             "speedup_vs_bf16": round(bf16_long_ms / lms, 3) if bf16_long_ms else None,
             "roofline": {"bound": "hbm", "kernel": "paged_gqa_decode_int8 (decode_int8_kernel + decode_merge_kernel)",
                          "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": int(rec["hbm_bytes_per_launch"]) if rec else None}}
     return res
 
 
@@ -438,6 +473,7 @@ def time_qkv(args):
         flops = 2 * T * n_out * dm
         nbytes = (n_out * dm + T * dm + T * n_out) * 2
         r = {"tokens": T, "ms": round(ms, 5), "flops": int(flops), "bytes": int(nbytes)}
+        rec = traffic_record("qkv" if name == "prefill_prompts" else "qkv_decode")
         if name == "prefill_prompts":
             tfs = flops / (ms * 1e-3) / 1e12
             r["roofline"] = {"bound": "mfma", "kernel": "qkv_project_append (qkv_append_kernel)",
@@ -445,9 +481,10 @@ def time_qkv(args):
                              "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}
         else:
             gbs = nbytes / (ms * 1e-3) / 1e9
-            r["roofline"] = {"bound": "hbm", "kernel": "qkv_project_append (qkv_append_kernel)",
+            r["roofline"] = {"bound": "hbm", "kernel": "qkv_project_append (qkv_append_skinny_kernel)",
                              "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        r["roofline"]["traffic"] = int(rec["hbm_bytes_per_launch"]) if rec else None
         res[name] = r
         del x, kp, vp, q
         torch.cuda.empty_cache()
