@@ -33,7 +33,7 @@
 //    32 x 32 tile; the destination row of every token of the tile (its q_out
 //    row and its cache slot) is computed once per workgroup into LDS.
 //  * Calls with too few tokens to give every CU a 128 x 128 tile (decode
-//    steps) use 32 x 32 tiles with d_model split over the waves instead.
+//    steps) use 32 x 32 tiles with d_model split over eight waves instead.
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -41,7 +41,8 @@ namespace pkv {
 namespace {
 
 constexpr int kQkvThreads = 256;
-constexpr int kQkvWaves = kQkvThreads / kWave;
+constexpr int kSkinnyThreads = 512;  // decode-step kernel: 8 waves split d_model
+constexpr int kSkinnyWaves = kSkinnyThreads / kWave;
 constexpr int kTileM = 128;  // tokens per workgroup
 constexpr int kTileN = 128;  // output features per workgroup
 constexpr int kTileK = 64;   // d_model per step
@@ -225,14 +226,15 @@ __global__ __launch_bounds__(kQkvThreads) void qkv_append_kernel(QkvKernelArgs p
 }
 
 // Few tokens (a decode step): the weight stream dominates and 128 x 128 tiles
-// would leave most CUs idle, so a workgroup takes a 32 x 32 tile and its four
-// waves split d_model (wave w: 64-wide steps w, w + 4, ..., three in flight),
-// reducing through LDS at the end.  Operands come straight from global memory: lane (row i,
-// half h) loads 64 contiguous bytes of its X row and of its W row per step
+// would leave most CUs idle, so a workgroup takes a 32 x 32 tile and its
+// eight waves split d_model (wave w: 64-wide steps w, w + 8, ..., three in
+// flight), reducing through LDS at the end.  Operands come straight from
+// global memory: lane (row i, half h) loads 64 contiguous bytes of its X row
+// and of its W row per step
 // (d_model k0 + 32 h .. k0 + 32 h + 31), and MFMA s of the step contracts
 // bytes [16 s, 16 s + 16) of each -- the same order of d_model on both sides.
-__global__ __launch_bounds__(kQkvThreads) void qkv_append_skinny_kernel(QkvKernelArgs p) {
-    __shared__ float s_red[kQkvWaves - 1][16][kWave];
+__global__ __launch_bounds__(kSkinnyThreads) void qkv_append_skinny_kernel(QkvKernelArgs p) {
+    __shared__ float s_red[kSkinnyWaves - 1][16][kWave];
     __shared__ int64_t s_dst[32];
 
     const QkvArgs& a = p.a;
@@ -254,10 +256,10 @@ __global__ __launch_bounds__(kQkvThreads) void qkv_append_skinny_kernel(QkvKerne
     // this wave's steps w, w + 4, ..., three in flight (a ring of three
     // register sets); loads past the last step repeat it and are not used
     const int steps = K / 64;
-    const int nsw = steps > wave ? (steps - wave + kQkvWaves - 1) / kQkvWaves : 0;
+    const int nsw = steps > wave ? (steps - wave + kSkinnyWaves - 1) / kSkinnyWaves : 0;
     u32x4 x0[4], w0[4], x1[4], w1[4], x2[4], w2[4];
     auto load = [&](u32x4* xv, u32x4* wv, int i) {
-        const int64_t k = (int64_t)(wave + kQkvWaves * min(i, nsw - 1)) * 64;
+        const int64_t k = (int64_t)(wave + kSkinnyWaves * min(i, nsw - 1)) * 64;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             xv[c] = load16(xr + k + 8 * c);
@@ -292,7 +294,7 @@ __global__ __launch_bounds__(kQkvThreads) void qkv_append_skinny_kernel(QkvKerne
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
-    for (int w = 0; w < kQkvWaves - 1; ++w)
+    for (int w = 0; w < kSkinnyWaves - 1; ++w)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[e] += s_red[w][e][lane];
     store_tile(a, p.n_out, acc, m0, 0, n0 + (lane & 31), s_dst);
@@ -311,7 +313,7 @@ hipError_t launch_qkv_append(const QkvArgs& a, hipStream_t stream) {
         kp.m_tiles = (a.total_new_tokens + 31) / 32;
         kp.tiles = kp.m_tiles * ((kp.n_out + 31) / 32);
         kp.per_xcd = (kp.tiles + kXcds - 1) / kXcds;
-        hipLaunchKernelGGL(qkv_append_skinny_kernel, dim3((unsigned)(kp.per_xcd * kXcds)), dim3(kQkvThreads), 0,
+        hipLaunchKernelGGL(qkv_append_skinny_kernel, dim3((unsigned)(kp.per_xcd * kXcds)), dim3(kSkinnyThreads), 0,
                            stream, kp);
         return hipGetLastError();
     }
