@@ -1,6 +1,6 @@
 /*
- * pkv_int8.h - INT8 KV cache for libpkv: a quantising kv_append and decode
- * over the INT8 cache.
+ * pkv_int8.h - INT8 KV cache for libpkv: a quantising kv_append, decode
+ * over the INT8 cache, and the two in one launch.
  *
  * "从零搭建AI工程能力：手写KV Cache与动态批处理实战" section 3.2 keeps the KV
  * cache as 8-bit integers instead of 16-bit floats: half the memory, and half
@@ -71,6 +71,32 @@ int32_t pkv_paged_gqa_decode_int8(uint16_t* out, const uint16_t* q,
                                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                   float scale, void* workspace, size_t workspace_bytes,
                                   void* stream);
+
+/*
+ * paged_gqa_decode_append_int8: one decode step over the INT8 cache in one
+ * launch -- pkv_kv_append_int8 of one new row per sequence followed by
+ * pkv_paged_gqa_decode_int8, as pkv_paged_gqa_decode_append does for bf16.
+ *
+ *   k_new, v_new     [num_seqs][num_kv_heads][head_dim] bf16: the row of
+ *                    position seq_lens[s] - 1 of each sequence (a sequence
+ *                    with seq_lens[s] == 0 appends nothing and yields zeros)
+ *   k_codes ... v_scales  written at that position (codes and scales equal
+ *                    to pkv_kv_append_int8's)
+ *   other arguments  as for pkv_paged_gqa_decode_int8 (same workspace size)
+ *
+ * The outputs equal pkv_kv_append_int8 followed by pkv_paged_gqa_decode_int8
+ * up to summation order.  Preconditions as for both: the new rows' slots
+ * belong to their sequence alone.
+ */
+int32_t pkv_paged_gqa_decode_append_int8(uint16_t* out, const uint16_t* q,
+                                         const uint16_t* k_new, const uint16_t* v_new,
+                                         int8_t* k_codes, int8_t* v_codes, float* k_scales, float* v_scales,
+                                         const int32_t* block_table, int32_t max_blocks_per_seq,
+                                         const int32_t* seq_lens, int32_t max_seq_len, int64_t total_kv_tokens,
+                                         int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                         float scale, void* workspace, size_t workspace_bytes,
+                                         void* stream);
 
 #ifdef __cplusplus
 }

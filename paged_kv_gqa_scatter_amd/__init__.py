@@ -29,7 +29,8 @@ EXPORTS = ("pkv_abi_version", "pkv_status_string", "pkv_kv_append", "pkv_decode_
 BLOCK_EXPORTS = ("pkv_bm_create", "pkv_bm_destroy", "pkv_bm_available", "pkv_bm_seq_len", "pkv_bm_append",
                  "pkv_bm_free_sequence", "pkv_bm_block_table", "pkv_bm_cache_prefix", "pkv_bm_fork",
                  "pkv_copy_blocks")
-INT8_EXPORTS = ("pkv_kv_append_int8", "pkv_decode_int8_workspace_bytes", "pkv_paged_gqa_decode_int8")
+INT8_EXPORTS = ("pkv_kv_append_int8", "pkv_decode_int8_workspace_bytes", "pkv_paged_gqa_decode_int8",
+                "pkv_paged_gqa_decode_append_int8")
 QKV_EXPORTS = ("pkv_qkv_project_append",)
 
 
@@ -85,6 +86,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_paged_gqa_decode_int8.restype = I32
     lib.pkv_paged_gqa_decode_int8.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I64, I32, I32, I32, I32, I32, I32,
                                               F32, P, SZ, P]
+    lib.pkv_paged_gqa_decode_append_int8.restype = I32
+    lib.pkv_paged_gqa_decode_append_int8.argtypes = [P, P, P, P, P, P, P, P, P, I32, P, I32, I64, I32, I32, I32, I32,
+                                                     I32, I32, F32, P, SZ, P]
     lib.pkv_qkv_project_append.restype = I32
     lib.pkv_qkv_project_append.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, I32, P]
     lib.pkv_paged_gqa_prefill.restype = I32
@@ -355,6 +359,44 @@ def qkv_project_append(x, w_qkv, k_pool, v_pool, cu_new_lens, ctx_lens, block_ta
                                      NB, _stream())
     _check(st, "qkv_project_append")
     return q_out
+
+
+def paged_gqa_decode_append_int8(q, k_new, v_new, k_codes, v_codes, k_scales, v_scales, block_table, seq_lens,
+                                 scale: float, *, max_seq_len: int, total_kv_tokens: int = 0, out=None,
+                                 workspace=None):
+    """One INT8 decode step in one launch: quantise ``k_new/v_new [S][Hkv][D]``
+    into position ``seq_lens[s] - 1`` of each sequence, then decode
+    ``q [S][Hq][D]`` over the INT8 cache -> ``out``."""
+    NB, Hkv, B, D = _int8_cache(k_codes, v_codes, k_scales, v_scales)
+    _bf16(q, "q", 3)
+    S, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError("q head_dim differs from the cache's")
+    _bf16(k_new, "k_new", 3)
+    _bf16(v_new, "v_new", 3)
+    if tuple(k_new.shape) != (S, Hkv, D) or tuple(v_new.shape) != (S, Hkv, D):
+        raise ValueError("k_new/v_new must be [S][num_kv_heads][head_dim]")
+    _i32(block_table, "block_table", 2)
+    _i32(seq_lens, "seq_lens", 1)
+    if block_table.shape[0] != S or seq_lens.shape[0] != S:
+        raise ValueError("block_table and seq_lens need one row per sequence")
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _bf16(out, "out", 3)
+    if tuple(out.shape) != (S, Hq, D):
+        raise ValueError("out must be [S][Hq][D]")
+    need = decode_int8_workspace_bytes(S, Hq, Hkv, D, max_seq_len, total_kv_tokens) if S > 0 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
+    st = lib().pkv_paged_gqa_decode_append_int8(out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                               k_codes.data_ptr(), v_codes.data_ptr(), k_scales.data_ptr(),
+                                               v_scales.data_ptr(), block_table.data_ptr(), block_table.shape[1],
+                                               seq_lens.data_ptr(), max_seq_len, total_kv_tokens, S, Hq, Hkv, D, B,
+                                               NB, float(scale), workspace.data_ptr(), workspace.numel(), _stream())
+    _check(st, "paged_gqa_decode_append_int8")
+    return out
 
 
 def copy_blocks(k_pool, v_pool, src_ids, dst_ids) -> None:

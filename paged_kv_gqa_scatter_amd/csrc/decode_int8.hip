@@ -28,6 +28,11 @@
 //  * Keys past the sequence end are masked to -inf and their v_scale taken
 //    as 0, so neither an unwritten code (any byte is a finite code) nor an
 //    unwritten scale (possibly NaN) reaches the result.
+//  * decode_append_int8 folds the step's kv_append_int8 into the launch, as
+//    decode_append does for bf16: every workgroup quantises its sequence's
+//    new row (its lanes hold the row, the row maximum is a butterfly), and
+//    the wave whose tile holds key L - 1 writes codes and scales to the cache
+//    and patches them into its LDS stage once the tile's copy has landed.
 #include "decode_common.h"
 
 namespace pkv {
@@ -108,6 +113,10 @@ struct Int8WaveItem {
     const DecodeArgs* a;
     int log2_block, g, k0, kend, wave, lane, n_tiles;
     int ids0, ids1;  // block id of tile t in lane t % 64 of ids(t / 64)
+    int L;           // keys of the sequence
+    bool append;     // decode_append_int8: the new row (this lane's codes, the scales) is key L - 1
+    u32x2 kq, vq;
+    float ks_new, vs_new;
     float c;         // scale * log2 e
     u32x4 qf[D / 32];
     Int8Lanes<D> tl;
@@ -152,6 +161,38 @@ __device__ __forceinline__ void issue8(const Int8WaveItem<D>& w, int t, int stag
     }
 }
 
+// decode_append_int8, on the tile holding key L - 1 (row r0 of the tile):
+// the new row's codes and scales replace that row of the wave's stage (its
+// copy may predate the store) and go to the cache.
+template <int D>
+__device__ __forceinline__ void put_new_row8(const Int8WaveItem<D>& w, int t, int kS) {
+    constexpr int kHalves = D / 8;  // 8-byte halves of 16-byte pieces per code row; one per lane
+    const int r0 = w.L - 1 - tile_key8(w, t);
+    const int p = w.lane % kHalves;
+    const int off = r0 * D + swz8<D>(r0, p / 2) * 16 + (p & 1) * 8;
+    if (w.lane < kHalves) {
+        *reinterpret_cast<u32x2*>(w.st.k[kS] + w.wave * kTile8 * D + off) = w.kq;
+        *reinterpret_cast<u32x2*>(w.st.v[kS] + w.wave * kTile8 * D + off) = w.vq;
+    }
+    float* ss = w.st.sc[kS] + w.wave * 2 * kTile8;
+    if (w.lane == 0) {
+        ss[r0] = w.ks_new;
+        ss[kTile8 + r0] = w.vs_new;
+    }
+    const int blk = tile_blk8(w, t);
+    if ((unsigned)blk < (unsigned)w.a->num_blocks && w.lane < 2 * kHalves) {
+        const int B = 1 << w.log2_block;
+        const int64_t row = ((int64_t)blk * w.a->num_kv_heads + w.g) * B + ((w.L - 1) & (B - 1));
+        if (w.lane < kHalves) {
+            *reinterpret_cast<u32x2*>(w.a->k_codes_w + row * D + p * 8) = w.kq;
+            if (p == 0) w.a->k_scales_w[row] = w.ks_new;
+        } else {
+            *reinterpret_cast<u32x2*>(w.a->v_codes_w + row * D + p * 8) = w.vq;
+            if (p == 0) w.a->v_scales_w[row] = w.vs_new;
+        }
+    }
+}
+
 // Eight int8 codes (two dwords, in order) -> eight bf16 (exact).
 __device__ __forceinline__ u32x4 codes_to_bf16(uint32_t lo, uint32_t hi) {
     auto cv = [](uint32_t w, int k) { return (float)((int32_t)(w << (24 - 8 * k)) >> 24); };
@@ -173,6 +214,7 @@ __device__ __forceinline__ void tile_step8(const Int8WaveItem<D>& w, int t, Wave
     else if (after == 1) wait_vmcnt<kDma>();
     else wait_vmcnt<0>();
     if (t + R - 1 < w.n_tiles) issue8(w, t + R - 1, (kS + R - 1) % R);
+    if (w.append && w.kend == w.L && tile_key8(w, t) + kTile8 >= w.kend) put_new_row8<D>(w, t, kS);
 
     // every LDS read of the tile goes out before the first MFMA waits on one
     const int8_t* sk = w.st.k[kS] + w.wave * kTile8 * D;
@@ -280,6 +322,7 @@ struct Int8Inputs {
     int L_raw;
     int ids0, ids1;
     u32x4 qf[D / 32];
+    u32x4 kn, vn;  // decode_append_int8: this lane's 8 values of the new K/V row
 };
 
 template <int D, int G>
@@ -302,6 +345,12 @@ __device__ __forceinline__ Int8Inputs<D> load_int8_inputs(const DecodeKernelArgs
     in.ids1 = p.chunk > kTile8 * kDecodeWaves * kWave
                   ? table[min((k0 + kTile8 * (wave + kDecodeWaves * (lane + kWave))) >> p.log2_block, last)]
                   : 0;
+    in.kn = in.vn = zero;
+    if (a.k_new) {
+        const int64_t row = ((int64_t)s * a.num_kv_heads + g) * D + (lane % (D / 8)) * 8;
+        in.kn = load16(a.k_new + row);
+        in.vn = load16(a.v_new + row);
+    }
     return in;
 }
 
@@ -327,6 +376,8 @@ __device__ __forceinline__ void decode_int8_item(const DecodeKernelArgs& p, Deco
     w.n_tiles = tiles > wave ? (tiles - wave + kDecodeWaves - 1) / kDecodeWaves : 0;
     w.ids0 = in.ids0;
     w.ids1 = in.ids1;
+    w.L = L;
+    w.append = a.k_new != nullptr;
     w.c = p.qk_scale_log2;
 #pragma unroll
     for (int cc = 0; cc < D / 32; ++cc) w.qf[cc] = in.qf[cc];
@@ -340,6 +391,12 @@ __device__ __forceinline__ void decode_int8_item(const DecodeKernelArgs& p, Deco
     ws.l = 0.f;
     wait_all_vm();  // the item's inputs are in
     prefetch();     // the next item's inputs travel with this item's first tiles
+    w.kq = w.vq = u32x2{0u, 0u};
+    w.ks_new = w.vs_new = 0.f;
+    if (w.append) {  // every lane group of the wave holds the row: quantise it (the scheme of kv_append_int8)
+        w.kq = quantize_piece<D / 8>(in.kn, &w.ks_new);
+        w.vq = quantize_piece<D / 8>(in.vn, &w.vs_new);
+    }
     wave_tiles8<D, R>(w, ws);
     finish_item<D, G>(p, sh, ws, s, g, nchunks, slot);
 }

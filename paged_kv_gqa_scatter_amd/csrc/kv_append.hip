@@ -58,35 +58,6 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendArgs a)
     store16(a.v_pool + dst, vv);
 }
 
-// Symmetric INT8 quantisation of one row held by `kPieces` consecutive lanes,
-// 8 values each: scale = max|x| / 127 and code = x / scale rounded to the
-// nearest integer, ties to even, in fp32 with IEEE division (an all-zero row
-// has scale 0 and codes 0).  Returns this lane's 8 codes; *scale gets the
-// row's scale on every lane of the row.
-template <int kPieces>
-__device__ __forceinline__ u32x2 quantize_piece(u32x4 x, float* scale) {
-    float f[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[2 * i] = bf16_lo(x[i]);
-        f[2 * i + 1] = bf16_hi(x[i]);
-    }
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-#pragma unroll
-    for (int off = kPieces / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
-    const float sc = amax / 127.f;
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float c = sc > 0.f ? fminf(fmaxf(rintf(f[i] / sc), -127.f), 127.f) : 0.f;
-        w[i / 4] |= ((uint32_t)(int32_t)c & 0xFFu) << (8 * (i % 4));
-    }
-    *scale = sc;
-    return u32x2{w[0], w[1]};
-}
-
 // kv_append into an INT8 cache ("从零搭建AI工程能力：手写KV Cache与动态批处理实战"
 // section 3.2): the placement of kv_append_kernel, each (token, KV head) row
 // quantised on the way in.  A thread holds one 16-byte piece (8 values) of K

@@ -268,6 +268,28 @@ int32_t pkv_paged_gqa_decode_int8(uint16_t* out, const uint16_t* q, const int8_t
     return hip_status(launch_decode_int8(a, pl, static_cast<hipStream_t>(stream)));
 }
 
+int32_t pkv_paged_gqa_decode_append_int8(uint16_t* out, const uint16_t* q, const uint16_t* k_new,
+                                         const uint16_t* v_new, int8_t* k_codes, int8_t* v_codes, float* k_scales,
+                                         float* v_scales, const int32_t* block_table, int32_t max_blocks_per_seq,
+                                         const int32_t* seq_lens, int32_t max_seq_len, int64_t total_kv_tokens,
+                                         int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+    if (block_size < 32) return PKV_ERR_BAD_SHAPE;  // a 32-key tile lies in one block
+    DecodeArgs a{out, q, nullptr, nullptr, block_table, max_blocks_per_seq, seq_lens, max_seq_len, total_kv_tokens,
+                 num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, workspace,
+                 workspace_bytes, k_new, v_new, nullptr, nullptr, k_codes, v_codes, k_scales, v_scales,
+                 k_codes, v_codes, k_scales, v_scales};
+    DecodePlan pl{};
+    const int32_t st = check_decode(a, pl, k_codes, v_codes, kDecodeInt8TileKeys);
+    if (st != PKV_OK || num_seqs == 0) return st;
+    if (max_seq_len > 0 && (!k_scales || !v_scales)) return PKV_ERR_NULL_POINTER;
+    if (!k_new || !v_new) return PKV_ERR_NULL_POINTER;
+    if (!aligned16(k_scales) || !aligned16(v_scales) || !aligned16(k_new) || !aligned16(v_new))
+        return PKV_ERR_MISALIGNED;
+    return hip_status(launch_decode_int8(a, pl, static_cast<hipStream_t>(stream)));
+}
+
 int32_t pkv_paged_gqa_prefill(uint16_t* out, const uint16_t* q, const int32_t* cu_q_lens, int32_t total_q_tokens,
                               int32_t max_q_len, const uint16_t* k_pool, const uint16_t* v_pool,
                               const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,

@@ -63,6 +63,11 @@ struct DecodeArgs {
     const int8_t* v_codes;
     const float* k_scales;
     const float* v_scales;
+    // decode_append_int8 (with k_new / v_new): the same cache, writable
+    int8_t* k_codes_w;
+    int8_t* v_codes_w;
+    float* k_scales_w;
+    float* v_scales_w;
 };
 
 struct PrefillArgs {

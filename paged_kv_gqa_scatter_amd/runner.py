@@ -14,7 +14,7 @@ import numpy as np
 import torch
 
 from . import (decode_int8_workspace_bytes, decode_workspace_bytes, kv_append, kv_append_int8, paged_gqa_decode,
-               paged_gqa_decode_append, paged_gqa_decode_int8, paged_gqa_prefill)
+               paged_gqa_decode_append, paged_gqa_decode_append_int8, paged_gqa_decode_int8, paged_gqa_prefill)
 from .workloads import INT8_CODE_SENTINEL, NAN_SENTINEL, AppendBatch, Case, DecodeBatch, Deferred, PrefillBatch
 
 
@@ -233,7 +233,13 @@ class Int8DeviceCase(DeviceCase):
                                      workspace=dd.workspace)
 
     def decode_append(self, a: DevAppend, dd: DevDecode, pool: int = 0):
-        raise NotImplementedError("the INT8 cache appends and decodes in two calls")
+        """The step's quantising append and decode in one launch; `a` must add
+        exactly one row per sequence of `dd`, in the same order."""
+        S = dd.q.shape[0]
+        return paged_gqa_decode_append_int8(dd.q, a.k_new.view(S, *a.k_new.shape[1:]),
+                                            a.v_new.view(S, *a.v_new.shape[1:]), *self.pools[pool], dd.block_table,
+                                            dd.seq_lens, float(self.case.scale), max_seq_len=dd.max_seq_len,
+                                            total_kv_tokens=dd.total_kv_tokens, out=dd.out, workspace=dd.workspace)
 
     def prefill(self, pp: DevPrefill, pool: int = 0):
         raise NotImplementedError("the INT8 cache has decode steps only")

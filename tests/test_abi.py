@@ -226,3 +226,20 @@ def test_qkv_project_append_rejects(lib):
     assert f(*qkv_args(q=None)) == 1
     assert f(*qkv_args(x=A16 + 2)) == 3
     assert f(*qkv_args(T=0, x=None)) == 0
+
+
+def test_decode_append_int8_rejects(lib):
+    f = lib.pkv_paged_gqa_decode_append_int8
+    base = dict(out=A16, q=A16, kn=A16, vn=A16, kc=A16, vc=A16, ks=A16, vs=A16, table=A16, mbs=9, lens=A16,
+                maxlen=2049, total=0, S=8, hq=32, hkv=8, d=128, bs=256, nb=50, scale=0.088, ws=A16, wsb=1 << 30,
+                stream=None)
+    keys = ("out", "q", "kn", "vn", "kc", "vc", "ks", "vs", "table", "mbs", "lens", "maxlen", "total", "S", "hq",
+            "hkv", "d", "bs", "nb", "scale", "ws", "wsb", "stream")
+    args = lambda **kw: tuple({**base, **kw}[k] for k in keys)
+    assert f(*args(bs=16, mbs=200)) == 2
+    assert f(*args(hq=30)) == 2
+    assert f(*args(kn=None)) == 1
+    assert f(*args(vs=None)) == 1
+    assert f(*args(vn=A16 + 2)) == 3
+    assert f(*args(ws=None)) == 4
+    assert f(*args(S=0)) == 0

@@ -174,6 +174,64 @@ def test_int8_quantisation_error_within_bound(orc):
     assert (err_gpu <= bound + 1e-2).all()
 
 
+# ---------------------------------------------------------------- decode_append_int8
+
+def _decode_append_int8_check(orc, case, k_new, v_new, q, seq_lens, table, what):
+    """decode_append_int8 on a case's fills (the step's rows not yet
+    appended): the cache (codes and scales, bit for bit) against the oracle's
+    kv_append_int8 of the new rows, the outputs against the oracle's INT8
+    decode."""
+    import paged_kv_gqa_scatter_amd as pkv
+    dc = _dev()(case)
+    dc.run_fills()
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+    bits = lambda x: dev(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
+    S = seq_lens.shape[0]
+    ws = torch.empty(pkv.decode_int8_workspace_bytes(S, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                                                     int(seq_lens.max())), dtype=torch.uint8, device="cuda")
+    out = pkv.paged_gqa_decode_append_int8(bits(q), bits(k_new), bits(v_new), *dc.pools[0],
+                                           dev(table.astype(np.int32)), dev(seq_lens.astype(np.int32)),
+                                           float(case.scale), max_seq_len=int(seq_lens.max()), workspace=ws)
+    torch.cuda.synchronize()
+    _, pools = oracle_int8(case, orc, upto_step=0, decode=False)
+    live = np.nonzero(seq_lens > 0)[0]
+    orc.kv_append_int8(*pools, k_new[live], v_new[live], np.arange(live.size + 1, dtype=np.int32),
+                       (seq_lens[live] - 1).astype(np.int32), np.ascontiguousarray(table[live]))
+    _assert_cache_equal(dc.pools_numpy(), pools, what)
+    ref = orc.decode_int8(q, *pools, table, seq_lens, case.scale)
+    got = out.float().cpu().numpy().astype(np.float64)
+    compare(got, ref, what)
+    return got
+
+
+def test_int8_decode_append_config2(orc):
+    case = W.config2_decode()
+    a, d = case.steps[0].append, case.steps[0].decode
+    _say(f"case {case.name}: decode_append_int8")
+    _decode_append_int8_check(orc, case, a.k_new, a.v_new, d.q, d.seq_lens, d.block_table, "INT8 decode_append 8 seqs")
+
+
+@pytest.mark.parametrize("d,bs,hq,hkv", [(128, 256, 32, 8), (64, 32, 4, 1), (128, 32, 16, 2)])
+def test_int8_decode_append_edge_lengths(orc, d, bs, hq, hkv):
+    # the new row is key 0, the last key of a tile or a block, the first of a
+    # new one, deep in a long many-chunk sequence, or absent (seq_len 0)
+    lens = [1, 31, 32, 33, bs - 1, bs, bs + 1, 2 * bs, 700, 32769, 0]
+    rng = np.random.default_rng(4000 + d + bs)
+    ctx = [max(L - 1, 0) for L in lens]
+    case = W.build_case(f"int8_decode_append_edges_d{d}_b{bs}", rng, hq=hq, hkv=hkv, d=d, bs=bs, ctx_lens=ctx[:-1],
+                        new_lens=[1] * (len(lens) - 1), kinds="d" * (len(lens) - 1))
+    a, dec = case.steps[0].append, case.steps[0].decode
+    pad = W.bf16_normal(rng, (1, hkv, d))
+    k_new = np.concatenate([a.k_new, pad])
+    v_new = np.concatenate([a.v_new, pad])
+    q = np.concatenate([dec.q, W.bf16_normal(rng, (1, hq, d))])
+    seq_lens = np.append(dec.seq_lens, 0).astype(np.int32)
+    table = np.vstack([dec.block_table, np.full((1, dec.block_table.shape[1]), -1, np.int32)])
+    _say(f"case {case.name}: lens {lens}")
+    out = _decode_append_int8_check(orc, case, k_new, v_new, q, seq_lens, table, "INT8 decode_append edge lengths")
+    assert np.array_equal(out[-1], np.zeros_like(out[-1])), "empty sequence must give zeros"
+
+
 # ---------------------------------------------------------------- HIP graphs
 
 def test_int8_graph_replays_match_eager(orc):
