@@ -8,11 +8,13 @@
 //
 //  * Work items, grids and the merge of chunks are those of decode_common.h;
 //    here a tile is 16 keys.
-//  * Every wave streams its own tiles through a private ring of 4 LDS stages:
-//    the K and V rows of a tile (16 rows of one contiguous (block, head) slab,
-//    as B >= 16) are copied by global_load_lds_dwordx4, each wave load moving
-//    1 KB of consecutive bytes, and three tiles are in flight while one is
-//    computed.  The block id is wave-uniform, so the slab address is scalar
+//  * Every wave streams its own tiles through a private ring of LDS stages
+//    (4, or 2 when two workgroups share a CU): the K and V rows of a tile (16
+//    rows of one contiguous (block, head) slab, as B >= 16) are copied by
+//    global_load_lds_dwordx4, each wave load moving 1 KB of consecutive
+//    bytes, and a stage is refilled as soon as its tile's LDS reads have
+//    returned, so every stage is in flight while the wave waits.  The block
+//    id is wave-uniform, so the slab address is scalar
 //    arithmetic and every lane's offset is fixed for the item.  No barrier is
 //    needed inside the loop: a wave only reads what it loaded itself.
 //  * The G query heads of the group are the N side of the matrix cores,
@@ -200,17 +202,17 @@ __device__ __forceinline__ void put_new_row(const WaveItem<D>& w, int t, int kS)
     }
 }
 
-// Tile t from stage kS of a ring of R: wait for it, refill the stage freed
-// by tile t - 1 with tile t + R - 1, then S^T, softmax, O^T.
+// Tile t from stage kS of a ring of R (all R stages in flight): wait for it,
+// S^T, softmax, O^T, then refill its stage with tile t + R.
 template <int D, int R, int kS>
 __device__ __forceinline__ void tile_step(const WaveItem<D>& w, int t, WaveState<D>& ws) {
     constexpr int kDma = TileLanes<D>::kDma;
     static_assert(R == 2 || R == 4, "ring depth");
-    const int after = min(R - 2, w.n_tiles - 1 - t);  // tiles issued after t
-    if (after >= 2) wait_vmcnt<2 * kDma>();
+    const int after = min(R - 1, w.n_tiles - 1 - t);  // tiles issued after t
+    if (after >= 3) wait_vmcnt<3 * kDma>();
+    else if (after == 2) wait_vmcnt<2 * kDma>();
     else if (after == 1) wait_vmcnt<kDma>();
     else wait_vmcnt<0>();
-    if (t + R - 1 < w.n_tiles) issue(w, t + R - 1, (kS + R - 1) % R);
     if (w.append && w.kend == w.L && tile_key(w, t) + kTileKeys >= w.kend) put_new_row<D>(w, t, kS);
 
     // every LDS read of the tile goes out before the first MFMA waits on one
@@ -261,12 +263,17 @@ __device__ __forceinline__ void tile_step(const WaveItem<D>& w, int t, WaveState
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
         ws.acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(vf[db]), as_s16x4(pk), ws.acc[db], 0, 0, 0);
+    // the stage's reads have returned (the MFMAs hold them): refill it with tile t + R
+    if (t + R < w.n_tiles) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+        issue(w, t + R, kS);
+    }
 }
 
 template <int D, int R>
 __device__ __forceinline__ void wave_tiles(const WaveItem<D>& w, WaveState<D>& ws) {
 #pragma unroll
-    for (int t = 0; t < R - 1; ++t)
+    for (int t = 0; t < R; ++t)
         if (t < w.n_tiles) issue(w, t, t);
     for (int t = 0; t < w.n_tiles; t += R) {
         tile_step<D, R, 0>(w, t, ws);
@@ -370,10 +377,10 @@ __device__ __forceinline__ void decode_item(const DecodeKernelArgs& p, DecodeSha
     finish_item<D, G>(p, sh, ws, s, g, nchunks, slot);
 }
 
-// R: LDS ring depth per wave.  R = 4 keeps three tiles in flight per wave
-// (128 KB of stages at D = 128: one workgroup per CU); R = 2 keeps one (64 KB:
-// two workgroups per CU, two waves per SIMD hiding each other's stalls), which
-// pays when there is more work than one pass over the chip.
+// R: LDS ring depth per wave.  R = 4: 128 KB of stages at D = 128, one
+// workgroup per CU; R = 2: 64 KB, two workgroups per CU, two waves per SIMD
+// hiding each other's stalls, which pays when there is more work than one
+// pass over the chip.
 template <int D, int G, int R>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeKernelArgs p, int32_t* prefix_out) {
     __shared__ DecodeShared<D, G> sh;

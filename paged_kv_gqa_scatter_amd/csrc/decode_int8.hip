@@ -12,7 +12,7 @@
 //  * A tile is 32 keys of one block (block_size >= 32): 32 rows of K codes,
 //    32 of V codes and their 2 x 32 scales, 8.25 KB at D = 128 (the bytes of
 //    a 16-key bf16 tile), copied by global_load_lds_dwordx4 into the wave's
-//    4-stage LDS ring as in the bf16 kernel.
+//    LDS ring as in the bf16 kernel.
 //  * Codes become bf16 MFMA operands exactly (|code| <= 127): a signed byte
 //    to fp32 conversion per code and one pack per two.  The scales stay off
 //    the matrix cores: S^T = (K_codes Q^T) times each key's k_scale, and each
@@ -202,18 +202,18 @@ __device__ __forceinline__ u32x4 codes_to_bf16(uint32_t lo, uint32_t hi) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8_8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Tile t from stage kS of a ring of R: wait for it, refill the stage freed by
-// tile t - 1 with tile t + R - 1, then S^T, softmax, O^T.
+// Tile t from stage kS of a ring of R (all R stages in flight): wait for it,
+// S^T, softmax, O^T, then refill its stage with tile t + R.
 template <int D, int R, int kS>
 __device__ __forceinline__ void tile_step8(const Int8WaveItem<D>& w, int t, WaveState<D>& ws) {
     using T = Int8Lanes<D>;
     constexpr int kDma = T::kDma;
     static_assert(R == 2 || R == 4, "ring depth");
-    const int after = min(R - 2, w.n_tiles - 1 - t);  // tiles issued after t
-    if (after >= 2) wait_vmcnt<2 * kDma>();
+    const int after = min(R - 1, w.n_tiles - 1 - t);  // tiles issued after t
+    if (after >= 3) wait_vmcnt<3 * kDma>();
+    else if (after == 2) wait_vmcnt<2 * kDma>();
     else if (after == 1) wait_vmcnt<kDma>();
     else wait_vmcnt<0>();
-    if (t + R - 1 < w.n_tiles) issue8(w, t + R - 1, (kS + R - 1) % R);
     if (w.append && w.kend == w.L && tile_key8(w, t) + kTile8 >= w.kend) put_new_row8<D>(w, t, kS);
 
     // every LDS read of the tile goes out before the first MFMA waits on one
@@ -298,12 +298,17 @@ __device__ __forceinline__ void tile_step8(const Int8WaveItem<D>& w, int t, Wave
     for (int db = 0; db < D / 16; ++db)
         ws.acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_8(codes_to_bf16(vc[db][0], vc[db][1])),
                                                              as_bf16x8_8(pk), ws.acc[db], 0, 0, 0);
+    // the stage's reads have returned (the MFMAs hold them): refill it with tile t + R
+    if (t + R < w.n_tiles) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+        issue8(w, t + R, kS);
+    }
 }
 
 template <int D, int R>
 __device__ __forceinline__ void wave_tiles8(const Int8WaveItem<D>& w, WaveState<D>& ws) {
 #pragma unroll
-    for (int t = 0; t < R - 1; ++t)
+    for (int t = 0; t < R; ++t)
         if (t < w.n_tiles) issue8(w, t, t);
     for (int t = 0; t < w.n_tiles; t += R) {
         tile_step8<D, R, 0>(w, t, ws);
@@ -401,10 +406,10 @@ __device__ __forceinline__ void decode_int8_item(const DecodeKernelArgs& p, Deco
     finish_item<D, G>(p, sh, ws, s, g, nchunks, slot);
 }
 
-// R: LDS ring depth per wave.  R = 4 keeps three tiles in flight per wave
-// (132 KB of stages at D = 128: one workgroup per CU); R = 2 keeps one (66 KB:
-// two workgroups per CU, so two waves share each SIMD and hide each other's
-// stalls: the long-context decode runs about 1.4x faster than with R = 4).
+// R: LDS ring depth per wave.  R = 4: 132 KB of stages at D = 128, one
+// workgroup per CU; R = 2: 66 KB, two workgroups per CU, so two waves share
+// each SIMD and hide each other's stalls (the long-context decode runs about
+// 1.4x faster than with R = 4).
 template <int D, int G, int R>
 __global__ __launch_bounds__(kDecodeThreads) void decode_int8_kernel(DecodeKernelArgs p, int32_t* prefix_out) {
     __shared__ DecodeShared<D, G> sh;
