@@ -257,3 +257,22 @@ def test_int8_graph_replays_match_eager(orc):
         torch.cuda.synchronize()
         assert torch.equal(st["decode"].out.view(torch.int16), want.view(torch.int16))
     _say("  4 replays bit-identical to the eager step")
+
+
+@pytest.mark.timeout(600)
+def test_int8_decode_persistent_grid_2048_sequences(orc):
+    # the largest batch of the persistent grid, over the INT8 cache
+    rng = np.random.default_rng(4096)
+    lens = rng.integers(1, 300, size=2048, endpoint=True)
+    lens[7] = 32768
+    case = W.build_case("int8_decode_2048_seqs", rng, hq=32, hkv=8, d=128, bs=256, ctx_lens=lens - 1,
+                        new_lens=np.ones(2048, np.int64), kinds="d" * 2048)
+    _say(f"case {case.name}: 2048 sequences, one of 32768 keys, INT8 cache")
+    out = _dev()(case).run_all()[0]["decode"]
+    _, pools = oracle_int8(case, orc, decode=False)
+    d = case.steps[0].decode
+    pick = sorted(set(rng.choice(2048, 24, replace=False).tolist()) | {0, 6, 7, 8, 2047})
+    items = np.array([(s, 0, h) for s in pick for h in range(case.num_q_heads)], np.int32)
+    cu = np.arange(2049, dtype=np.int32)
+    ref = orc.attention_rows_int8(items, d.q, cu, *pools, d.block_table, d.seq_lens, case.num_q_heads, case.scale)
+    compare(out[items[:, 0], items[:, 2]], ref, f"INT8 decode {len(pick)} of 2048 sequences x all heads")

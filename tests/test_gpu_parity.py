@@ -449,3 +449,24 @@ def test_block_manager_prefix_sharing_end_to_end(orc):
     ref = orc.decode(q, K, V, table, seq_lens, scale)
     compare(_f64(out), ref, "decode_append over shared prefix blocks")
     bm.close()
+
+
+@pytest.mark.timeout(600)
+def test_decode_persistent_grid_2048_sequences(orc):
+    # the largest batch the persistent grid takes (its chunk prefix in LDS):
+    # 2047 short sequences and one of 32768 keys, so that the direct grid would
+    # be mostly empty; checked on sampled sequences
+    rng = np.random.default_rng(2048)
+    lens = rng.integers(1, 300, size=2048, endpoint=True)
+    lens[1000] = 32768
+    case = W.build_case("decode_2048_seqs", rng, hq=32, hkv=8, d=128, bs=256, ctx_lens=lens - 1,
+                        new_lens=np.ones(2048, np.int64), kinds="d" * 2048)
+    _say(f"case {case.name}: 2048 sequences, one of 32768 keys")
+    out = _dev()(case).run_all()[0]["decode"]
+    K, V = oracle_pools(case, orc)
+    d = case.steps[0].decode
+    pick = sorted(set(rng.choice(2048, 24, replace=False).tolist()) | {0, 999, 1000, 1001, 2047})
+    items = np.array([(s, 0, h) for s in pick for h in range(case.num_q_heads)], np.int32)
+    cu = np.arange(2049, dtype=np.int32)
+    ref = orc.attention_rows(items, d.q, cu, K, V, d.block_table, d.seq_lens, case.num_q_heads, case.scale)
+    compare(out[items[:, 0], items[:, 2]], ref, f"decode {len(pick)} of 2048 sequences x all heads")
