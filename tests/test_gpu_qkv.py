@@ -173,3 +173,15 @@ def test_qkv_wide_tiles_ragged_tails(orc):
     pick = set(rng.choice(T, 40, replace=False).tolist()) | {0, 127, 128, 7999, 8000, 16383, 16384, T - 1}
     _say(f"case qkv wide tiles: T {T}, n_out {(hq + 2 * hkv) * d}, {len(pick)} tokens sampled")
     _compare(orc, x, w, hq, hkv, d, bs, nb, cu, ctx, table, sorted(pick), "wide, ragged tails")
+
+
+@pytest.mark.parametrize("dm", [256, 192])
+def test_qkv_few_tokens(orc, dm):
+    # 13 tokens over 3 sequences (a ragged token tile of the few-token path),
+    # d_model a multiple of 128 or not
+    rng = np.random.default_rng(50 + dm)
+    hq, hkv, d, bs = 4, 2, 64, 32
+    table, cu, ctx, nb = _placement(rng, [31, 0, 64], [2, 10, 1], bs)
+    x, w = _inputs(rng, int(cu[-1]), dm, (hq + 2 * hkv) * d)
+    _say(f"case qkv few tokens: T {int(cu[-1])}, dm {dm}")
+    _compare(orc, x, w, hq, hkv, d, bs, nb, cu, ctx, table, np.arange(int(cu[-1])), "few tokens")
