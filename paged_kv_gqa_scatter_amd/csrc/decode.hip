@@ -295,6 +295,7 @@ struct ItemInputs {
     int ids0, ids1;
     u32x4 qf[D / 32];
     u32x4 kn, vn;  // decode_append: this lane's piece of the new K/V row
+    PackInputs pk;  // sequences sharing the chunk
 };
 
 
@@ -304,12 +305,18 @@ __device__ __forceinline__ ItemInputs<D> load_item_inputs(const DecodeKernelArgs
     const int lane = threadIdx.x & 63, wave = wave_id();
     ItemInputs<D> in;
     in.L_raw = a.seq_lens[s];
-    // Q^T fragment: head lane % 16 (zero past G), dims 32 c' + 8 (lane / 16) + [0, 8)
+    // Q^T fragment: column lane % 16, dims 32 c' + 8 (lane / 16) + [0, 8);
+    // column h is head h of sequence s (zero past G), or, for the first
+    // sequence of a run that may pack, head h % G of sequence s + h / G
+    in.pk = load_pack_inputs<G>(p, s, c);
     const int h = lane & 15, j = lane >> 4;
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    const uint16_t* qp = a.q + ((int64_t)s * a.num_q_heads + g * G + min(h, G - 1)) * D + 8 * j;
+    const bool lead = in.pk.on && s % pack_width<G>() == 0;
+    const int qs = lead ? s + h / G : s;
+    const bool qv = lead ? qs < a.num_seqs : h < G;
+    const uint16_t* qp = a.q + ((int64_t)min(qs, a.num_seqs - 1) * a.num_q_heads + g * G + h % G) * D + 8 * j;
 #pragma unroll
-    for (int cc = 0; cc < D / 32; ++cc) in.qf[cc] = h < G ? load16(qp + 32 * cc) : zero;
+    for (int cc = 0; cc < D / 32; ++cc) in.qf[cc] = qv ? load16(qp + 32 * cc) : zero;
     // block ids of tiles t = lane and lane + 64 (entries past the table row clamp to its end)
     const int32_t* table = a.block_table + (int64_t)s * a.max_blocks_per_seq;
     const int k0 = c * p.chunk;
@@ -357,8 +364,6 @@ __device__ __forceinline__ void decode_item(const DecodeKernelArgs& p, DecodeSha
     w.kn = in.kn;
     w.vn = in.vn;
     w.c = p.qk_scale_log2;
-#pragma unroll
-    for (int cc = 0; cc < D / 32; ++cc) w.qf[cc] = in.qf[cc];
     w.tl = tile_lanes<D>(lane);
     w.st = st;
 
@@ -367,14 +372,28 @@ __device__ __forceinline__ void decode_item(const DecodeKernelArgs& p, DecodeSha
     for (int db = 0; db < D / 16; ++db) ws.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     ws.m = -INFINITY;
     ws.l = 0.f;
-    wait_all_vm();  // the item's inputs (block ids, q) are in
+    wait_all_vm();  // the item's inputs (block ids, q, the pack's lengths and ids) are in
+    // sequences sharing the chunk: a member's item exits (its run's first
+    // item decodes it); the first item keeps the columns of its pack
+    const int lead = s - s % pack_width<G>();
+    const uint32_t pack = pack_of<G>(p, in.pk, c);
     // the next item's inputs go out before this item's tile copies: counted
     // in issue order, they retire with the first tile, so the next item
     // starts without a round trip of its own
     prefetch();
+    if (s != lead && ((pack >> (s - lead)) & 1)) return;
+    const bool packed = s == lead && pack != 0;
+    const int h = lane & 15;
+    const bool keep = h < G || (packed && ((pack >> (h / G)) & 1));
+#pragma unroll
+    for (int cc = 0; cc < D / 32; ++cc) w.qf[cc] = keep ? in.qf[cc] : u32x4{0u, 0u, 0u, 0u};
     wave_tiles<D, R>(w, ws);
 
-    finish_item<D, G>(p, sh, ws, s, g, nchunks, slot);
+    if (packed)
+        finish_pack<D, G>(p, reinterpret_cast<float*>(st.k[0]), reinterpret_cast<float*>(st.v[0]), ws, lead, g, c,
+                          pack);
+    else
+        finish_item<D, G>(p, sh, ws, s, g, nchunks, slot);
 }
 
 // R: LDS ring depth per wave.  R = 4: 128 KB of stages at D = 128, one
@@ -438,6 +457,7 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
                         ? 1
                         : 0;
     pl.max_partials = pl.persistent ? (direct_items < real_items ? direct_items : real_items) : direct_items;
+    pl.pack = pl.items > 2 * slots ? 1 : 0;
     auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
     pl.prefix_offset = 0;
     pl.lse_offset = align(sizeof(int32_t) * (size_t)(num_seqs + 1));
@@ -468,6 +488,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     kp.log2_block = ilog2(a.block_size);
     kp.max_chunks = pl.max_chunks;
     kp.persistent = pl.persistent;
+    kp.pack = pl.pack;
     kp.max_partials = pl.max_partials;
     char* ws = static_cast<char*>(a.workspace);
     int32_t* prefix = reinterpret_cast<int32_t*>(ws + pl.prefix_offset);

@@ -44,6 +44,7 @@ struct DecodeKernelArgs {
     int32_t log2_block;
     int32_t max_chunks;  // chunks of the longest sequence
     int32_t persistent;  // 1: persistent grid over the compact item list
+    int32_t pack;        // 1: sequences sharing a chunk are decoded together
     int64_t max_partials;
     float* lse;         // [max_partials][Hq]
     float* part;        // [max_partials][Hq][D]
@@ -232,6 +233,129 @@ __device__ __forceinline__ void finish_item(const DecodeKernelArgs& p, DecodeSha
 #pragma unroll
         for (int k = 0; k < kElems; ++k) dst[k] = val[k] * inv;
         if (d0 == 0) p.lse[slot * Hq + qh] = mx + log2f(den);
+    }
+    __syncthreads();  // LDS is reused by the next item
+}
+
+// ---- sequences sharing a chunk (a common prefix: aliased blocks)
+//
+// The MFMA tiles have 16 columns and a group fills G of them, so up to
+// P = 16 / G sequences whose chunk c is the same physical K/V (every block of
+// the chunk equal) are decoded by one item, in columns [j G, (j + 1) G) for
+// the pack's j-th sequence: the chunk is read once instead of P times.  The
+// pack of chunk c is fixed per aligned run of P sequences starting at
+// lead = s - s % P: sequence lead + j joins when lead and it both hold keys
+// past the chunk (so neither's new row of a decode_append is in it, and both
+// write partials) and its chunk's block ids equal lead's.  Every item of the
+// run evaluates the same predicate on the same data, so the members' own
+// items know to exit, with no communication.  Only chunks whose P x (blocks
+// per chunk) ids fit one load per lane are considered, and only in launches
+// with more items than two rounds of resident workgroups: below that every
+// item runs at once, a pack does not shorten the step, and its loads and
+// ballots lengthen each item's start.
+
+template <int G>
+constexpr int pack_width() { return 16 / G; }
+
+// What an item loads for the predicate: lane j < P the length of sequence
+// lead + j, lane l < P nb the id of block l % nb of sequence lead + l / nb.
+struct PackInputs {
+    int len;
+    int id;
+    bool on;  // this chunk is considered for packing
+};
+
+template <int G>
+__device__ __forceinline__ PackInputs load_pack_inputs(const DecodeKernelArgs& p, int s, int c) {
+    constexpr int P = pack_width<G>();
+    const DecodeArgs& a = p.a;
+    const int lane = threadIdx.x & 63;
+    const int nb = p.chunk >> p.log2_block;
+    PackInputs pk;
+    pk.on = p.pack && P > 1 && P * nb <= kWave;
+    pk.len = 0;
+    pk.id = -1;
+    if (!pk.on) return pk;
+    const int lead = s - s % P;
+    if (lane < P && lead + lane < a.num_seqs) pk.len = a.seq_lens[lead + lane];
+    const int js = lane / nb, b = (c * p.chunk >> p.log2_block) + lane % nb;
+    if (lane < P * nb && lead + js < a.num_seqs && b < a.max_blocks_per_seq)
+        pk.id = a.block_table[(int64_t)(lead + js) * a.max_blocks_per_seq + b];
+    return pk;
+}
+
+// The pack of chunk c for the run of s (bit j: sequence lead + j; 0 when no
+// sequence joins lead).  Needs pk's loads to have landed.
+template <int G>
+__device__ __forceinline__ uint32_t pack_of(const DecodeKernelArgs& p, const PackInputs& pk, int c) {
+    constexpr int P = pack_width<G>();
+    if (!pk.on) return 0;
+    const int lane = threadIdx.x & 63;
+    const int nb = p.chunk >> p.log2_block;
+    const int cap = p.a.max_blocks_per_seq << p.log2_block;
+    const int after = (c + 1) * p.chunk;  // both need keys past the chunk
+    const uint64_t long_enough = __ballot(lane < P && clamp_len(pk.len, cap) > after);
+    const int lead_id = __shfl(pk.id, lane % nb, kWave);
+    const uint64_t same = __ballot(lane < P * nb && pk.id == lead_id && pk.id >= 0);
+    if (!(long_enough & 1)) return 0;
+    const uint64_t all = nb == 64 ? ~0ull : ((1ull << nb) - 1);
+    uint32_t pack = 0;
+    for (int j = 1; j < P; ++j)
+        if (((long_enough >> j) & 1) && ((same >> (j * nb)) & all) == all) pack |= 1u << j;
+    return pack ? pack | 1u : 0u;
+}
+
+// The end of a packed item: as finish_item, for the 16 columns of the pack's
+// sequences, through LDS that the stages no longer need (o: [waves][16][D]
+// floats in obuf, the waves' maxima and sums in ml); each member writes the
+// normalised partial and log2-sum-exp of chunk c to its own slot.
+template <int D, int G>
+__device__ __forceinline__ void finish_pack(const DecodeKernelArgs& p, float* obuf, float* ml, const WaveState<D>& ws,
+                                            int lead, int g, int c, uint32_t pack) {
+    extern __shared__ int32_t s_prefix[];  // the persistent grid's chunk prefix
+    const DecodeArgs& a = p.a;
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int Hq = a.num_q_heads;
+    float l = ws.l + __shfl_xor(ws.l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    __syncthreads();  // every wave is past its tiles: the stages are free
+    const int h = lane & 15, j = lane >> 4;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+        *reinterpret_cast<f32x4*>(&obuf[(wave * 16 + h) * D + 16 * db + 4 * j]) = ws.acc[db];
+    if (j == 0) {
+        ml[wave * 16 + h] = ws.m;
+        ml[kDecodeWaves * 16 + wave * 16 + h] = l;
+    }
+    __syncthreads();
+    constexpr int kElems = 16 * D / kDecodeThreads;
+    const int e0 = threadIdx.x * kElems, col = e0 / D, d0 = e0 % D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kDecodeWaves; ++v) mx = fmaxf(mx, ml[v * 16 + col]);
+    float den = 0.f, val[kElems];
+#pragma unroll
+    for (int k = 0; k < kElems; ++k) val[k] = 0.f;
+#pragma unroll
+    for (int v = 0; v < kDecodeWaves; ++v) {
+        const float mv = ml[v * 16 + col];
+        const float sc = mv == -INFINITY ? 0.f : fast_exp2(mv - mx);
+        den += ml[kDecodeWaves * 16 + v * 16 + col] * sc;
+#pragma unroll
+        for (int k = 0; k < kElems; ++k) val[k] += obuf[(v * 16 + col) * D + d0 + k] * sc;
+    }
+    const int js = col / G;
+    if ((pack >> js) & 1) {
+        const int seq = lead + js;
+        const int64_t slot = p.persistent ? (int64_t)s_prefix[seq] + c : (int64_t)seq * p.max_chunks + c;
+        const int qh = g * G + col % G;
+        if (slot < p.max_partials) {
+            const float inv = 1.f / den;
+            float* dst = p.part + (slot * Hq + qh) * D + d0;
+#pragma unroll
+            for (int k = 0; k < kElems; ++k) dst[k] = val[k] * inv;
+            if (d0 == 0) p.lse[slot * Hq + qh] = mx + log2f(den);
+        }
     }
     __syncthreads();  // LDS is reused by the next item
 }

@@ -440,6 +440,7 @@ hipError_t launch_decode_int8(const DecodeArgs& a, const DecodePlan& pl, hipStre
     kp.log2_block = ilog2(a.block_size);
     kp.max_chunks = pl.max_chunks;
     kp.persistent = pl.persistent;
+    kp.pack = 0;  // the INT8 kernel decodes every sequence on its own
     kp.max_partials = pl.max_partials;
     char* ws = static_cast<char*>(a.workspace);
     int32_t* prefix = reinterpret_cast<int32_t*>(ws + pl.prefix_offset);

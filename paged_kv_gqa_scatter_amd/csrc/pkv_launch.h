@@ -123,6 +123,7 @@ struct DecodePlan {
     int32_t chunk;            // keys per work item (a multiple of 16 tiles)
     int32_t max_chunks;       // chunks of the longest sequence
     int32_t persistent;       // 1: persistent grid over a compact item list
+    int32_t pack;             // 1: decode sequences sharing a chunk together (bf16)
 
     int64_t items;            // bound on (chunk, KV head) work items
     int64_t max_partials;     // (sequence, split) slots the workspace holds

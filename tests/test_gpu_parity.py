@@ -470,3 +470,58 @@ def test_decode_persistent_grid_2048_sequences(orc):
     cu = np.arange(2049, dtype=np.int32)
     ref = orc.attention_rows(items, d.q, cu, K, V, d.block_table, d.seq_lens, case.num_q_heads, case.scale)
     compare(out[items[:, 0], items[:, 2]], ref, f"decode {len(pick)} of 2048 sequences x all heads")
+
+
+
+def _shared_case(name, seed, hq, hkv, d, bs, S, prefix, private, long_seq=None):
+    # S sequences of prefix + U[0, 600) cached keys sharing the prefix's
+    # blocks, except `private` ones (U[1, 2800) keys of their own); an
+    # optional last private sequence of `long_seq` keys
+    rng = np.random.default_rng(seed)
+    ctx = prefix + rng.integers(0, 600, S)
+    for s in private:
+        ctx[s] = rng.integers(1, 2800)
+    if long_seq:
+        ctx[S - 1] = long_seq
+    shared = [s for s in range(S) if s not in private and not (long_seq and s == S - 1)]
+    return W.build_case(name, rng, hq=hq, hkv=hkv, d=d, bs=bs, ctx_lens=ctx, new_lens=np.ones(S, np.int64),
+                        kinds="d" * S, shared_prefix=prefix, shared_seqs=shared)
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs,S,prefix,private,long_seq,cut", [
+    # G 4 (packs of 4): a full pack, packs missing a member (5; 17, 18), a run
+    # whose first sequence is private (20); a direct grid
+    (32, 8, 128, 256, 64, 2048, (5, 17, 18, 20), None, {1: 1024, 2: 1500, 8: 1024, 13: 2048, 14: 1}),
+    # G 8 (packs of 2) over blocks of 32 with one long private sequence: the
+    # persistent grid
+    (64, 8, 128, 32, 65, 1024, (7,), 8191, {1: 1024, 2: 1000, 9: 32}),
+    # G 1 (packs of 16) at D 64
+    (8, 8, 64, 256, 64, 1024, (33,), None, {3: 512, 16: 512, 20: 1024, 34: 700}),
+])
+def test_decode_shared_prefix_packs(orc, hq, hkv, d, bs, S, prefix, private, long_seq, cut):
+    # launches with many work items decode sequences whose chunk is the same
+    # physical K/V in one item's spare MFMA columns; the outputs must be those
+    # of separate decodes.  First the decode step, then a decode (no append)
+    # over the same cache with some shared sequences cut to lengths at block
+    # and 512-key boundaries inside the prefix (a member or a run's first
+    # sequence then holds no keys past a shared chunk) or inside it
+    import paged_kv_gqa_scatter_amd as pkv
+    case = _shared_case(f"shared_prefix_g{hq // hkv}_d{d}_b{bs}", 7000 + hq + bs, hq, hkv, d, bs, S, prefix,
+                        private, long_seq)
+    _say(f"case {case.name}: {S} seqs, prefix {prefix}, private {private}, long {long_seq}, cut {cut}")
+    dc = _dev()(case)
+    out = dc.run_all()[0]["decode"]
+    ref, _ = oracle_outputs(case, orc)
+    compare(out, ref[0]["decode"], "decode step with shared chunks")
+    dd = dc.steps[0]["decode"]
+    lens = case.steps[0].decode.seq_lens.copy()
+    for s, n in cut.items():
+        lens[s] = n
+    # the step's length bound and token count: the same split plan
+    got = pkv.paged_gqa_decode(dd.q, dc.k_pool, dc.v_pool, dd.block_table, torch.from_numpy(lens).cuda(),
+                               float(case.scale), max_seq_len=dd.max_seq_len, total_kv_tokens=dd.total_kv_tokens,
+                               workspace=dd.workspace)
+    torch.cuda.synchronize()
+    K, V = oracle_pools(case, orc)
+    d_ = case.steps[0].decode
+    compare(_f64(got), orc.decode(d_.q, K, V, d_.block_table, lens, case.scale), "decode, cut lengths")
