@@ -433,6 +433,10 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
     // (wgs_per_cu on each of a 256-CU part's CUs) times the round's length, a
     // load round trip (about 12 tiles) plus the tiles each wave streams.  The
     // item count is a bound (each sequence adds at most one partial chunk).
+    // Finer steps (any multiple of one tile per wave) measured slower: a
+    // chunk that is not a whole number of blocks turns shared-chunk packing
+    // off, and one that leaves the direct grid (chunks x sequences x KV heads)
+    // larger than the resident workgroups delays real items behind empty ones.
     const int64_t slots = (int64_t)kPlanCus * wgs_per_cu;
     const int max_chunk = kMaxTilesPerWave * tile_keys * kDecodeWaves;
     int chunk = kDecodeWaves * 4 * tile_keys;

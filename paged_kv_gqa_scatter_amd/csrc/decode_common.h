@@ -119,40 +119,90 @@ struct WaveState {
 };
 
 // Merge kernel: one workgroup per (sequence, KV head) merges that sequence's
-// chunk partials into the bf16 output, one pass with a running maximum so all
-// loads are independent.  Sequences with fewer than two chunks were finished
-// by the split kernel.
+// chunk partials into the bf16 output with a running maximum.  Sequences with
+// fewer than two chunks were finished by the split kernel.  The partials are
+// loaded kMergeBatch at a time, all of a batch's loads in flight together; in
+// the direct grid a sequence's slots start at s * max_chunks whatever its
+// length, so the first batch goes out with the length itself and a short
+// sequence merges after a single memory round trip.  Slots past the
+// sequence's chunk count are loaded (they lie inside the workspace) but never
+// used: they may hold anything from earlier launches.
 template <int D, int G>
 constexpr int elems_per_thread() { return (G * D + kDecodeThreads - 1) / kDecodeThreads; }
+
+constexpr int kMergeBatch = 8;
+
+// One batch of the merge: the lse and output slice of partials
+// [base + i0, base + i0 + lim) (lim >= 1), loaded unconditionally (entries past
+// lim repeat the batch's last slot) so the batch issues back to back.
+template <int D, int kElems>
+__device__ __forceinline__ void merge_load(const DecodeKernelArgs& p, int64_t base, int i0, int lim, int qh, int d0,
+                                           float (&lb)[kMergeBatch], float (&vb)[kMergeBatch][kElems]) {
+    const int Hq = p.a.num_q_heads;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+        const int64_t slot = base + i0 + min(i, lim - 1);
+        lb[i] = p.lse[slot * Hq + qh];
+        const float* src = p.part + (slot * Hq + qh) * D + d0;
+#pragma unroll
+        for (int k = 0; k < kElems; ++k) vb[i][k] = src[k];
+    }
+}
+
+// Folds the batch's partials below n into the running (max, sum, numerator).
+template <int kElems>
+__device__ __forceinline__ void merge_fold(int i0, int n, const float (&lb)[kMergeBatch],
+                                           const float (&vb)[kMergeBatch][kElems], float& mx, float& den,
+                                           float (&num)[kElems]) {
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+        if (i0 + i < n) {
+            const float m_new = fmaxf(mx, lb[i]);
+            const float a_old = fast_exp2(mx - m_new);  // 0 on the first partial
+            const float w = fast_exp2(lb[i] - m_new);
+            den = den * a_old + w;
+#pragma unroll
+            for (int k = 0; k < kElems; ++k) num[k] = num[k] * a_old + w * vb[i][k];
+            mx = m_new;
+        }
+    }
+}
 
 template <int D, int G>
 __global__ __launch_bounds__(kDecodeThreads) void decode_merge_kernel(DecodeKernelArgs p, const int32_t* prefix) {
     constexpr int kElems = elems_per_thread<D, G>();  // outputs per thread
     const int Hkv = p.a.num_kv_heads, Hq = p.a.num_q_heads;
     const int g = blockIdx.x % Hkv, s = blockIdx.x / Hkv;
-    const int cap = p.a.max_blocks_per_seq << p.log2_block;
-    const int n = num_chunks(clamp_len(p.a.seq_lens[s], cap), p.chunk);
-    if (n < 2) return;
-    const int64_t base = p.persistent ? (int64_t)prefix[s] : (int64_t)s * p.max_chunks;
-    if (base + n > p.max_partials) return;  // precondition broken: no partials to merge
     const int e0 = threadIdx.x * kElems;
     if (e0 >= G * D) return;
     const int h = e0 / D, d0 = e0 % D;
     const int qh = g * G + h;
+    const int cap = p.a.max_blocks_per_seq << p.log2_block;
+    // the length (and the persistent grid's first slot) as vector loads
+    // issued first: waiting for them leaves a batch issued after them in flight
+    int si = s;
+    asm volatile("" : "+v"(si));
+    const int len = p.a.seq_lens[si];
+    const int pre = p.persistent ? prefix[si] : 0;
+    // in the direct grid the first batch is bounded by the host's chunk count
+    // of the longest sequence (this sequence's slots whatever its length), so
+    // it goes out with the length
+    float lb[kMergeBatch], vb[kMergeBatch][kElems];
+    if (!p.persistent)
+        merge_load<D, kElems>(p, (int64_t)s * p.max_chunks, 0, min(p.max_chunks, kMergeBatch), qh, d0, lb, vb);
+    const int n = __builtin_amdgcn_readfirstlane(num_chunks(clamp_len(len, cap), p.chunk));
+    const int64_t base = p.persistent ? (int64_t)__builtin_amdgcn_readfirstlane(pre) : (int64_t)s * p.max_chunks;
+    // slots [base, base + n) must lie in the workspace (else: nothing to merge)
+    const bool fits = base + n <= p.max_partials;
+    if (p.persistent && fits && n > 0) merge_load<D, kElems>(p, base, 0, min(n, kMergeBatch), qh, d0, lb, vb);
+    if (n < 2 || !fits) return;
     float mx = -INFINITY, den = 0.f, num[kElems];
 #pragma unroll
     for (int k = 0; k < kElems; ++k) num[k] = 0.f;
-#pragma unroll 8
-    for (int i = 0; i < n; ++i) {
-        const float li = p.lse[(base + i) * Hq + qh];
-        const float* src = p.part + ((base + i) * Hq + qh) * D + d0;
-        const float m_new = fmaxf(mx, li);
-        const float a_old = fast_exp2(mx - m_new);  // 0 on the first partial
-        const float w = fast_exp2(li - m_new);
-        den = den * a_old + w;
-#pragma unroll
-        for (int k = 0; k < kElems; ++k) num[k] = num[k] * a_old + w * src[k];
-        mx = m_new;
+    merge_fold<kElems>(0, n, lb, vb, mx, den, num);
+    for (int i0 = kMergeBatch; i0 < n; i0 += kMergeBatch) {
+        merge_load<D, kElems>(p, base, i0, min(n - i0, kMergeBatch), qh, d0, lb, vb);
+        merge_fold<kElems>(i0, n, lb, vb, mx, den, num);
     }
     const float inv = 1.f / den;
     uint16_t* dst = p.a.out + ((int64_t)s * Hq + qh) * D + d0;
