@@ -315,6 +315,43 @@ def time_prefill_workload(args):
     return case, flops, ms
 
 
+def device_context():
+    """The device and a practical HBM ceiling: a 1 GiB device-to-device copy
+    (read + write bytes over its median time, 10 timed copies), and the
+    engine clock the driver reports as current when there is one GPU to
+    read it from."""
+    import glob
+    import torch
+    n = 1 << 29  # int16 elements: 1 GiB
+    src = torch.empty(n, dtype=torch.int16, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    s = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for a, b in evs:
+        a.record(s)
+        dst.copy_(src)
+        b.record(s)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)[len(evs) // 2]
+    del src, dst
+    props = torch.cuda.get_device_properties(0)
+    ctx = {"name": props.name, "compute_units": props.multi_processor_count,
+           "copy_GBps": round(2 * 2 * n / (ms * 1e-3) / 1e9, 1),
+           "copy_note": "1 GiB device-to-device copy, read + write bytes: a practical ceiling for HBM-bound kernels"}
+    clocks = []
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(f) as fh:
+                cur = [ln for ln in fh.read().split("\n") if ln.strip().endswith("*")]
+            clocks += [c.split(":", 1)[1].strip(" *") for c in cur]
+        except OSError:
+            pass
+    ctx["sclk_current"] = clocks[0] if len(clocks) == 1 else None
+    return ctx
+
+
 def time_long_decode(args):
     """Decode at a bandwidth-bound scale: 256 sequences sharing a 4096-token
     prefix (aliased blocks) plus 0..2048 private tokens, and 16 sequences of
@@ -583,6 +620,7 @@ def main():
         line["int8_kv_cache"] = time_int8(args, step_ms, line.get("long_context_decode", {}).get("ms"))
     if not args.no_mixed:
         line["mixed_step"] = time_mixed_step(args)
+    line["device"] = device_context()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, dec, kv_bytes, args.cpu_seconds)
     print(json.dumps(line), flush=True)
