@@ -106,7 +106,8 @@ int32_t pkv_kv_append(uint16_t* k_pool, uint16_t* v_pool,
 /*
  * Bytes of device workspace pkv_paged_gqa_decode needs.  total_kv_tokens is a
  * host-side upper bound on the sum of seq_lens (<= 0: num_seqs * max_seq_len
- * is assumed).  Returns 0 for unsupported shapes.
+ * is assumed).  Returns 0 for unsupported shapes.  The workspace must be
+ * zero-filled once, before the first decode call that uses it.
  */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t max_seq_len, int64_t total_kv_tokens);
@@ -127,13 +128,17 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *   scale            softmax scale (usually 1/sqrt(head_dim))
  *   workspace        device scratch of workspace_bytes >=
  *                    pkv_decode_workspace_bytes(...) with the same shapes and
- *                    total_kv_tokens; it needs no initialisation, and calls
- *                    that share it must be ordered (same stream or
- *                    synchronised)
+ *                    total_kv_tokens, zero-filled before its first use (its
+ *                    first 16 KiB hold per-(sequence, KV head) chunk counters,
+ *                    which every completed call leaves at zero, whatever the
+ *                    shapes); calls that share it must be ordered (same stream
+ *                    or synchronised)
  *
  * Long sequences are split into chunks of keys whose partial results are
- * merged with a log-sum-exp combine.  A sequence with seq_len 0 yields zeros.
- * Supports num_seqs <= 8192.
+ * merged with a log-sum-exp combine: by the last of a sequence's chunks to
+ * finish (counted in the workspace) when the launch is small, else by a
+ * second kernel.  A sequence with seq_len 0 yields zeros.  Supports
+ * num_seqs <= 8192.
  */
 int32_t pkv_paged_gqa_decode(uint16_t* out, const uint16_t* q,
                              const uint16_t* k_pool, const uint16_t* v_pool,

@@ -50,7 +50,9 @@ int32_t pkv_kv_append_int8(int8_t* k_codes, int8_t* v_codes, float* k_scales, fl
 
 /*
  * Bytes of device workspace pkv_paged_gqa_decode_int8 needs (its split plan
- * differs from the bf16 decode's).  Returns 0 for unsupported shapes.
+ * differs from the bf16 decode's).  Returns 0 for unsupported shapes.  As for
+ * the bf16 decode, the workspace is zero-filled before its first use, and one
+ * workspace may serve both formats.
  */
 size_t pkv_decode_int8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t max_seq_len, int64_t total_kv_tokens);

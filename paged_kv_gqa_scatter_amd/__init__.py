@@ -175,7 +175,8 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, h
 def paged_gqa_decode(q, k_pool, v_pool, block_table, seq_lens, scale: float, *, max_seq_len: int,
                      total_kv_tokens: int = 0, out=None, workspace=None):
     """One query row per sequence: ``q [S][Hq][D]`` -> ``out [S][Hq][D]`` bf16.
-    ``workspace`` (uint8 CUDA tensor) is allocated if not given."""
+    ``workspace`` (uint8 CUDA tensor, zero-filled before its first use; every
+    call leaves its counters at zero) is allocated zero-filled if not given."""
     NB, Hkv, B, D = _pool_shape(k_pool, v_pool)
     _bf16(q, "q", 3)
     S, Hq, Dq = q.shape
@@ -192,7 +193,7 @@ def paged_gqa_decode(q, k_pool, v_pool, block_table, seq_lens, scale: float, *, 
         raise ValueError("out must be [S][Hq][D]")
     need = decode_workspace_bytes(S, Hq, Hkv, D, max_seq_len, total_kv_tokens) if S > 0 else 0
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
     if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
     st = lib().pkv_paged_gqa_decode(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
@@ -228,7 +229,7 @@ def paged_gqa_decode_append(q, k_new, v_new, k_pool, v_pool, block_table, seq_le
         raise ValueError("out must be [S][Hq][D]")
     need = decode_workspace_bytes(S, Hq, Hkv, D, max_seq_len, total_kv_tokens) if S > 0 else 0
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
     if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
     st = lib().pkv_paged_gqa_decode_append(out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
@@ -319,7 +320,7 @@ def paged_gqa_decode_int8(q, k_codes, v_codes, k_scales, v_scales, block_table, 
         raise ValueError("out must be [S][Hq][D]")
     need = decode_int8_workspace_bytes(S, Hq, Hkv, D, max_seq_len, total_kv_tokens) if S > 0 else 0
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
     if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
     st = lib().pkv_paged_gqa_decode_int8(out.data_ptr(), q.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(),
@@ -387,7 +388,7 @@ def paged_gqa_decode_append_int8(q, k_new, v_new, k_codes, v_codes, k_scales, v_
         raise ValueError("out must be [S][Hq][D]")
     need = decode_int8_workspace_bytes(S, Hq, Hkv, D, max_seq_len, total_kv_tokens) if S > 0 else 0
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
     if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
     st = lib().pkv_paged_gqa_decode_append_int8(out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),

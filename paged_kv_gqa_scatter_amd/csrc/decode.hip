@@ -462,9 +462,13 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
                         : 0;
     pl.max_partials = pl.persistent ? (direct_items < real_items ? direct_items : real_items) : direct_items;
     pl.pack = pl.items > 2 * slots ? 1 : 0;
+    pl.fused = can_fuse_merge(pl, num_seqs, num_kv_heads);
     auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    pl.prefix_offset = 0;
-    pl.lse_offset = align(sizeof(int32_t) * (size_t)(num_seqs + 1));
+    // the counters sit in a fixed region that no plan writes anything else
+    // into, so a launch of any shape finds them as the last one left them
+    pl.counter_offset = 0;
+    pl.prefix_offset = kCounterBytes;
+    pl.lse_offset = align(pl.prefix_offset + sizeof(int32_t) * (size_t)(num_seqs + 1));
     pl.o_offset = align(pl.lse_offset + sizeof(float) * (size_t)pl.max_partials * num_q_heads);
     pl.bytes = pl.o_offset + sizeof(float) * (size_t)pl.max_partials * num_q_heads * head_dim;
     return pl;
@@ -495,6 +499,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     kp.pack = pl.pack;
     kp.max_partials = pl.max_partials;
     char* ws = static_cast<char*>(a.workspace);
+    kp.counters = pl.fused ? reinterpret_cast<int32_t*>(ws + pl.counter_offset) : nullptr;
     int32_t* prefix = reinterpret_cast<int32_t*>(ws + pl.prefix_offset);
     kp.lse = reinterpret_cast<float*>(ws + pl.lse_offset);
     kp.part = reinterpret_cast<float*>(ws + pl.o_offset);

@@ -45,6 +45,8 @@ struct DecodeKernelArgs {
     int32_t max_chunks;  // chunks of the longest sequence
     int32_t persistent;  // 1: persistent grid over the compact item list
     int32_t pack;        // 1: sequences sharing a chunk are decoded together
+    int32_t* counters;   // direct grid: chunks finished per (sequence, KV head),
+                         // the last one merges; null: the merge kernel does
     int64_t max_partials;
     float* lse;         // [max_partials][Hq]
     float* part;        // [max_partials][Hq][D]
@@ -135,17 +137,33 @@ constexpr int kMergeBatch = 8;
 // One batch of the merge: the lse and output slice of partials
 // [base + i0, base + i0 + lim) (lim >= 1), loaded unconditionally (entries past
 // lim repeat the batch's last slot) so the batch issues back to back.
-template <int D, int kElems>
+// Agent-scope (relaxed) accesses of partials: coherent across the XCDs'
+// separate L2 caches (stores write through, loads fetch past the L2), for
+// partials merged inside the split kernel by a workgroup on any XCD.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D, int kElems, bool kAgent = false>
 __device__ __forceinline__ void merge_load(const DecodeKernelArgs& p, int64_t base, int i0, int lim, int qh, int d0,
                                            float (&lb)[kMergeBatch], float (&vb)[kMergeBatch][kElems]) {
     const int Hq = p.a.num_q_heads;
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
         const int64_t slot = base + i0 + min(i, lim - 1);
-        lb[i] = p.lse[slot * Hq + qh];
         const float* src = p.part + (slot * Hq + qh) * D + d0;
+        if constexpr (kAgent) {
+            lb[i] = load_agent(p.lse + slot * Hq + qh);
 #pragma unroll
-        for (int k = 0; k < kElems; ++k) vb[i][k] = src[k];
+            for (int k = 0; k < kElems; ++k) vb[i][k] = load_agent(src + k);
+        } else {
+            lb[i] = p.lse[slot * Hq + qh];
+#pragma unroll
+            for (int k = 0; k < kElems; ++k) vb[i][k] = src[k];
+        }
     }
 }
 
@@ -224,12 +242,14 @@ struct __attribute__((aligned(16))) DecodeShared {
     float m[kDecodeWaves][G];
     float l[kDecodeWaves][G];
     int32_t wave_sum[kDecodeWaves];
+    int32_t ticket;  // the item's place among its sequence's finished chunks
 };
 
 // The end of a work item: the waves' states (ws: O^T fragments, lane (j, h)
 // holding dims 16 db + 4 j + i of head h) are merged through LDS, and the
 // item's result goes out, directly (a sequence with one chunk) or as a
-// normalised partial with its log2-sum-exp for the merge kernel.
+// normalised partial with its log2-sum-exp, merged by the sequence's last
+// chunk (direct grid) or by the merge kernel.
 template <int D, int G>
 __device__ __forceinline__ void finish_item(const DecodeKernelArgs& p, DecodeShared<D, G>& sh, const WaveState<D>& ws,
                                             int s, int g, int nchunks, int64_t slot) {
@@ -278,11 +298,53 @@ __device__ __forceinline__ void finish_item(const DecodeKernelArgs& p, DecodeSha
         __syncthreads();  // LDS is reused by the next item
         return;
     }
-    if (active && slot < p.max_partials) {
+    if (!p.counters) {  // partials for the merge kernel
+        if (active && slot < p.max_partials) {
+            float* dst = p.part + (slot * Hq + qh) * D + d0;
+#pragma unroll
+            for (int k = 0; k < kElems; ++k) dst[k] = val[k] * inv;
+            if (d0 == 0) p.lse[slot * Hq + qh] = mx + log2f(den);
+        }
+        __syncthreads();  // LDS is reused by the next item
+        return;
+    }
+    // direct grid, no merge kernel: the partial goes out with agent-scope
+    // stores, which complete (vmcnt) only once visible at the device's point
+    // of coherence; after every thread's have, the chunk is counted in with an
+    // agent-scope atomic, and the sequence's last chunk to arrive reads all
+    // partials (slots s * max_chunks + c, c < n) with agent-scope loads issued
+    // after the count returned, merges them and puts the counter back to zero.
+    // Every value handed between workgroups is an agent-scope access, so no
+    // L2 write-back or invalidate (the release / acquire fences) is needed.
+    const int n = min(nchunks, p.max_chunks);  // chunks the grid holds
+    if (active) {
         float* dst = p.part + (slot * Hq + qh) * D + d0;
 #pragma unroll
-        for (int k = 0; k < kElems; ++k) dst[k] = val[k] * inv;
-        if (d0 == 0) p.lse[slot * Hq + qh] = mx + log2f(den);
+        for (int k = 0; k < kElems; ++k) store_agent(dst + k, val[k] * inv);
+        if (d0 == 0) store_agent(p.lse + slot * Hq + qh, mx + log2f(den));
+    }
+    wait_all_vm();
+    __syncthreads();
+    int32_t* cnt = p.counters + (int64_t)s * a.num_kv_heads + g;
+    if (threadIdx.x == 0) sh.ticket = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (sh.ticket == n - 1) {
+        if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (active) {
+            const int64_t base = (int64_t)s * p.max_chunks;
+            float lb[kMergeBatch], vb[kMergeBatch][kElems];
+            float m2 = -INFINITY, den2 = 0.f, num[kElems];
+#pragma unroll
+            for (int k = 0; k < kElems; ++k) num[k] = 0.f;
+            for (int i0 = 0; i0 < n; i0 += kMergeBatch) {
+                merge_load<D, kElems, true>(p, base, i0, min(n - i0, kMergeBatch), qh, d0, lb, vb);
+                merge_fold<kElems>(i0, n, lb, vb, m2, den2, num);
+            }
+            const float inv2 = 1.f / den2;
+            uint16_t* dst = a.out + ((int64_t)s * Hq + qh) * D + d0;
+#pragma unroll
+            for (int k = 0; k < kElems; ++k) dst[k] = __builtin_bit_cast(uint16_t, (__bf16)(num[k] * inv2));
+        }
     }
     __syncthreads();  // LDS is reused by the next item
 }
@@ -515,7 +577,8 @@ hipError_t launch_split(SplitKernel kernel, const DecodeKernelArgs& kp, int32_t*
         hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kDecodeThreads), lds, stream, kp, prefix);
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || kp.max_chunks < 2) return e;  // no sequence has two chunks: nothing to merge
+    // no sequence has two chunks, or the split kernel merges: no merge kernel
+    if (e != hipSuccess || kp.max_chunks < 2 || kp.counters) return e;
     hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3((unsigned)(a.num_seqs * a.num_kv_heads)),
                        dim3(kDecodeThreads), 0, stream, kp, (const int32_t*)prefix);
     return hipGetLastError();

@@ -443,6 +443,7 @@ hipError_t launch_decode_int8(const DecodeArgs& a, const DecodePlan& pl, hipStre
     kp.pack = 0;  // the INT8 kernel decodes every sequence on its own
     kp.max_partials = pl.max_partials;
     char* ws = static_cast<char*>(a.workspace);
+    kp.counters = pl.fused ? reinterpret_cast<int32_t*>(ws + pl.counter_offset) : nullptr;
     int32_t* prefix = reinterpret_cast<int32_t*>(ws + pl.prefix_offset);
     kp.lse = reinterpret_cast<float*>(ws + pl.lse_offset);
     kp.part = reinterpret_cast<float*>(ws + pl.o_offset);
@@ -475,6 +476,8 @@ DecodePlan plan_decode_int8(int32_t num_seqs, int32_t num_q_heads, int32_t num_k
     DecodePlan pl = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, total_kv_tokens,
                                 kTile8, wgs);
     pl.ring = ring;
+    pl.pack = 0;
+    pl.fused = can_fuse_merge(pl, num_seqs, num_kv_heads);
     return pl;
 }
 

@@ -124,14 +124,26 @@ struct DecodePlan {
     int32_t max_chunks;       // chunks of the longest sequence
     int32_t persistent;       // 1: persistent grid over a compact item list
     int32_t pack;             // 1: decode sequences sharing a chunk together (bf16)
-
+    int32_t fused;            // 1: the split kernel merges (counters), no merge kernel
     int64_t items;            // bound on (chunk, KV head) work items
     int64_t max_partials;     // (sequence, split) slots the workspace holds
+    size_t counter_offset;    // int32 [num_seqs][num_kv_heads] chunk counters (fused merge)
     size_t prefix_offset;     // int32 [num_seqs + 1] chunk prefix (persistent grid)
     size_t lse_offset;        // float [max_partials][num_q_heads]
     size_t o_offset;          // float [max_partials][num_q_heads][head_dim]
     size_t bytes;
 };
+
+// The split kernel merges a sequence's partials itself (the last of its
+// chunks to finish, counted per (sequence, KV head)) when the grid is direct,
+// no sequences are packed and the counters fit the fixed region at the start
+// of every decode workspace; otherwise a merge kernel follows it.
+constexpr int64_t kMaxFusedPairs = 4096;
+constexpr size_t kCounterBytes = sizeof(int32_t) * kMaxFusedPairs;
+inline int32_t can_fuse_merge(const DecodePlan& pl, int32_t num_seqs, int32_t num_kv_heads) {
+    return !pl.persistent && !pl.pack && pl.max_chunks >= 2 && (int64_t)num_seqs * num_kv_heads <= kMaxFusedPairs;
+}
+
 // plan_decode: the split of a kernel whose tiles hold tile_keys keys and of
 // which wgs_per_cu workgroups are resident on one CU; the plan of each cache
 // format (which also picks its ring depth) comes from plan_decode_bf16 /

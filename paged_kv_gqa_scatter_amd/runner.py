@@ -112,7 +112,7 @@ class DeviceCase:
         ws = decode_workspace_bytes(S, c.num_q_heads, c.num_kv_heads, c.head_dim, max_len, total) if S else 16
         return DevDecode(_bits(b.q, d), _i32(b.seq_lens, d), _i32(b.block_table, d), max_len, total,
                          torch.empty((S, c.num_q_heads, c.head_dim), dtype=torch.bfloat16, device=d),
-                         torch.empty(max(ws, 16), dtype=torch.uint8, device=d))
+                         torch.zeros(max(ws, 16), dtype=torch.uint8, device=d))
 
     def _prefill(self, b: PrefillBatch) -> DevPrefill:
         d = self.device
@@ -221,7 +221,7 @@ class Int8DeviceCase(DeviceCase):
         S = b.seq_lens.shape[0]
         ws = decode_int8_workspace_bytes(S, c.num_q_heads, c.num_kv_heads, c.head_dim, dd.max_seq_len,
                                          dd.total_kv_tokens) if S else 16
-        dd.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=self.device)
+        dd.workspace = torch.zeros(max(ws, 16), dtype=torch.uint8, device=self.device)
         return dd
 
     def append(self, a: DevAppend, pool: int = 0):

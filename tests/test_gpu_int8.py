@@ -187,7 +187,7 @@ def _decode_append_int8_check(orc, case, k_new, v_new, q, seq_lens, table, what)
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
     bits = lambda x: dev(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
     S = seq_lens.shape[0]
-    ws = torch.empty(pkv.decode_int8_workspace_bytes(S, case.num_q_heads, case.num_kv_heads, case.head_dim,
+    ws = torch.zeros(pkv.decode_int8_workspace_bytes(S, case.num_q_heads, case.num_kv_heads, case.head_dim,
                                                      int(seq_lens.max())), dtype=torch.uint8, device="cuda")
     out = pkv.paged_gqa_decode_append_int8(bits(q), bits(k_new), bits(v_new), *dc.pools[0],
                                            dev(table.astype(np.int32)), dev(seq_lens.astype(np.int32)),

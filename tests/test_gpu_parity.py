@@ -321,7 +321,7 @@ def _decode_append_check(orc, case, k_new, v_new, q, seq_lens, table, what):
     dev = lambda a, dt=torch.int32: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
     bits = lambda a: dev(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
     S = seq_lens.shape[0]
-    ws = torch.empty(pkv.decode_workspace_bytes(S, case.num_q_heads, case.num_kv_heads, case.head_dim,
+    ws = torch.zeros(pkv.decode_workspace_bytes(S, case.num_q_heads, case.num_kv_heads, case.head_dim,
                                                 int(seq_lens.max())), dtype=torch.uint8, device="cuda")
     out = pkv.paged_gqa_decode_append(bits(q), bits(k_new), bits(v_new), dc.k_pool, dc.v_pool,
                                       dev(table.astype(np.int32)), dev(seq_lens.astype(np.int32)),
@@ -437,7 +437,7 @@ def test_block_manager_prefix_sharing_end_to_end(orc):
     seq_lens = np.array(lens, np.int32)
     kn, vn = W.bf16_normal(rng, (4, Hkv, D)), W.bf16_normal(rng, (4, Hkv, D))
     q = W.bf16_normal(rng, (4, Hq, D))
-    ws = torch.empty(pkv.decode_workspace_bytes(4, Hq, Hkv, D, int(seq_lens.max())), dtype=torch.uint8,
+    ws = torch.zeros(pkv.decode_workspace_bytes(4, Hq, Hkv, D, int(seq_lens.max())), dtype=torch.uint8,
                      device="cuda")
     out = pkv.paged_gqa_decode_append(bits(q), bits(kn), bits(vn), kp, vp, dev(table), dev(seq_lens), scale,
                                       max_seq_len=int(seq_lens.max()), workspace=ws)
