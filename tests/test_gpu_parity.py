@@ -525,3 +525,45 @@ def test_decode_shared_prefix_packs(orc, hq, hkv, d, bs, S, prefix, private, lon
     K, V = oracle_pools(case, orc)
     d_ = case.steps[0].decode
     compare(_f64(got), orc.decode(d_.q, K, V, d_.block_table, lens, case.scale), "decode, cut lengths")
+
+
+def test_decode_workspace_shared_across_shapes_and_formats():
+    # one zero-filled workspace serving, in turn, a decode whose split kernel
+    # merges (config 2), a persistent-grid decode of another shape, an INT8
+    # decode that merges in its split kernel, and config 2 again: the chunk
+    # counters (the first 16 KiB) are zero after every call, and the repeated
+    # call gives the first one's outputs bit for bit
+    import paged_kv_gqa_scatter_amd as pkv
+    from paged_kv_gqa_scatter_amd.runner import Int8DeviceCase
+    c2 = W.config2_decode()
+    rng = np.random.default_rng(4096)
+    lens = rng.integers(1, 300, size=300, endpoint=True)
+    lens[7] = 20000
+    cp = W.build_case("decode_300_seqs_one_long", rng, hq=32, hkv=8, d=128, bs=256, ctx_lens=lens - 1,
+                      new_lens=np.ones(300, np.int64), kinds="d" * 300)
+    d2, dp, d8 = _dev()(c2), _dev()(cp), Int8DeviceCase(c2)
+    for dc in (d2, dp, d8):
+        dc.run_fills()
+        dc.append(dc.steps[0]["append"])
+    steps = [("config 2", d2), ("persistent 300 seqs", dp), ("INT8 config 2", d8)]
+    size = max(int(dc.steps[0]["decode"].workspace.numel()) for _, dc in steps)
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    first = None
+    for name, dc in steps + [steps[0]]:
+        dd = dc.steps[0]["decode"]
+        dd.workspace = ws
+        out = dc.decode(dd).clone()
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws[:16384])) == 0, f"{name}: chunk counters left non-zero"
+        if first is None:
+            first = out
+        elif dc is d2:
+            assert torch.equal(out.view(torch.int16), first.view(torch.int16)), "repeated call differs"
+        _say(f"  {name}: counters zero after the call")
+    # the persistent decode's outputs on the shared workspace, against the oracle
+    orc = oracle.get()
+    K, V = oracle_pools(cp, orc)
+    d = cp.steps[0].decode
+    pick = [0, 7, 150, 299]
+    ref = orc.decode(d.q[pick], K, V, np.ascontiguousarray(d.block_table[pick]), d.seq_lens[pick], cp.scale)
+    compare(_f64(dp.steps[0]["decode"].out)[pick], ref, "persistent decode on the shared workspace")
