@@ -104,13 +104,14 @@ def profile_pass(args):
         dc = DeviceCase(case, pools=n_rot)
         dc.run_fills()
         st = dc.steps[0]
-        warm(lambda: dc.decode_append(st["append"], st["decode"]))
+        # as timed: every pool copy's step in one HIP graph, replayed
+        g = dc.capture(lambda: [dc.decode_append(st["append"], st["decode"], pool=r) for r in range(n_rot)])
+        warm(g.replay)
+        for _ in range(-(-n // n_rot)):
+            g.replay()
         torch.cuda.synchronize()
-        for i in range(n):
-            dc.decode_append(st["append"], st["decode"], pool=i % n_rot)
-        torch.cuda.synchronize()
-        del dc
-        done.append(f"{n} decode steps")
+        del g, dc
+        done.append(f"{-(-n // n_rot) * n_rot} decode steps")
     if only in (None, "prefill"):
         pc = DeviceCase(W.config3_prefill())
         pc.run_fills()
@@ -215,12 +216,41 @@ def _timed_replays(graphs, n, warmup):
     return t0.elapsed_time(t1) / n
 
 
+def _timed_steps(dc, call, n_rot, k, warmup):
+    """Mean ms per step over exactly `k` steps, where step i is `call(i %
+    n_rot)` (pool copy i % n_rot): one HIP graph holds the steps of all n_rot
+    copies in order -- as a serving engine's per-token graph holds one
+    attention step per layer, each over that layer's cache -- and is replayed
+    k // n_rot times, then a graph of the k % n_rot steps left runs once;
+    events on the current stream bracket the replays, after about `warmup`
+    steps of the same graph."""
+    import torch
+    full = dc.capture(lambda: [call(r) for r in range(n_rot)])
+    part = dc.capture(lambda: [call(r) for r in range(k % n_rot)]) if k % n_rot else None
+    stream = torch.cuda.current_stream()
+    for _ in range(max(1, warmup // n_rot)):
+        full.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(k // n_rot):
+        full.replay()
+    if part is not None:
+        part.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    del full, part
+    return t0.elapsed_time(t1) / k
+
+
 def time_decode_workload(args):
     """The headline step: kv_append of one row per sequence, then the decode,
-    captured once per pool copy in a HIP graph (as a serving loop replays its
-    decode step).  Returns the step time, the decode call's time per launch
-    (its own graphs, replayed back to back) and the eagerly launched step's
-    time for context."""
+    in one decode_append launch, timed over exactly args.steps steps rotating
+    over the pool copies, all copies' steps in one HIP graph (_timed_steps).
+    Returns the step time, the two-call step's and the decode call's (same
+    graphs), the eagerly launched two-call step's, and the step's with one
+    graph per step (each replay then pays a graph launch) for context."""
     import torch
     from paged_kv_gqa_scatter_amd import workloads as W
     from paged_kv_gqa_scatter_amd.runner import DeviceCase
@@ -251,15 +281,17 @@ def time_decode_workload(args):
     torch.cuda.synchronize()
     eager_ms = t0.elapsed_time(t1) / args.steps
 
-    # the step as one decode_append launch (append + decode fused), and as
-    # kv_append then paged_gqa_decode, each captured per pool copy
-    fused = [dc.capture(lambda r=r: dc.decode_append(step["append"], step["decode"], pool=r)) for r in range(n_rot)]
-    split = [dc.capture_step(0, pool=r) for r in range(n_rot)]
-    decodes = [dc.capture(lambda r=r: dc.decode(step["decode"], pool=r)) for r in range(n_rot)]
-    step_ms = _timed_replays(fused, args.steps, args.warmup)
-    split_ms = _timed_replays(split, args.steps, max(args.warmup // 2, 10))
-    dec_ms = _timed_replays(decodes, args.steps, max(args.warmup // 2, 10))
-    return case, dec, kv_bytes, n_rot, step_ms, dec_ms, eager_ms, split_ms
+    # the step as one decode_append launch (append + decode fused), as
+    # kv_append then paged_gqa_decode, and the decode call alone
+    step_ms = _timed_steps(dc, lambda r: dc.decode_append(step["append"], step["decode"], pool=r), n_rot,
+                           args.steps, args.warmup)
+    split_ms = _timed_steps(dc, lambda r: dc.run_step(0, r), n_rot, args.steps, max(args.warmup // 2, 10))
+    dec_ms = _timed_steps(dc, lambda r: dc.decode(step["decode"], pool=r), n_rot, args.steps,
+                          max(args.warmup // 2, 10))
+    one = [dc.capture(lambda r=r: dc.decode_append(step["append"], step["decode"], pool=r)) for r in range(n_rot)]
+    one_ms = _timed_replays(one, args.steps, max(args.warmup // 2, 10))
+    del one
+    return case, dec, kv_bytes, n_rot, step_ms, dec_ms, eager_ms, split_ms, one_ms
 
 
 def time_mixed_step(args):
@@ -414,18 +446,16 @@ def time_int8(args, bf16_step_ms, bf16_long_ms):
     dc = Int8DeviceCase(case, pools=n_rot)
     dc.run_fills()
     step = dc.steps[0]
-    fused = [dc.capture(lambda r=r: dc.decode_append(step["append"], step["decode"], pool=r)) for r in range(n_rot)]
-    split = [dc.capture_step(0, pool=r) for r in range(n_rot)]
-    decodes = [dc.capture(lambda r=r: dc.decode(step["decode"], pool=r)) for r in range(n_rot)]
-    ms = _timed_replays(fused, args.steps, max(args.warmup // 2, 10))
-    sms = _timed_replays(split, args.steps, max(args.warmup // 2, 10))
-    dms = _timed_replays(decodes, args.steps, max(args.warmup // 2, 10))
-    del fused, split, decodes, dc
+    ms = _timed_steps(dc, lambda r: dc.decode_append(step["append"], step["decode"], pool=r), n_rot, args.steps,
+                      max(args.warmup // 2, 10))
+    sms = _timed_steps(dc, lambda r: dc.run_step(0, r), n_rot, args.steps, max(args.warmup // 2, 10))
+    dms = _timed_steps(dc, lambda r: dc.decode(step["decode"], pool=r), n_rot, args.steps, max(args.warmup // 2, 10))
+    del dc
     torch.cuda.empty_cache()
     gbs = nbytes / (ms * 1e-3) / 1e9
     res["decode_step"] = {
         "workload": "the headline decode step over an INT8 cache: one paged_gqa_decode_append_int8 launch "
-                    "(quantising append + decode), HIP graph per pool copy",
+                    "(quantising append + decode), pool copies' steps in one HIP graph",
         "ms_per_step": round(ms, 5), "bf16_fused_step_ms": round(bf16_step_ms, 5),
         "ms_per_step_append_then_decode": round(sms, 5), "decode_only_ms": round(dms, 5),
         "unique_kv_bytes": int(nbytes),
@@ -570,7 +600,7 @@ def main():
         profile_pass(args)
         return
 
-    case, dec, kv_bytes, n_rot, step_ms, dec_ms, eager_ms, split_ms = time_decode_workload(args)
+    case, dec, kv_bytes, n_rot, step_ms, dec_ms, eager_ms, split_ms, one_ms = time_decode_workload(args)
     gbs = kv_bytes / (step_ms * 1e-3) / 1e9
     line = {
         "metric": "paged GQA attn: decode KV-read GB/s + prefill causal TFLOP/s (bf16, 1 GPU)",
@@ -588,11 +618,14 @@ def main():
         "config": {"workload": "qwen3-8b one-layer decode step: kv_append + paged_gqa_decode (one decode_append "
                                "launch), 8 seqs, ctx U[512,2048], 32q/8kv heads, d128, block 256",
                    "seqs": int(dec.seq_lens.shape[0]), "keys": int(dec.seq_lens.sum()),
-                   "unique_kv_bytes": int(kv_bytes), "pool_copies_rotated": n_rot, "hip_graph": True,
+                   "unique_kv_bytes": int(kv_bytes), "pool_copies_rotated": n_rot,
+                   "hip_graph": f"the {n_rot} pool copies' steps in one graph (one step per layer of a decode "
+                                f"iteration), replayed",
                    "ms_per_step_append_then_decode": round(split_ms, 5),
-                   "eager_ms_per_step_append_then_decode": round(eager_ms, 5)},
+                   "eager_ms_per_step_append_then_decode": round(eager_ms, 5),
+                   "ms_per_step_one_graph_per_step": round(one_ms, 5)},
         "roofline": {"bound": "hbm", "kernel": "paged_gqa_decode_append (decode_kernel, split sequences merged "
-                                                "in the kernel), one HIP-graph replay per launch, back to back",
+                                                "in the kernel), launches back to back in HIP graphs",
                      "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": int(kv_bytes),
                      "ms": round(step_ms, 5), "decode_only_ms": round(dec_ms, 5)},
