@@ -157,20 +157,22 @@ def test_qkv_qwen3_prefill_sampled(orc):
     x, w = _inputs(rng, T, 4096, (32 + 16) * 128)
     cu = a.cu_new_lens
     pick = set(rng.choice(T, 24, replace=False).tolist()) | set(cu[:-1].tolist()) | set((cu[1:] - 1).tolist())
-    pick |= {127, 128, 255, 256, T - 1}
+    pick |= {127, 128, 255, 256, 511, 512, T - 257, T - 256, T - 1}
     _say(f"case qkv qwen3-8b prefill prompts: T {T}, {len(pick)} tokens sampled")
     _compare(orc, x, w, 32, 8, 128, 256, case.num_blocks, cu, a.ctx_lens, a.block_table, sorted(pick), "sampled")
 
 
 def test_qkv_wide_tiles_ragged_tails(orc):
-    # enough tokens for the 128 x 128 tile path (258 tiles), with a ragged
-    # token tail (16400 = 128 * 128 + 16) and a ragged feature tail (n_out 192)
+    # enough tokens for the 128 x 128 tile path (129 x 5 = 645 tiles), with a
+    # ragged token tail (16400 = 128 * 128 + 16) and a ragged feature tail
+    # (n_out 576 = 4.5 x 128)
     rng = np.random.default_rng(41)
-    hq, hkv, d, bs, dm = 1, 1, 64, 16, 128
+    hq, hkv, d, bs, dm = 3, 3, 64, 16, 128
     table, cu, ctx, nb = _placement(rng, [3, 0, 9], [8000, 8000, 400], bs)
     x, w = _inputs(rng, int(cu[-1]), dm, (hq + 2 * hkv) * d)
     T = int(cu[-1])
-    pick = set(rng.choice(T, 40, replace=False).tolist()) | {0, 127, 128, 7999, 8000, 16383, 16384, T - 1}
+    pick = set(rng.choice(T, 40, replace=False).tolist()) | {0, 127, 128, 255, 256, 511, 512, 7999, 8000, 16383,
+                                                               16384, T - 1}
     _say(f"case qkv wide tiles: T {T}, n_out {(hq + 2 * hkv) * d}, {len(pick)} tokens sampled")
     _compare(orc, x, w, hq, hkv, d, bs, nb, cu, ctx, table, sorted(pick), "wide, ragged tails")
 
