@@ -295,9 +295,11 @@ def time_decode_workload(args):
 
 
 def time_mixed_step(args):
-    """The mixed continuous-batching step (one kv_append of 64 + 1024 rows,
-    a 64-sequence decode, two 512-row chunks on 1024 cached tokens), captured
-    in a HIP graph and replayed."""
+    """The mixed continuous-batching step (64 + 1024 new rows appended, a
+    64-sequence decode, two 512-row chunks on 1024 cached tokens), captured
+    in a HIP graph and replayed: the decode sequences' rows are appended by
+    the decode launch itself, and the prefill rows' append and the prefill
+    run beside it on a second stream (DeviceCase.run_step)."""
     import torch
     from paged_kv_gqa_scatter_amd import workloads as W
     from paged_kv_gqa_scatter_amd.runner import DeviceCase
@@ -313,7 +315,8 @@ def time_mixed_step(args):
     del g, dc
     torch.cuda.empty_cache()
     return {"workload": "qwen3-8b mixed step: 64 decode seqs (ctx log-uniform [128, 8192]) + 2 x 512-row chunks on "
-                        "1024 cached; 32q/8kv, d128, block 256; one HIP graph",
+                        "1024 cached; 32q/8kv, d128, block 256; one HIP graph, decode_append and "
+                        "kv_append + prefill as parallel branches",
             "ms": round(ms, 5), "decode_unique_kv_bytes": int(kv_bytes), "prefill_causal_flops": int(flops),
             "decode_gbs_if_alone": round(kv_bytes / (ms * 1e-3) / 1e9, 2)}
 

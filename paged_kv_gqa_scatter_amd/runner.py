@@ -75,6 +75,8 @@ class DeviceCase:
     def __init__(self, case: Case, device: str = "cuda", pools: int = 1):
         self.case = case
         self.device = torch.device(device)
+        self._side = None  # second stream of a step with both decode and prefill
+        self._mixed = {}   # such steps' append batches split into decode and prefill rows
         shape = (case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim)
         self.pools = []
         for _ in range(pools):  # several copies let a timing loop rotate past the caches
@@ -153,9 +155,38 @@ class DeviceCase:
             for f in self.fills:
                 self.append(f, p)
 
+    def _mixed_parts(self, i: int):
+        """The append batch of step i split into its decode rows (one per
+        decode sequence, first in the batch) and its prefill rows."""
+        if i not in self._mixed:
+            a, nd = self.steps[i]["append"], self.steps[i]["decode"].q.shape[0]
+            dec = DevAppend(a.k_new[:nd], a.v_new[:nd], a.cu_new_lens[:nd + 1], a.ctx_lens[:nd], a.block_table[:nd])
+            pre = DevAppend(a.k_new[nd:], a.v_new[nd:], (a.cu_new_lens[nd:] - nd).contiguous(), a.ctx_lens[nd:],
+                            a.block_table[nd:])
+            self._mixed[i] = (dec, pre)
+        return self._mixed[i]
+
     def run_step(self, i: int, pool: int = 0) -> Dict[str, torch.Tensor]:
+        """Step i: its append, then its decode and prefill.  A step with both
+        runs them side by side: the decode sequences' rows are appended by the
+        decode itself (decode_append) on the current stream, while a second
+        stream appends the prefill rows and runs the prefill -- the decode
+        streams HBM while the prefill keeps the matrix cores busy.  Captured
+        in a graph, the two are parallel branches."""
         st = self.steps[i]
         res = {}
+        if st["append"] is not None and st["decode"] is not None and st["prefill"] is not None:
+            dec, pre = self._mixed_parts(i)
+            cur = torch.cuda.current_stream(self.device)
+            if self._side is None:
+                self._side = torch.cuda.Stream(self.device)  # default priority
+            self._side.wait_stream(cur)
+            with torch.cuda.stream(self._side):
+                self.append(pre, pool)
+                res["prefill"] = self.prefill(st["prefill"], pool)
+            res["decode"] = self.decode_append(dec, st["decode"], pool)
+            cur.wait_stream(self._side)
+            return res
         if st["append"] is not None:
             self.append(st["append"], pool)
         if st["decode"] is not None:
