@@ -33,7 +33,9 @@
 //    32 x 32 tile; the destination row of every token of the tile (its q_out
 //    row and its cache slot) is computed once per workgroup into LDS.
 //  * Calls with too few tokens to give every CU a 128 x 128 tile (decode
-//    steps) use 32 x 32 tiles with d_model split over eight waves instead.
+//    steps) use tiles of 32 tokens x tn features, tn the widest multiple of 8
+//    up to 32 that still gives every CU a tile (24 at 6144 features: 256
+//    tiles instead of 192 of 32), with d_model split over eight waves.
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -57,6 +59,7 @@ struct QkvKernelArgs {
     int32_t m_tiles;  // token tiles
     int32_t tiles;    // token tiles * feature tiles
     int32_t per_xcd;  // tiles dealt to each XCD
+    int32_t tn;       // few-token kernel: output features per tile (8..32)
 };
 
 // global_load_lds_dwordx4 with a scalar base: lane l's 16 bytes at
@@ -226,7 +229,8 @@ __global__ __launch_bounds__(kQkvThreads) void qkv_append_kernel(QkvKernelArgs p
 }
 
 // Few tokens (a decode step): the weight stream dominates and 128 x 128 tiles
-// would leave most CUs idle, so a workgroup takes a 32 x 32 tile and its
+// would leave most CUs idle, so a workgroup takes a 32 x tn tile (computed as
+// 32 x 32, the columns past tn masked) and its
 // eight waves split d_model (wave w: 64-wide steps w, w + 8, ..., three in
 // flight), reducing through LDS at the end.  Operands come straight from
 // global memory: lane (row i, half h) loads 64 contiguous bytes of its X row
@@ -242,14 +246,16 @@ __global__ __launch_bounds__(kSkinnyThreads) void qkv_append_skinny_kernel(QkvKe
     const int tile = xcd * p.per_xcd + j;
     if (j >= p.per_xcd || tile >= p.tiles) return;
     const int m0 = (tile % p.m_tiles) * 32;
-    const int n0 = (tile / p.m_tiles) * 32;
+    const int n0 = (tile / p.m_tiles) * p.tn;
     const int T = a.total_new_tokens, K = a.d_model;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (threadIdx.x < 32) s_dst[threadIdx.x] = token_dst(a, m0 + threadIdx.x);
 
-    const int h = lane >> 5;
-    const uint16_t* xr = a.x + (int64_t)min(m0 + (lane & 31), T - 1) * K + 32 * h;
-    const uint16_t* wr = a.w + (int64_t)min(n0 + (lane & 31), p.n_out - 1) * K + 32 * h;
+    // columns past the tile's tn features repeat its last row (the same
+    // cache lines) and are not stored
+    const int h = lane >> 5, col = lane & 31;
+    const uint16_t* xr = a.x + (int64_t)min(m0 + col, T - 1) * K + 32 * h;
+    const uint16_t* wr = a.w + (int64_t)min(n0 + min(col, p.tn - 1), p.n_out - 1) * K + 32 * h;
     f32x16 acc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.f;
@@ -297,7 +303,7 @@ __global__ __launch_bounds__(kSkinnyThreads) void qkv_append_skinny_kernel(QkvKe
     for (int w = 0; w < kSkinnyWaves - 1; ++w)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[e] += s_red[w][e][lane];
-    store_tile(a, p.n_out, acc, m0, 0, n0 + (lane & 31), s_dst);
+    store_tile(a, p.n_out, acc, m0, 0, col < p.tn ? n0 + col : p.n_out, s_dst);
 }
 
 }  // namespace
@@ -310,13 +316,18 @@ hipError_t launch_qkv_append(const QkvArgs& a, hipStream_t stream) {
     kp.m_tiles = (a.total_new_tokens + kTileM - 1) / kTileM;
     kp.tiles = kp.m_tiles * ((kp.n_out + kTileN - 1) / kTileN);
     if (kp.tiles < device_cu_count()) {  // too few 128 x 128 tiles to fill the chip: 32 x 32 tiles
+        // the widest tiles (a multiple of 8 features, at most 32) that still
+        // give every CU one
         kp.m_tiles = (a.total_new_tokens + 31) / 32;
-        kp.tiles = kp.m_tiles * ((kp.n_out + 31) / 32);
+        kp.tn = 32;
+        while (kp.tn > 8 && (int64_t)kp.m_tiles * ((kp.n_out + kp.tn - 1) / kp.tn) < device_cu_count()) kp.tn -= 8;
+        kp.tiles = kp.m_tiles * ((kp.n_out + kp.tn - 1) / kp.tn);
         kp.per_xcd = (kp.tiles + kXcds - 1) / kXcds;
         hipLaunchKernelGGL(qkv_append_skinny_kernel, dim3((unsigned)(kp.per_xcd * kXcds)), dim3(kSkinnyThreads), 0,
                            stream, kp);
         return hipGetLastError();
     }
+    kp.tn = kTileN;
     kp.per_xcd = (kp.tiles + kXcds - 1) / kXcds;
     hipLaunchKernelGGL(qkv_append_kernel, dim3((unsigned)(kp.per_xcd * kXcds)), dim3(kQkvThreads), 0, stream, kp);
     return hipGetLastError();

@@ -187,3 +187,15 @@ def test_qkv_few_tokens(orc, dm):
     x, w = _inputs(rng, int(cu[-1]), dm, (hq + 2 * hkv) * d)
     _say(f"case qkv few tokens: T {int(cu[-1])}, dm {dm}")
     _compare(orc, x, w, hq, hkv, d, bs, nb, cu, ctx, table, np.arange(int(cu[-1])), "few tokens")
+
+
+def test_qkv_few_tokens_narrow_ragged_tiles(orc):
+    # 8 tokens and 6400 features (80 + 2 x 10 heads of 64): 32-feature tiles
+    # would give 200 workgroups, so tiles of 24 features are used, the last
+    # one holding 16
+    rng = np.random.default_rng(61)
+    hq, hkv, d, bs, dm = 80, 10, 64, 16, 256
+    table, cu, ctx, nb = _placement(rng, [40, 7, 0], [3, 4, 1], bs)
+    x, w = _inputs(rng, int(cu[-1]), dm, (hq + 2 * hkv) * d)
+    _say(f"case qkv few tokens, narrow tiles: T {int(cu[-1])}, n_out {(hq + 2 * hkv) * d}")
+    _compare(orc, x, w, hq, hkv, d, bs, nb, cu, ctx, table, np.arange(int(cu[-1])), "narrow ragged tiles")
