@@ -68,7 +68,8 @@ def parse():
     ap.add_argument("--copy-mib", type=int, default=256, help="size of the reference copy in --profile-pass")
     ap.add_argument("--profile-warm-s", type=float, default=0.0,
                     help="--profile-pass: run each workload this long before its counted calls (steady clocks)")
-    ap.add_argument("--profile-only", choices=("decode", "prefill", "long", "int8", "qkv", "qkvdec", "copy"),
+    ap.add_argument("--profile-only", choices=("decode", "prefill", "long", "int8", "int8step", "qkv", "qkvdec",
+                                               "copy"),
                     default=None,
                     help="--profile-pass: run only this workload (counter passes per workload)")
     return ap.parse_args()
@@ -80,8 +81,9 @@ def profile_pass(args):
     few times each (the long one last, unless --no-long), and one plain
     device-to-device copy of --copy-mib MiB whose counter readings calibrate
     the byte counters.  --profile-only also offers the INT8 long-context
-    decode (int8) and the fused QKV projection at the prefill-prompt (qkv)
-    and decode-step (qkvdec) shapes."""
+    decode (int8), the INT8 decode step (int8step, graphed as timed) and the
+    fused QKV projection at the prefill-prompt (qkv) and decode-step (qkvdec)
+    shapes."""
     import torch
     import paged_kv_gqa_scatter_amd as pkv
     from paged_kv_gqa_scatter_amd import workloads as W
@@ -132,6 +134,20 @@ def profile_pass(args):
         torch.cuda.synchronize()
         del lc
         done.append(f"{n} long-context decodes")
+    if only == "int8step":
+        case = W.config2_decode()
+        pool_bytes = case.pool_bytes * (case.head_dim + 4) // (2 * case.head_dim)
+        n_rot = max(1, -(-ROTATE_BYTES // pool_bytes))  # as timed: every step reads HBM
+        ic = Int8DeviceCase(case, pools=n_rot)
+        ic.run_fills()
+        st = ic.steps[0]
+        g = ic.capture(lambda: [ic.decode_append(st["append"], st["decode"], pool=r) for r in range(n_rot)])
+        warm(g.replay)
+        for _ in range(-(-n // n_rot)):
+            g.replay()
+        torch.cuda.synchronize()
+        del g, ic
+        done.append(f"{-(-n // n_rot) * n_rot} INT8 decode steps")
     if only == "int8":
         ic = Int8DeviceCase(W.config5_prefix_long(draw_values=False))
         ic.run_fills()
@@ -465,7 +481,10 @@ def time_int8(args, bf16_step_ms, bf16_long_ms):
         "roofline": {"bound": "hbm", "kernel": "paged_gqa_decode_append_int8 (decode_int8_kernel, split "
                                                 "sequences merged in the kernel)",
                      "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
+    rec = traffic_record("int8_decode_append")
+    if rec is not None:
+        res["decode_step"]["roofline"]["traffic"] = int(rec["hbm_bytes_per_launch"])
     if not args.no_long:
         case = W.config5_prefix_long(draw_values=False)
         dec = case.steps[0].decode
