@@ -60,6 +60,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long", action="store_true", help="skip the long-context decode measurement")
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed continuous-batching step")
+    ap.add_argument("--no-append", action="store_true", help="skip the kv_append measurement")
     ap.add_argument("--no-int8", action="store_true", help="skip the INT8 KV cache measurements")
     ap.add_argument("--no-qkv", action="store_true", help="skip the fused QKV projection measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -232,7 +233,7 @@ def _timed_replays(graphs, n, warmup):
     return t0.elapsed_time(t1) / n
 
 
-def _timed_steps(dc, call, n_rot, k, warmup):
+def _timed_steps(capture, call, n_rot, k, warmup):
     """Mean ms per step over exactly `k` steps, where step i is `call(i %
     n_rot)` (pool copy i % n_rot): one HIP graph holds the steps of all n_rot
     copies in order -- as a serving engine's per-token graph holds one
@@ -241,8 +242,8 @@ def _timed_steps(dc, call, n_rot, k, warmup):
     events on the current stream bracket the replays, after about `warmup`
     steps of the same graph."""
     import torch
-    full = dc.capture(lambda: [call(r) for r in range(n_rot)])
-    part = dc.capture(lambda: [call(r) for r in range(k % n_rot)]) if k % n_rot else None
+    full = capture(lambda: [call(r) for r in range(n_rot)])
+    part = capture(lambda: [call(r) for r in range(k % n_rot)]) if k % n_rot else None
     stream = torch.cuda.current_stream()
     for _ in range(max(1, warmup // n_rot)):
         full.replay()
@@ -299,15 +300,63 @@ def time_decode_workload(args):
 
     # the step as one decode_append launch (append + decode fused), as
     # kv_append then paged_gqa_decode, and the decode call alone
-    step_ms = _timed_steps(dc, lambda r: dc.decode_append(step["append"], step["decode"], pool=r), n_rot,
+    step_ms = _timed_steps(dc.capture, lambda r: dc.decode_append(step["append"], step["decode"], pool=r), n_rot,
                            args.steps, args.warmup)
-    split_ms = _timed_steps(dc, lambda r: dc.run_step(0, r), n_rot, args.steps, max(args.warmup // 2, 10))
-    dec_ms = _timed_steps(dc, lambda r: dc.decode(step["decode"], pool=r), n_rot, args.steps,
+    split_ms = _timed_steps(dc.capture, lambda r: dc.run_step(0, r), n_rot, args.steps, max(args.warmup // 2, 10))
+    dec_ms = _timed_steps(dc.capture, lambda r: dc.decode(step["decode"], pool=r), n_rot, args.steps,
                           max(args.warmup // 2, 10))
     one = [dc.capture(lambda r=r: dc.decode_append(step["append"], step["decode"], pool=r)) for r in range(n_rot)]
     one_ms = _timed_replays(one, args.steps, max(args.warmup // 2, 10))
     del one
     return case, dec, kv_bytes, n_rot, step_ms, dec_ms, eager_ms, split_ms, one_ms
+
+
+def time_kv_append(args):
+    """kv_append alone: config 3's prompt rows (8130 tokens x 8 KV heads x
+    128 dims, K and V) into 256-token blocks, bf16 and through the INT8 cache
+    (quantising append), each over exactly args.steps calls rotating over
+    pool copies and copies of the new rows (>= 1 GiB together) so that every
+    call reads and writes HBM.  Bytes are the rows read plus the rows written:
+    bf16 2 x T x Hkv x D x 2 x 2; INT8 T x Hkv x (2 D x 2 read + 2 (D + 4)
+    written)."""
+    import torch
+    import paged_kv_gqa_scatter_amd as pkv
+    from paged_kv_gqa_scatter_amd import workloads as W
+    from paged_kv_gqa_scatter_amd.runner import capture_graph
+
+    case = W.config3_prefill(draw_values=False)
+    a = case.steps[0].append
+    T = int(a.cu_new_lens[-1])
+    NB, Hkv, B, D = case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim
+    dev = lambda v: torch.from_numpy(np.ascontiguousarray(v)).cuda()
+    cu, ctx, tab = dev(a.cu_new_lens), dev(a.ctx_lens), dev(a.block_table)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0xA99)
+    res = {"workload": f"qwen3-8b prefill prompts' rows appended: {T} tokens x {Hkv} KV heads x {D}, block {B}"}
+    for name in ("bf16", "int8"):
+        rows_bytes = T * Hkv * D * 2 * 2
+        pool_bytes = case.pool_bytes if name == "bf16" else case.pool_bytes * (D + 4) // (2 * D)
+        n_rot = max(1, -(-ROTATE_BYTES // (pool_bytes + rows_bytes)))
+        rows = [(torch.randn((T, Hkv, D), generator=gen, device="cuda").to(torch.bfloat16),
+                 torch.randn((T, Hkv, D), generator=gen, device="cuda").to(torch.bfloat16)) for _ in range(n_rot)]
+        if name == "bf16":
+            caches = [(torch.empty((NB, Hkv, B, D), dtype=torch.bfloat16, device="cuda"),
+                       torch.empty((NB, Hkv, B, D), dtype=torch.bfloat16, device="cuda")) for _ in range(n_rot)]
+            call = lambda r: pkv.kv_append(*caches[r], *rows[r], cu, ctx, tab)
+            nbytes = 2 * rows_bytes
+        else:
+            caches = [pkv.empty_int8_cache(NB, Hkv, B, D) for _ in range(n_rot)]
+            call = lambda r: pkv.kv_append_int8(*caches[r], *rows[r], cu, ctx, tab)
+            nbytes = rows_bytes + T * Hkv * 2 * (D + 4)
+        ms = _timed_steps(capture_graph, call, n_rot, args.steps, max(args.warmup // 4, 10))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 5), "bytes": int(nbytes), "copies_rotated": n_rot,
+                     "roofline": {"bound": "hbm", "kernel": "kv_append" if name == "bf16" else "kv_append_int8",
+                                  "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+        del rows, caches
+        torch.cuda.empty_cache()
+    return res
 
 
 def time_mixed_step(args):
@@ -465,10 +514,11 @@ def time_int8(args, bf16_step_ms, bf16_long_ms):
     dc = Int8DeviceCase(case, pools=n_rot)
     dc.run_fills()
     step = dc.steps[0]
-    ms = _timed_steps(dc, lambda r: dc.decode_append(step["append"], step["decode"], pool=r), n_rot, args.steps,
-                      max(args.warmup // 2, 10))
-    sms = _timed_steps(dc, lambda r: dc.run_step(0, r), n_rot, args.steps, max(args.warmup // 2, 10))
-    dms = _timed_steps(dc, lambda r: dc.decode(step["decode"], pool=r), n_rot, args.steps, max(args.warmup // 2, 10))
+    ms = _timed_steps(dc.capture, lambda r: dc.decode_append(step["append"], step["decode"], pool=r), n_rot,
+                      args.steps, max(args.warmup // 2, 10))
+    sms = _timed_steps(dc.capture, lambda r: dc.run_step(0, r), n_rot, args.steps, max(args.warmup // 2, 10))
+    dms = _timed_steps(dc.capture, lambda r: dc.decode(step["decode"], pool=r), n_rot, args.steps,
+                       max(args.warmup // 2, 10))
     del dc
     torch.cuda.empty_cache()
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -675,6 +725,8 @@ def main():
         line["int8_kv_cache"] = time_int8(args, step_ms, line.get("long_context_decode", {}).get("ms"))
     if not args.no_mixed:
         line["mixed_step"] = time_mixed_step(args)
+    if not args.no_append:
+        line["kv_append"] = time_kv_append(args)
     line["device"] = device_context()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, dec, kv_bytes, args.cpu_seconds)

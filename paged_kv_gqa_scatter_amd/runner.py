@@ -68,6 +68,24 @@ class DevPrefill:
     out: torch.Tensor
 
 
+def capture_graph(fn) -> "torch.cuda.CUDAGraph":
+    """Record what ``fn()`` launches on the current stream into a HIP graph
+    (torch.cuda.CUDAGraph); ``replay()`` reruns it with the same buffers.  The
+    library's calls allocate nothing, synchronise nothing and clear nothing
+    with memset, so a whole step can be captured; ``fn`` runs once eagerly
+    first, on a side stream, as torch's capture requires."""
+    cur = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        fn()
+    cur.wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
 class DeviceCase:
     """A case resident on one GPU: pools, and every batch's inputs and outputs
     preallocated, so that running a step allocates nothing."""
@@ -196,21 +214,8 @@ class DeviceCase:
         return res
 
     def capture(self, fn) -> "torch.cuda.CUDAGraph":
-        """Record what ``fn()`` launches on the current stream into a HIP
-        graph (torch.cuda.CUDAGraph); ``replay()`` reruns it with the same
-        buffers.  The library's calls allocate nothing, synchronise nothing and
-        clear nothing with memset, so a whole step can be captured; ``fn`` runs
-        once eagerly first, on a side stream, as torch's capture requires."""
-        cur = torch.cuda.current_stream()
-        side = torch.cuda.Stream()
-        side.wait_stream(cur)
-        with torch.cuda.stream(side):
-            fn()
-        cur.wait_stream(side)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            fn()
-        return g
+        """``capture_graph(fn)``."""
+        return capture_graph(fn)
 
     def capture_step(self, i: int, pool: int = 0) -> "torch.cuda.CUDAGraph":
         """A HIP graph of step ``i`` (append, then decode and/or prefill)."""
