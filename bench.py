@@ -664,7 +664,7 @@ def cpu_baseline(case, dec, kv_bytes, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "bench.py measures one GPU; --gpus must be 1"}))
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench needs a GPU"
