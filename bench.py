@@ -411,8 +411,8 @@ def time_prefill_workload(args):
         dc.prefill(step["prefill"])
         b.record(stream)
     torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    return case, flops, ms
+    times = [a.elapsed_time(b) for a, b in evs]
+    return case, flops, float(np.mean(times)), float(np.median(times)), float(np.min(times))
 
 
 def device_context():
@@ -481,13 +481,16 @@ def time_long_decode(args):
         dc.decode(step["decode"])
         b.record(stream)
     torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    times = [a.elapsed_time(b) for a, b in evs]
+    ms = float(np.mean(times))
     del dc
     torch.cuda.empty_cache()
     gbs = uniq / (ms * 1e-3) / 1e9
     return {"workload": "qwen3-8b decode, 256 seqs sharing a 4096-token prefix + U[0,2048] private, 16 seqs x 32768; "
                         "32q/8kv, d128, block 256",
-            "ms": round(ms, 5), "unique_kv_bytes": int(uniq), "logical_kv_bytes": int(logical),
+            "ms": round(ms, 5), "ms_median": round(float(np.median(times)), 5),
+            "ms_min": round(float(np.min(times)), 5),
+            "launches_timed": len(times), "unique_kv_bytes": int(uniq), "logical_kv_bytes": int(logical),
             "value": round(gbs, 2), "unit": "GB/s", "logical_gbs": round(logical / (ms * 1e-3) / 1e9, 2),
             "roofline": {"bound": "hbm", "kernel": "paged_gqa_decode (decode_kernel + decode_merge_kernel)",
                          "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -706,11 +709,12 @@ def main():
     if rec is not None:
         line["roofline"]["traffic"] = int(rec["hbm_bytes_per_launch"])
     if not args.no_prefill:
-        pcase, flops, pms = time_prefill_workload(args)
+        pcase, flops, pms, pmed, pmin = time_prefill_workload(args)
         tfs = flops / (pms * 1e-3) / 1e12
         line["prefill"] = {
             "workload": "qwen3-8b one-layer causal prefill: 4 prompts U[1024,4096], 32q/8kv, d128, block 256",
             "value": round(tfs, 2), "unit": "TFLOP/s", "causal_flops": int(flops), "ms": round(pms, 5),
+            "ms_median": round(pmed, 5), "ms_min": round(pmin, 5), "launches_timed": args.prefill_steps,
             "roofline": {"bound": "mfma", "kernel": "paged_gqa_prefill (prefill_kernel)", "achieved": round(tfs, 2),
                          "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
                          "traffic": None}}
