@@ -115,6 +115,8 @@ def test_decode_workspace_bytes(lib):
     assert f(8, 32, 8, 128, 2049, 10248) > 0
     assert f(8, 32, 8, 128, 2049, 0) > 0
     assert f(272, 32, 8, 128, 32769, 1_830_000) < f(272, 32, 8, 128, 32769, 0)
+    # every workspace starts with the 16 KiB of chunk counters, whatever the shape
+    assert all(f(S, 4, 1, 64, L, 0) > 16384 for S in (1, 8) for L in (1, 300))
 
 
 def decode_append_args(**kw):
@@ -204,6 +206,7 @@ def test_decode_int8_workspace_bytes(lib):
     assert f(8, 32, 8, 96, 2049, 0) == 0
     assert f(8, 32, 8, 128, 2049, 0) > 0
     assert f(272, 32, 8, 128, 32769, 1_830_000) < f(272, 32, 8, 128, 32769, 0)
+    assert f(1, 4, 1, 64, 1, 0) > 16384  # the chunk counters come first here too
 
 
 def qkv_args(**kw):
