@@ -499,6 +499,50 @@ def time_long_decode(args):
                              traffic_record("long_decode"))}}
 
 
+def time_private_long_decode(args):
+    """Decode over private long contexts only: 16 sequences of 32768 cached
+    tokens + 1 (2.15 GB of K/V, no block shared), the streaming rate of the
+    split kernel without the shared prefix of the long-context workload.
+    Lengths and placement seeded; values drawn on the device (timing only)."""
+    import torch
+    from paged_kv_gqa_scatter_amd import workloads as W
+    from paged_kv_gqa_scatter_amd.runner import DeviceCase
+
+    rng = np.random.default_rng(16)
+    case = W.build_case("qwen3_8b_16x32k_private", rng, hq=32, hkv=8, d=128, bs=256,
+                        ctx_lens=np.full(16, 32768), new_lens=np.ones(16, np.int64), kinds="d" * 16,
+                        draw_values=False)
+    dec = case.steps[0].decode
+    uniq = W.decode_unique_kv_bytes(case, dec)
+    dc = DeviceCase(case)
+    dc.run_fills()
+    step = dc.steps[0]
+    dc.append(step["append"])
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        dc.decode(step["decode"])
+    torch.cuda.synchronize()
+    n = max(5, args.prefill_steps)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record(stream)
+        dc.decode(step["decode"])
+        b.record(stream)
+    torch.cuda.synchronize()
+    times = [a.elapsed_time(b) for a, b in evs]
+    ms = float(np.mean(times))
+    del dc
+    torch.cuda.empty_cache()
+    gbs = uniq / (ms * 1e-3) / 1e9
+    return {"workload": "qwen3-8b decode, 16 seqs x 32769 keys, private blocks; 32q/8kv, d128, block 256",
+            "ms": round(ms, 5), "ms_median": round(float(np.median(times)), 5),
+            "ms_min": round(float(np.min(times)), 5), "launches_timed": len(times), "unique_kv_bytes": int(uniq),
+            "value": round(gbs, 2), "unit": "GB/s",
+            "roofline": {"bound": "hbm", "kernel": "paged_gqa_decode (decode_kernel + decode_merge_kernel)",
+                         "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
 def time_int8(args, bf16_step_ms, bf16_long_ms):
     """The INT8 KV cache (quantising kv_append_int8, paged_gqa_decode_int8) on
     the headline decode step (both calls in one HIP graph per pool copy,
@@ -723,6 +767,7 @@ def main():
             line["prefill"]["roofline"]["traffic"] = int(prec["hbm_bytes_per_launch"])
     if not args.no_long:
         line["long_context_decode"] = time_long_decode(args)
+        line["private_long_decode"] = time_private_long_decode(args)
     if not args.no_qkv:
         line["qkv_project_append"] = time_qkv(args)
     if not args.no_int8:
