@@ -433,10 +433,9 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
     // (wgs_per_cu on each of a 256-CU part's CUs) times the round's length, a
     // load round trip (about 12 tiles) plus the tiles each wave streams.  The
     // item count is a bound (each sequence adds at most one partial chunk).
-    // Finer steps (any multiple of one tile per wave) measured slower: a
-    // chunk that is not a whole number of blocks turns shared-chunk packing
-    // off, and one that leaves the direct grid (chunks x sequences x KV heads)
-    // larger than the resident workgroups delays real items behind empty ones.
+    // Finer steps (any multiple of one tile per wave, or 1.5x powers of two)
+    // measured slower on multi-round launches (config 5: a chunk that is not
+    // a whole number of blocks also turns shared-chunk packing off).
     const int64_t slots = (int64_t)kPlanCus * wgs_per_cu;
     const int max_chunk = kMaxTilesPerWave * tile_keys * kDecodeWaves;
     int chunk = kDecodeWaves * 4 * tile_keys;
@@ -448,6 +447,15 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
             best = cost;
             chunk = c;
         }
+    }
+    // a launch of one round: three quarters of that chunk, if the items
+    // still fit the round, shorten its longest item (config 2: 512 -> 384
+    // keys, 176 -> 216 items on 256 CUs; measured 15.0 -> 14.6 us)
+    const int64_t items_at = ((total + chunk - 1) / chunk + num_seqs) * num_kv_heads;
+    if (items_at <= slots) {
+        const int c34 = chunk / 4 * 3;
+        if (c34 >= 4 * kDecodeWaves * tile_keys && ((total + c34 - 1) / c34 + num_seqs) * num_kv_heads <= slots)
+            chunk = c34;
     }
     pl.ring = 4;
     pl.chunk = chunk;

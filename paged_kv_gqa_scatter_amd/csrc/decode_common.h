@@ -360,8 +360,8 @@ __device__ __forceinline__ void finish_item(const DecodeKernelArgs& p, DecodeSha
 // past the chunk (so neither's new row of a decode_append is in it, and both
 // write partials) and its chunk's block ids equal lead's.  Every item of the
 // run evaluates the same predicate on the same data, so the members' own
-// items know to exit, with no communication.  Only chunks whose P x (blocks
-// per chunk) ids fit one load per lane are considered, and only in launches
+// items know to exit, with no communication.  Only chunks of whole blocks
+// whose P x (blocks per chunk) ids fit one load per lane are considered, and only in launches
 // with more items than two rounds of resident workgroups: below that every
 // item runs at once, a pack does not shorten the step, and its loads and
 // ballots lengthen each item's start.
@@ -384,7 +384,7 @@ __device__ __forceinline__ PackInputs load_pack_inputs(const DecodeKernelArgs& p
     const int lane = threadIdx.x & 63;
     const int nb = p.chunk >> p.log2_block;
     PackInputs pk;
-    pk.on = p.pack && P > 1 && P * nb <= kWave;
+    pk.on = p.pack && P > 1 && (p.chunk & ((1 << p.log2_block) - 1)) == 0 && P * nb <= kWave;
     pk.len = 0;
     pk.id = -1;
     if (!pk.on) return pk;
@@ -486,12 +486,15 @@ __device__ __forceinline__ void run_items(const DecodeKernelArgs& p, DecodeShare
     const int cap = p.a.max_blocks_per_seq << p.log2_block;
 
     if (!p.persistent) {
-        // direct grid: workgroup -> (chunk, sequence, KV head), KV head fastest
+        // direct grid: workgroup -> (chunk, sequence, KV head), KV head
+        // fastest, the last chunks first: they are mostly empty and leave at
+        // once, so when the grid is larger than the resident workgroups the
+        // real items are not dispatched behind them
         int idx = blockIdx.x;
         const int g = idx % Hkv;
         idx /= Hkv;
         const int s = idx % S;
-        const int c = idx / S;
+        const int c = p.max_chunks - 1 - idx / S;
         const auto in = load(s, g, c);  // before the exit test: one round trip
         const int L = clamp_len(in.L_raw, cap);
         const int n = num_chunks(L, p.chunk);
