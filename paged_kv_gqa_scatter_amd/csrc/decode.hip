@@ -452,6 +452,7 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
     // still fit the round, shorten its longest item (config 2: 512 -> 384
     // keys, 176 -> 216 items on 256 CUs; measured 15.0 -> 14.6 us)
     const int64_t items_at = ((total + chunk - 1) / chunk + num_seqs) * num_kv_heads;
+    pl.last_first = items_at <= slots ? 1 : 0;
     if (items_at <= slots) {
         const int c34 = chunk / 4 * 3;
         if (c34 >= 4 * kDecodeWaves * tile_keys && ((total + c34 - 1) / c34 + num_seqs) * num_kv_heads <= slots)
@@ -505,6 +506,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     kp.max_chunks = pl.max_chunks;
     kp.persistent = pl.persistent;
     kp.pack = pl.pack;
+    kp.last_first = pl.last_first;
     kp.max_partials = pl.max_partials;
     char* ws = static_cast<char*>(a.workspace);
     kp.counters = pl.fused ? reinterpret_cast<int32_t*>(ws + pl.counter_offset) : nullptr;

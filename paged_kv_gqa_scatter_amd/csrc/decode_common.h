@@ -45,6 +45,7 @@ struct DecodeKernelArgs {
     int32_t max_chunks;  // chunks of the longest sequence
     int32_t persistent;  // 1: persistent grid over the compact item list
     int32_t pack;        // 1: sequences sharing a chunk are decoded together
+    int32_t last_first;  // direct grid: 1 deals the last chunks first
     int32_t* counters;   // direct grid: chunks finished per (sequence, KV head),
                          // the last one merges; null: the merge kernel does
     int64_t max_partials;
@@ -487,14 +488,15 @@ __device__ __forceinline__ void run_items(const DecodeKernelArgs& p, DecodeShare
 
     if (!p.persistent) {
         // direct grid: workgroup -> (chunk, sequence, KV head), KV head
-        // fastest, the last chunks first: they are mostly empty and leave at
-        // once, so when the grid is larger than the resident workgroups the
-        // real items are not dispatched behind them
+        // fastest; in a one-round launch the last chunks first: they are
+        // mostly empty and leave at once, so when the grid is larger than
+        // the resident workgroups the real items are not dispatched behind
+        // them
         int idx = blockIdx.x;
         const int g = idx % Hkv;
         idx /= Hkv;
         const int s = idx % S;
-        const int c = p.max_chunks - 1 - idx / S;
+        const int c = p.last_first ? p.max_chunks - 1 - idx / S : idx / S;
         const auto in = load(s, g, c);  // before the exit test: one round trip
         const int L = clamp_len(in.L_raw, cap);
         const int n = num_chunks(L, p.chunk);

@@ -441,6 +441,7 @@ hipError_t launch_decode_int8(const DecodeArgs& a, const DecodePlan& pl, hipStre
     kp.max_chunks = pl.max_chunks;
     kp.persistent = pl.persistent;
     kp.pack = 0;  // the INT8 kernel decodes every sequence on its own
+    kp.last_first = pl.last_first;
     kp.max_partials = pl.max_partials;
     char* ws = static_cast<char*>(a.workspace);
     kp.counters = pl.fused ? reinterpret_cast<int32_t*>(ws + pl.counter_offset) : nullptr;

@@ -125,6 +125,7 @@ struct DecodePlan {
     int32_t persistent;       // 1: persistent grid over a compact item list
     int32_t pack;             // 1: decode sequences sharing a chunk together (bf16)
     int32_t fused;            // 1: the split kernel merges (counters), no merge kernel
+    int32_t last_first;       // 1: a one-round direct grid deals its last chunks first
     int64_t items;            // bound on (chunk, KV head) work items
     int64_t max_partials;     // (sequence, split) slots the workspace holds
     size_t counter_offset;    // int32 [num_seqs][num_kv_heads] chunk counters (fused merge)
