@@ -257,6 +257,17 @@ __device__ __forceinline__ void tile_step(const Loop<D>& lp, int t, BlockIds& bi
         st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), as_bf16x8(qreg[ks]), st[0], 0, 0, 0);
         st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), as_bf16x8(qreg[ks]), st[1], 0, 0, 0);
     }
+    // read the K fragments three steps (six reads) ahead of their MFMAs, so
+    // the LDS latency is hidden behind the MFMAs in flight rather than waited
+    // for before each pair
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // LDS reads
+#pragma unroll
+    for (int i = 0; i < D / 8 - 6; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+#pragma unroll
+    for (int i = 0; i < 6; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 
     // scores -> exp2 domain; mask only where the tile crosses this wave's diagonal
     const int half = lane >> 5;
