@@ -37,6 +37,15 @@ __device__ __forceinline__ void store16(uint16_t* p, u32x4 v) { *reinterpret_cas
 // 2^x (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max of v over lanes l and l ^ 32.  v_permlane32_swap exchanges the two
+// halves of the wave in registers (no LDS round trip, unlike a shuffle);
+// whichever result holds which half, the max of the pair is the same.
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
+                                                     false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)sw[0]), __builtin_bit_cast(float, (unsigned)sw[1]));
+}
+
 // DPP lane moves inside a row of 16 lanes (v_mov_b32_dpp).  Each control is
 // a permutation of the row: quad xor 1, quad xor 2, xor 7 within 8 lanes
 // (half-row mirror), xor 15 within 16 (row mirror), and broadcast of lane n.

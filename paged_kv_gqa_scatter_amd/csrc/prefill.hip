@@ -292,7 +292,7 @@ __device__ __forceinline__ void tile_step(const Loop<D>& lp, int t, BlockIds& bi
             for (int r = 0; r < 16; ++r) e = kNegScale ? fminf(e, st[kb][r]) : fmaxf(e, st[kb][r]);
         mt = e * c;
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    mt = max_xor32(mt);  // the row's other half is in lane l ^ 32
     // rescale only when a row maximum outgrows the stale one by 2^8
     if (__any(mt > m + kRescaleSlack)) {
         const float m_new = fmaxf(m, mt);
