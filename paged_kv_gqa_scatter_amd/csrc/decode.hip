@@ -434,7 +434,8 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
     // load round trip (about 12 tiles) plus the tiles each wave streams.  The
     // item count is a bound (each sequence adds at most one partial chunk).
     // Finer steps (any multiple of one tile per wave, or 1.5x powers of two)
-    // measured slower on multi-round launches (config 5: a chunk that is not
+    // measured slower on multi-round launches (256 sequences on a shared
+    // 4096-token prefix plus 16 of 32K tokens: a chunk that is not
     // a whole number of blocks also turns shared-chunk packing off).
     const int64_t slots = (int64_t)kPlanCus * wgs_per_cu;
     const int max_chunk = kMaxTilesPerWave * tile_keys * kDecodeWaves;
@@ -449,8 +450,9 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
         }
     }
     // a launch of one round: three quarters of that chunk, if the items
-    // still fit the round, shorten its longest item (config 2: 512 -> 384
-    // keys, 176 -> 216 items on 256 CUs; measured 15.0 -> 14.6 us)
+    // still fit the round, shorten its longest item (8 sequences of
+    // 512..2048 keys, 8 KV heads: 512 -> 384 keys, 176 -> 216 items on 256
+    // CUs; measured 15.0 -> 14.6 us)
     const int64_t items_at = ((total + chunk - 1) / chunk + num_seqs) * num_kv_heads;
     pl.last_first = items_at <= slots ? 1 : 0;
     if (items_at <= slots) {
