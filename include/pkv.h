@@ -107,10 +107,25 @@ int32_t pkv_kv_append(uint16_t* k_pool, uint16_t* v_pool,
  * Bytes of device workspace pkv_paged_gqa_decode needs.  total_kv_tokens is a
  * host-side upper bound on the sum of seq_lens (<= 0: num_seqs * max_seq_len
  * is assumed).  Returns 0 for unsupported shapes.  The workspace must be
- * zero-filled once, before the first decode call that uses it.
+ * zero-filled once (or reset with pkv_decode_workspace_reset), before the
+ * first decode call that uses it.
  */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t max_seq_len, int64_t total_kv_tokens);
+
+/*
+ * Zero the chunk counters at the start of a decode workspace (its first
+ * 16 KiB, the region every decode plan, bf16 or INT8, reserves for them).
+ * A workspace must hold zero counters when a decode call starts; every
+ * completed call leaves them so.  Use this on a workspace that was never
+ * zero-filled, or whose last call did not complete (an aborted stream, a
+ * launch that failed part-way): partials of such a call may otherwise be
+ * merged wrongly by the next one.  Enqueued on `stream` as a kernel (no
+ * memset node), so it may be captured in a graph.  Needs workspace_bytes >=
+ * 16 KiB (every decode workspace is larger); errors: PKV_ERR_NULL_POINTER,
+ * PKV_ERR_MISALIGNED (16-byte alignment), PKV_ERR_WORKSPACE, PKV_ERR_HIP.
+ */
+int32_t pkv_decode_workspace_reset(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * paged_gqa_decode: one query row per sequence attends to all seq_lens[s]

@@ -25,7 +25,8 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 STATUS = {0: "PKV_OK", 1: "PKV_ERR_NULL_POINTER", 2: "PKV_ERR_BAD_SHAPE", 3: "PKV_ERR_MISALIGNED",
           4: "PKV_ERR_WORKSPACE", 5: "PKV_ERR_HIP", 6: "PKV_ERR_NO_BLOCKS", 7: "PKV_ERR_UNKNOWN_SEQ"}
 EXPORTS = ("pkv_abi_version", "pkv_status_string", "pkv_kv_append", "pkv_decode_workspace_bytes",
-           "pkv_paged_gqa_decode", "pkv_paged_gqa_decode_append", "pkv_paged_gqa_prefill")
+           "pkv_decode_workspace_reset", "pkv_paged_gqa_decode", "pkv_paged_gqa_decode_append",
+           "pkv_paged_gqa_prefill")
 BLOCK_EXPORTS = ("pkv_bm_create", "pkv_bm_destroy", "pkv_bm_available", "pkv_bm_seq_len", "pkv_bm_append",
                  "pkv_bm_free_sequence", "pkv_bm_block_table", "pkv_bm_cache_prefix", "pkv_bm_fork",
                  "pkv_copy_blocks")
@@ -54,6 +55,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_kv_append.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P]
     lib.pkv_decode_workspace_bytes.restype = SZ
     lib.pkv_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I64]
+    lib.pkv_decode_workspace_reset.restype = I32
+    lib.pkv_decode_workspace_reset.argtypes = [P, SZ, P]
     lib.pkv_paged_gqa_decode.restype = I32
     lib.pkv_paged_gqa_decode.argtypes = [P, P, P, P, P, I32, P, I32, I64, I32, I32, I32, I32, I32, I32, F32, P, SZ, P]
     lib.pkv_paged_gqa_decode_append.restype = I32
@@ -170,6 +173,16 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, h
     if n == 0 and num_seqs > 0:
         raise PkvError(2, "decode_workspace_bytes")
     return int(n)
+
+
+def decode_workspace_reset(workspace) -> None:
+    """Zero the chunk counters of a decode workspace (uint8 CUDA tensor) on the
+    current stream: needed before the first use of a workspace that was not
+    zero-filled, or after a call on it that did not complete."""
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
+    _check(lib().pkv_decode_workspace_reset(workspace.data_ptr(), workspace.numel(), _stream()),
+           "decode_workspace_reset")
 
 
 def paged_gqa_decode(q, k_pool, v_pool, block_table, seq_lens, scale: float, *, max_seq_len: int,

@@ -12,12 +12,18 @@
 // block that is not cached; only the last block of a chain may be partial.
 // Blocks carry a reference count (sequences and cache entries holding them)
 // and a fill level; a sequence writes a block in place only at its frontier,
-// else it first gets a private copy (copy-on-write).
+// else it first gets a private copy (copy-on-write).  The count of blocks
+// only the cache holds is kept up to date, so available() is O(1), and the
+// cache entries that may be evicted are kept ordered by last use, so the
+// least recently used one is found in O(log n).
+#include <algorithm>
 #include <cstdint>
 #include <deque>
 #include <memory>
 #include <new>
+#include <set>
 #include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "../../include/pkv.h"
@@ -32,12 +38,15 @@ struct Entry {
     uint64_t key;
     int32_t children = 0;  // entries whose parent this is
     uint64_t last_use = 0;
+    bool in_lru = false;   // listed among the evictable entries, under lru_key
+    uint64_t lru_key = 0;
 };
 
 struct Block {
     int32_t ref = 0;     // sequences + cache entries holding the block
     int32_t cached = 0;  // cache entries among them
     int32_t fill = 0;    // slots [0, fill) hold K/V
+    std::vector<Entry*> owners;  // the cache entries holding the block
 };
 
 struct Sequence {
@@ -85,23 +94,62 @@ struct pkv_block_manager {
         return nullptr;
     }
 
+    // evictable entries (no child entry, no sequence holding the block) by last use
+    std::set<std::pair<uint64_t, Entry*>> lru;
+    int32_t cache_only = 0;  // blocks held by cache entries alone (ref > 0, ref == cached)
+
     bool evictable(const Entry* e) const {
         const Block& b = blocks[e->block];
         return e->children == 0 && b.ref == b.cached;
     }
 
-    int32_t available() const {
-        int32_t n = (int32_t)free_pool.size();
-        for (const Block& b : blocks)
-            if (b.ref > 0 && b.ref == b.cached) ++n;
-        return n;
+    // Put e in or out of the eviction order (and re-key it) after a change of
+    // its last use, its children or its block's holders.
+    void refresh(Entry* e) {
+        if (e->in_lru) {
+            lru.erase({e->lru_key, e});
+            e->in_lru = false;
+        }
+        if (evictable(e)) {
+            e->lru_key = e->last_use;
+            lru.insert({e->lru_key, e});
+            e->in_lru = true;
+        }
     }
 
-    void release(int32_t b) {
-        if (--blocks[b].ref == 0) {
+    // Change a block's holders (sequences via dref, cache entries via dcached
+    // as well), keeping the cache-only count and the eviction order current.
+    void hold(int32_t b, int32_t dref, int32_t dcached) {
+        Block& bl = blocks[b];
+        const bool was = bl.ref > 0 && bl.ref == bl.cached;
+        bl.ref += dref;
+        bl.cached += dcached;
+        const bool now = bl.ref > 0 && bl.ref == bl.cached;
+        cache_only += (int32_t)now - (int32_t)was;
+        if (was != now)
+            for (Entry* e : bl.owners) refresh(e);
+    }
+
+    int32_t available() const { return (int32_t)free_pool.size() + cache_only; }
+
+    // One holder less (a cache entry's too when dcached = -1); the block goes
+    // back to the free pool when nothing holds it.
+    void release(int32_t b, int32_t dcached = 0) {
+        hold(b, -1, dcached);
+        if (blocks[b].ref == 0) {
             blocks[b].fill = 0;
             free_pool.push_back(b);
         }
+    }
+
+    void add_entry(Entry* e) {
+        blocks[e->block].owners.push_back(e);
+        hold(e->block, 1, 1);
+        if (e->parent) {
+            ++e->parent->children;
+            refresh(e->parent);
+        }
+        refresh(e);
     }
 
     void evict(Entry* e) {
@@ -111,28 +159,29 @@ struct pkv_block_manager {
                 table.erase(it);
                 break;
             }
-        if (e->parent) --e->parent->children;
-        --blocks[e->block].cached;
-        release(e->block);
+        if (e->in_lru) lru.erase({e->lru_key, e});
+        e->in_lru = false;
+        if (e->parent) {
+            --e->parent->children;
+            refresh(e->parent);
+        }
+        std::vector<Entry*>& own = blocks[e->block].owners;
+        own.erase(std::find(own.begin(), own.end(), e));
+        release(e->block, -1);
         entries.erase(e);
     }
 
     // A block from the free pool, evicting least recently used cached chain
     // ends no sequence holds while the pool is empty.  The caller has checked
-    // available(), so this succeeds.
+    // available(), so this succeeds: a cache-only block's entries are evicted
+    // chain end first, and each eviction frees a block or makes its parent
+    // evictable.
     int32_t alloc() {
-        while (free_pool.empty()) {
-            Entry* victim = nullptr;
-            for (auto& kv : entries) {
-                Entry* e = kv.first;
-                if (evictable(e) && (!victim || e->last_use < victim->last_use)) victim = e;
-            }
-            evict(victim);
-        }
+        while (free_pool.empty() && !lru.empty()) evict(lru.begin()->second);
+        if (free_pool.empty()) return -1;  // unreachable when available() was checked
         const int32_t b = free_pool.front();
         free_pool.pop_front();
-        blocks[b].ref = 1;
-        blocks[b].cached = 0;
+        hold(b, 1, 0);
         blocks[b].fill = 0;
         return b;
     }
@@ -250,13 +299,13 @@ int32_t pkv_bm_cache_prefix(pkv_block_manager* bm, int64_t seq_id, const int32_t
             ne->tokens.assign(t, t + n);
             ne->key = chain_key(parent ? parent->key : kRootKey, t, n);
             e = ne.get();
+            e->last_use = now;
             bm->entries.emplace(e, std::move(ne));
             bm->table.emplace(e->key, e);
-            ++bm->blocks[e->block].ref;
-            ++bm->blocks[e->block].cached;
-            if (parent) ++parent->children;
+            bm->add_entry(e);
         }
         e->last_use = now;
+        bm->refresh(e);
         parent = e;
     }
     return PKV_OK;
@@ -276,6 +325,7 @@ int32_t pkv_bm_fork(pkv_block_manager* bm, int64_t new_seq_id, const int32_t* to
         Entry* e = bm->find(parent, tokens + m, B);
         if (!e) break;
         e->last_use = now;
+        bm->refresh(e);
         s.blocks.push_back(e->block);
         parent = e;
         m += B;
@@ -285,12 +335,13 @@ int32_t pkv_bm_fork(pkv_block_manager* bm, int64_t new_seq_id, const int32_t* to
         Entry* e = bm->find(parent, tokens + m, r);
         if (e) {
             e->last_use = now;
+            bm->refresh(e);
             s.blocks.push_back(e->block);
             m += r;
             break;
         }
     }
-    for (int32_t b : s.blocks) ++bm->blocks[b].ref;
+    for (int32_t b : s.blocks) bm->hold(b, 1, 0);
     s.len = m;
     bm->seqs.emplace(new_seq_id, std::move(s));
     *matched = m;

@@ -321,8 +321,9 @@ __device__ __forceinline__ ItemInputs<D> load_item_inputs(const DecodeKernelArgs
     const int32_t* table = a.block_table + (int64_t)s * a.max_blocks_per_seq;
     const int k0 = c * p.chunk;
     const int last = a.max_blocks_per_seq - 1;
-    in.ids0 = table[min((k0 + kTileKeys * (wave + kDecodeWaves * lane)) >> p.log2_block, last)];
-    in.ids1 = p.chunk > kTileKeys * kDecodeWaves * kWave
+    // (an empty table row, possible only when every sequence is empty, is not read)
+    in.ids0 = last >= 0 ? table[min((k0 + kTileKeys * (wave + kDecodeWaves * lane)) >> p.log2_block, last)] : -1;
+    in.ids1 = last >= 0 && p.chunk > kTileKeys * kDecodeWaves * kWave
                   ? table[min((k0 + kTileKeys * (wave + kDecodeWaves * (lane + kWave))) >> p.log2_block, last)]
                   : 0;
     in.kn = in.vn = zero;
@@ -463,7 +464,9 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
     pl.ring = 4;
     pl.chunk = chunk;
     pl.items = ((total + chunk - 1) / chunk + num_seqs) * num_kv_heads;
-    pl.max_chunks = (max_seq_len + chunk - 1) / chunk;
+    // at least one chunk: a launch whose sequences are all empty still runs
+    // chunk 0 of each, which writes its zero rows
+    pl.max_chunks = max_seq_len > 0 ? (max_seq_len + chunk - 1) / chunk : 1;
     const int64_t direct_items = (int64_t)num_seqs * pl.max_chunks;
     const int64_t real_items = (total + chunk - 1) / chunk + num_seqs;  // bound on chunks actually present
     // a direct grid when its empty workgroups are few (or the launch is small)
@@ -497,6 +500,21 @@ DecodePlan plan_decode_bf16(int32_t num_seqs, int32_t num_q_heads, int32_t num_k
         pl.ring = 2;
     }
     return pl;
+}
+
+namespace {
+
+__global__ __launch_bounds__(256) void zero_counters_kernel(u32x4* p) {
+    p[blockIdx.x * 256 + threadIdx.x] = u32x4{0u, 0u, 0u, 0u};
+}
+
+}  // namespace
+
+hipError_t launch_workspace_reset(void* workspace, hipStream_t stream) {
+    static_assert(kCounterBytes % (256 * 16) == 0, "whole workgroups of 16-byte stores");
+    hipLaunchKernelGGL(zero_counters_kernel, dim3(kCounterBytes / (256 * 16)), dim3(256), 0, stream,
+                       static_cast<u32x4*>(workspace));
+    return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t stream) {

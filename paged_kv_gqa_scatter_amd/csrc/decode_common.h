@@ -12,14 +12,31 @@
 //    the low bits of the workgroup index, so items of one KV head run on one
 //    XCD (workgroups are dealt round-robin over the 8 XCDs) and K/V rows
 //    shared between sequences (a common prefix) are re-read from that XCD's L2.
-//  * Chunks of a sequence write a normalised partial and its log2-sum-exp; a
-//    second kernel merges them in one pass with a running maximum
-//    (out = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M)).  The hand-off goes
-//    through a kernel boundary on purpose: the L2 is per XCD, so a device-scope
-//    fence inside the kernel would write back and invalidate an XCD's whole
-//    L2 under every other workgroup's streaming loads.  A sequence with one
-//    chunk is written directly (and the merge kernel is not launched when no
-//    sequence can have two); a sequence with no keys gets zeros.
+//  * Chunks of a sequence write a normalised partial and its log2-sum-exp,
+//    merged in one pass with a running maximum
+//    (out = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M)).  In a direct grid
+//    without packing (small launches) the merge happens inside the split
+//    kernel: each chunk stores its partial with agent-scope atomic stores,
+//    waits for them to complete, then counts itself in with an agent-scope
+//    atomic add, and the chunk that sees the count reach n - 1 loads all
+//    partials with agent-scope atomic loads and merges them.  Otherwise (the
+//    persistent grid, packed launches) a second kernel merges after a kernel
+//    boundary.  A sequence with one chunk is written directly (and the merge
+//    kernel is not launched when no sequence can have two); a sequence with
+//    no keys gets zeros.
+//  * Why the in-kernel hand-off needs no L2 write-back or invalidate: the L2
+//    is per XCD and not coherent across XCDs, and the LLVM AMDGPU memory
+//    model for this target family (GFX942 and later) makes an agent-scope
+//    release "buffer_wbl2 sc1; s_waitcnt vmcnt(0)" and an agent-scope acquire
+//    "buffer_inv sc1" -- whole-L2 operations that exist for data moved by
+//    non-atomic accesses, which may sit dirty or stale in the L2.  Agent-scope
+//    atomic loads, stores and read-modify-writes are themselves coherent at
+//    agent scope (the model issues them with sc1, past the XCD's L2), so when
+//    every value handed between workgroups is such an access the only part of
+//    the release that still matters is the wait for the partial stores to
+//    complete before the counter add (vmcnt(0)), and the acquire reduces to
+//    issuing the partial loads after the add has returned.  Measured on the
+//    8-sequence decode step: with the full fences 18.6 us, without 15.0 us.
 #pragma once
 
 #include <math.h>

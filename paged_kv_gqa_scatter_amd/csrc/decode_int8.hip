@@ -16,9 +16,12 @@
 //  * Codes become bf16 MFMA operands exactly (|code| <= 127): a signed byte
 //    to fp32 conversion per code and one pack per two.  The scales stay off
 //    the matrix cores: S^T = (K_codes Q^T) times each key's k_scale, and each
-//    key's v_scale multiplies its softmax weight before the bf16 rounding
-//    (P' = P v_scale), so that O^T = V_codes^T P'^T.  The running sum adds
-//    the unscaled weights.
+//    key's v_scale multiplies its softmax weight (P' = P v_scale), so that
+//    O^T = V_codes^T P'^T.  P' goes to the matrix cores as two bf16 parts,
+//    hi = bf16(P') and lo = bf16(P' - hi), one MFMA each, so the weights keep
+//    16 significant bits and the running sum, which adds the unscaled
+//    weights, divides the same weights out: the output is a convex
+//    combination of the dequantised rows.
 //  * S^T of each 16-key half: v_mfma_f32_16x16x32_bf16, lane (key i, group j)
 //    holding dims [j D/4, (j + 1) D/4) of its key row (the Q fragments follow
 //    the same dim order).  The 8 weights a lane then holds (keys 4j..4j+3 of
@@ -292,12 +295,27 @@ __device__ __forceinline__ void tile_step8(const Int8WaveItem<D>& w, int t, Wave
 #pragma unroll
     for (int i = 0; i < 8; ++i) p[i] = fast_exp2(z[i] - mref);
     ws.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-    const u32x4 pk = {pack_bf16x2(p[0] * vs[0], p[1] * vs[1]), pack_bf16x2(p[2] * vs[2], p[3] * vs[3]),
-                      pack_bf16x2(p[4] * vs[4], p[5] * vs[5]), pack_bf16x2(p[6] * vs[6], p[7] * vs[7])};
+    // the numerator weights p * v_scale as a bf16 pair hi + lo (16 significant
+    // bits): the output is sum_j p_j (v_scale_j code_j) / sum_j p_j to about
+    // 2^-17 relative, a convex combination of the dequantised rows, so a
+    // one-key row returns code * v_scale rounded once
+    float wt[8];
+    uint32_t hi[4], lo[4];
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-        ws.acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_8(codes_to_bf16(vc[db][0], vc[db][1])),
-                                                             as_bf16x8_8(pk), ws.acc[db], 0, 0, 0);
+    for (int i = 0; i < 8; ++i) wt[i] = p[i] * vs[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = pack_bf16x2(wt[2 * i], wt[2 * i + 1]);
+        lo[i] = pack_bf16x2(wt[2 * i] - bf16_lo(hi[i]), wt[2 * i + 1] - bf16_hi(hi[i]));
+    }
+    const u32x4 pk_hi = {hi[0], hi[1], hi[2], hi[3]};
+    const u32x4 pk_lo = {lo[0], lo[1], lo[2], lo[3]};
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+        const bf16x8 vcb = as_bf16x8_8(codes_to_bf16(vc[db][0], vc[db][1]));
+        ws.acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vcb, as_bf16x8_8(pk_hi), ws.acc[db], 0, 0, 0);
+        ws.acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vcb, as_bf16x8_8(pk_lo), ws.acc[db], 0, 0, 0);
+    }
     // the stage's reads have returned (the MFMAs hold them): refill it with tile t + R
     if (t + R < w.n_tiles) {
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
@@ -346,8 +364,9 @@ __device__ __forceinline__ Int8Inputs<D> load_int8_inputs(const DecodeKernelArgs
     const int32_t* table = a.block_table + (int64_t)s * a.max_blocks_per_seq;
     const int k0 = c * p.chunk;
     const int last = a.max_blocks_per_seq - 1;
-    in.ids0 = table[min((k0 + kTile8 * (wave + kDecodeWaves * lane)) >> p.log2_block, last)];
-    in.ids1 = p.chunk > kTile8 * kDecodeWaves * kWave
+    // (an empty table row, possible only when every sequence is empty, is not read)
+    in.ids0 = last >= 0 ? table[min((k0 + kTile8 * (wave + kDecodeWaves * lane)) >> p.log2_block, last)] : -1;
+    in.ids1 = last >= 0 && p.chunk > kTile8 * kDecodeWaves * kWave
                   ? table[min((k0 + kTile8 * (wave + kDecodeWaves * (lane + kWave))) >> p.log2_block, last)]
                   : 0;
     in.kn = in.vn = zero;

@@ -179,6 +179,13 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
     return plan_decode_bf16(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, total_kv_tokens).bytes;
 }
 
+int32_t pkv_decode_workspace_reset(void* workspace, size_t workspace_bytes, void* stream) {
+    if (!workspace) return PKV_ERR_NULL_POINTER;
+    if (!aligned16(workspace)) return PKV_ERR_MISALIGNED;
+    if (workspace_bytes < kCounterBytes) return PKV_ERR_WORKSPACE;
+    return hip_status(launch_workspace_reset(workspace, static_cast<hipStream_t>(stream)));
+}
+
 size_t pkv_decode_int8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t max_seq_len, int64_t total_kv_tokens) {
     if (num_seqs < 0 || num_seqs > kMaxDecodeSeqs || max_seq_len < 0) return 0;

@@ -46,48 +46,6 @@ __device__ __forceinline__ float max_xor32(float v) {
     return fmaxf(__builtin_bit_cast(float, (unsigned)sw[0]), __builtin_bit_cast(float, (unsigned)sw[1]));
 }
 
-// DPP lane moves inside a row of 16 lanes (v_mov_b32_dpp).  Each control is
-// a permutation of the row: quad xor 1, quad xor 2, xor 7 within 8 lanes
-// (half-row mirror), xor 15 within 16 (row mirror), and broadcast of lane n.
-enum : int {
-    kDppXor1 = 0xB1,       // quad_perm [1,0,3,2]
-    kDppXor2 = 0x4E,       // quad_perm [2,3,0,1]
-    kDppHalfMirror = 0x141,
-    kDppMirror = 0x140,
-    kDppRowRor8 = 0x128,     // xor 8 within 16
-    kDppRowBcast15 = 0x142,  // lane 15 of each row -> the next row (scans)
-    kDppRowBcast31 = 0x143,  // lane 31 -> rows 2 and 3 (scans)
-    kDppRowBcast0 = 0x150    // + n: row_newbcast:n
-};
-
-template <int kCtrl>
-__device__ __forceinline__ float dpp(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
-}
-
-// DPP move of v into the rows enabled by kRowMask; other rows get `old`.
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ float dpp_rows(float old, float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
-                                                                  kCtrl, kRowMask, 0xF, false));
-}
-
-__device__ __forceinline__ float readlane(float v, int lane) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
-}
-
-// Round to bf16 (nearest even) and back.
-__device__ __forceinline__ float round_bf16(float x) { return (float)(__bf16)x; }
-
-// Lane-crossing reductions over groups of lanes.  `width` lanes with
-// consecutive ids form a group; the xor partner stays inside the group.
-template <int kWidth>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int off = kWidth / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-    return v;
-}
-
 // Symmetric INT8 quantisation of one row held by `kPieces` consecutive lanes
 // (an aligned group), 8 bf16 values each ("从零搭建AI工程能力：手写KV Cache与
 // 动态批处理实战" section 3.2 keeps the cache in INT8; the scheme is this

@@ -170,6 +170,9 @@ struct CopyBlocksArgs {
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
+// Zero the chunk counters at the start of a decode workspace (a kernel, so
+// that the call may sit in a captured graph).
+hipError_t launch_workspace_reset(void* workspace, hipStream_t stream);
 hipError_t launch_decode_int8(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_qkv_append(const QkvArgs& a, hipStream_t stream);

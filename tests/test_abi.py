@@ -119,6 +119,16 @@ def test_decode_workspace_bytes(lib):
     assert all(f(S, 4, 1, 64, L, 0) > 16384 for S in (1, 8) for L in (1, 300))
 
 
+def test_decode_workspace_reset_rejects(lib):
+    # the reset validates on the host and launches nothing when it rejects
+    f = lib.pkv_decode_workspace_reset
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert f(None, 1 << 20, None) == 1
+    assert f(A16 + 4, 1 << 20, None) == 3
+    assert f(A16, 16383, None) == 4
+    assert f(A16, 0, None) == 4
+
+
 def decode_append_args(**kw):
     a = dict(out=A16, q=A16, kn=A16, vn=A16, kp=A16, vp=A16, table=A16, mbs=9, lens=A16, maxlen=2049, total=0, S=8,
              hq=32, hkv=8, d=128, bs=256, nb=90, scale=0.088, ws=A16, wsb=1 << 30, stream=None)

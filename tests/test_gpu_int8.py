@@ -3,10 +3,12 @@
 kv_append_int8 must match the oracle's quantiser bit for bit over the whole
 cache (codes and fp32 scales; unwritten slots keep their sentinels).  Decode
 over the INT8 cache is compared with the oracle's decode over the same INT8
-cache at the attention bar of the bf16 path (max|err| <= 1e-2 or within one
-bf16 ulp, rel-L2 <= 1e-2): both read identical codes and scales, so the
-remaining difference is the kernel's own rounding (bf16 weights times the
-value scales, fp32 accumulation).  The quantisation error itself is checked
+cache at the attention bar of the bf16 path (max|err| <= 1e-2, rel-L2 <=
+1e-2; at |ref| >= 4 a bf16 neighbour of the exact value): both read identical
+codes and scales, so the remaining difference is the kernel's own rounding --
+fp32 scores and weights, the weight times the value scale carried as a bf16
+pair (16 significant bits), fp32 accumulation and one bf16 rounding of the
+output, which is where nearly all of the difference comes from.  The quantisation error itself is checked
 separately: the oracle's INT8 decode must stay within the closed-form bound
 of the oracle's bf16 decode of the unquantised rows.
 """
@@ -133,9 +135,10 @@ def test_int8_decode_edge_lengths(orc, d, bs, hq, hkv):
 
 
 @pytest.mark.timeout(900)
-def test_int8_decode_config5_sampled(orc):
+def test_int8_decode_config5_full(orc):
+    # all 272 sequences, every head, and the whole INT8 cache bit for bit
     case = W.config5_prefix_long()
-    _say(f"case {case.name}: INT8 cache, sampled sequences")
+    _say(f"case {case.name}: INT8 cache, every sequence")
     dc = _dev()(case)
     out = dc.run_all()[0]["decode"]
     got = dc.pools_numpy()
@@ -145,12 +148,8 @@ def test_int8_decode_config5_sampled(orc):
     _assert_cache_equal(got, pools, case.name)
     del got
     d = case.steps[0].decode
-    S = d.seq_lens.shape[0]
-    pick = sorted(set(np.random.default_rng(56).choice(256, 12, replace=False).tolist()) | {0, 255, 256, 263, S - 1})
-    items = np.array([(s, 0, h) for s in pick for h in range(case.num_q_heads)], np.int32)
-    cu = np.arange(S + 1, dtype=np.int32)
-    ref = orc.attention_rows_int8(items, d.q, cu, *pools, d.block_table, d.seq_lens, case.num_q_heads, case.scale)
-    compare(out[items[:, 0], items[:, 2]], ref, f"INT8 decode {len(pick)} sequences x all heads")
+    ref = orc.decode_int8(d.q, *pools, d.block_table, d.seq_lens, case.scale)
+    compare(out, ref, f"INT8 decode {d.seq_lens.shape[0]} sequences x all heads")
 
 
 def test_int8_quantisation_error_within_bound(orc):

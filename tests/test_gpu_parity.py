@@ -136,7 +136,18 @@ def _prefill_sample_items(batch, rng, n_random=384):
     return np.array(items, np.int32)
 
 
+def test_config3_prefill_full(orc):
+    # every (row, head) output of the four prompts against the oracle
+    case = W.config3_prefill()
+    _say(f"case {case.name}: every output")
+    outs = _dev()(case).run_all()
+    ref, _ = oracle_outputs(case, orc)
+    p = case.steps[0].prefill
+    compare(outs[0]["prefill"], ref[0]["prefill"], f"prefill {p.q.shape[0]} rows x {case.num_q_heads} heads")
+
+
 def test_config3_prefill_sampled(orc):
+    # tile edges and random rows: a quick look at the same launch
     case = W.config3_prefill()
     _say(f"case {case.name}: sampled rows")
     outs = _dev()(case).run_all()
@@ -170,9 +181,10 @@ def test_config4_mixed(orc):
 
 
 @pytest.mark.timeout(900)
-def test_config5_prefix_long_sampled(orc):
+def test_config5_prefix_long_full(orc):
+    # all 272 sequences (256 on the shared prefix, 16 of 32769 keys), every head
     case = W.config5_prefix_long()
-    _say(f"case {case.name}: sampled sequences")
+    _say(f"case {case.name}: every sequence")
     dc = _dev()(case)
     out = dc.run_all()[0]["decode"]
     gk, gv = dc.pools_numpy()
@@ -182,13 +194,8 @@ def test_config5_prefix_long_sampled(orc):
     assert np.array_equal(gk, K) and np.array_equal(gv, V), "pools differ"
     del gk, gv
     d = case.steps[0].decode
-    S = d.seq_lens.shape[0]
-    pick = sorted(set(np.random.default_rng(55).choice(256, 12, replace=False).tolist()) | {0, 255, 256, 263, S - 1})
-    items = np.array([(s, 0, h) for s in pick for h in range(case.num_q_heads)], np.int32)
-    cu = np.arange(S + 1, dtype=np.int32)
-    ref = orc.attention_rows(items, d.q, cu, K, V, d.block_table, d.seq_lens, case.num_q_heads, case.scale)
-    gpu = out[items[:, 0], items[:, 2]]
-    compare(gpu, ref, f"decode {len(pick)} sequences x all heads")
+    ref = orc.decode(d.q, K, V, d.block_table, d.seq_lens, case.scale)
+    compare(out, ref, f"decode {d.seq_lens.shape[0]} sequences x all heads")
 
 
 # ---------------------------------------------------------------- edge cases
@@ -567,3 +574,71 @@ def test_decode_workspace_shared_across_shapes_and_formats():
     pick = [0, 7, 150, 299]
     ref = orc.decode(d.q[pick], K, V, np.ascontiguousarray(d.block_table[pick]), d.seq_lens[pick], cp.scale)
     compare(_f64(dp.steps[0]["decode"].out)[pick], ref, "persistent decode on the shared workspace")
+
+
+def test_decode_all_sequences_empty():
+    # every sequence empty (max_seq_len 0): each output row must be zero, and
+    # the _append variants must leave the caches alone (no sequence has a row
+    # to append); with max_blocks_per_seq 0 the (empty) table row is not read
+    import ctypes
+    import paged_kv_gqa_scatter_amd as pkv
+    S, Hq, Hkv, D, B, NB = 5, 8, 2, 128, 32, 3
+    dev = "cuda"
+    rng = np.random.default_rng(5)
+    q = torch.from_numpy(W.bf16_normal(rng, (S, Hq, D)).view(np.int16)).to(dev)
+    kn = torch.from_numpy(W.bf16_normal(rng, (S, Hkv, D)).view(np.int16)).to(dev)
+    vn = torch.from_numpy(W.bf16_normal(rng, (S, Hkv, D)).view(np.int16)).to(dev)
+    kp = torch.full((NB, Hkv, B, D), W.NAN_SENTINEL, dtype=torch.int32).to(torch.int16).to(dev)
+    vp = kp.clone()
+    codes = [torch.full((NB, Hkv, B, D), -128, dtype=torch.int8, device=dev) for _ in range(2)]
+    scales = [torch.full((NB, Hkv, B), float("nan"), device=dev) for _ in range(2)]
+    table = torch.full((S, 1), -1, dtype=torch.int32, device=dev)
+    lens = torch.zeros(S, dtype=torch.int32, device=dev)
+    nan_rows = lambda: torch.full((S, Hq, D), W.NAN_SENTINEL, dtype=torch.int32).to(torch.int16).to(dev)
+    k0, v0 = kp.clone(), vp.clone()
+    outs = {}
+    outs["decode"] = pkv.paged_gqa_decode(q, kp, vp, table, lens, 0.088, max_seq_len=0, out=nan_rows())
+    outs["decode_append"] = pkv.paged_gqa_decode_append(q, kn, vn, kp, vp, table, lens, 0.088, max_seq_len=0,
+                                                        out=nan_rows())
+    outs["decode_int8"] = pkv.paged_gqa_decode_int8(q, *codes, *scales, table, lens, 0.088, max_seq_len=0,
+                                                    out=nan_rows())
+    outs["decode_append_int8"] = pkv.paged_gqa_decode_append_int8(q, kn, vn, *codes, *scales, table, lens, 0.088,
+                                                                  max_seq_len=0, out=nan_rows())
+    # max_blocks_per_seq 0, straight through the C ABI (the table pointer is
+    # valid but holds no row)
+    out0 = nan_rows()
+    ws = torch.zeros(pkv.decode_workspace_bytes(S, Hq, Hkv, D, 0), dtype=torch.uint8, device=dev)
+    st = pkv.lib().pkv_paged_gqa_decode(out0.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(),
+                                        table.data_ptr(), 0, lens.data_ptr(), 0, 0, S, Hq, Hkv, D, B, NB,
+                                        ctypes.c_float(0.088), ws.data_ptr(), ws.numel(),
+                                        torch.cuda.current_stream().cuda_stream)
+    assert st == 0, pkv.lib().pkv_status_string(st)
+    outs["decode, max_blocks_per_seq 0"] = out0
+    torch.cuda.synchronize()
+    for name, o in outs.items():
+        assert int(torch.count_nonzero(o.view(torch.int16))) == 0, f"{name}: rows of empty sequences not zero"
+        _say(f"  {name}: all {S} rows zero")
+    assert torch.equal(kp, k0) and torch.equal(vp, v0), "decode_append wrote a row for an empty sequence"
+    assert bool((codes[0] == -128).all()) and bool(torch.isnan(scales[0]).all()), "INT8 append wrote a row"
+
+
+def test_decode_workspace_reset():
+    # a workspace whose chunk counters hold garbage (never zero-filled, or left
+    # by an interrupted call) is made usable again by
+    # pkv_decode_workspace_reset, a kernel (so it may be captured in a graph)
+    import paged_kv_gqa_scatter_amd as pkv
+    c2 = W.config2_decode()
+    d2 = _dev()(c2)
+    d2.run_fills()
+    d2.append(d2.steps[0]["append"])
+    dd = d2.steps[0]["decode"]
+    good = d2.decode(dd).clone()
+    ws = torch.randint(0, 255, (dd.workspace.numel(),), dtype=torch.uint8, device="cuda")
+    pkv.decode_workspace_reset(ws)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(ws[:16384])) == 0, "counters not cleared"
+    dd.workspace = ws
+    out = d2.decode(dd).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), good.view(torch.int16)), "decode on the reset workspace differs"
+    assert int(torch.count_nonzero(ws[:16384])) == 0, "counters left non-zero"
