@@ -66,7 +66,8 @@ enum {
     PKV_ERR_BAD_SHAPE = 2,    /* sizes negative, inconsistent or unsupported      */
     PKV_ERR_MISALIGNED = 3,   /* a tensor pointer is not 16-byte aligned          */
     PKV_ERR_WORKSPACE = 4,    /* decode workspace missing or too small            */
-    PKV_ERR_HIP = 5           /* a kernel launch failed                           */
+    PKV_ERR_HIP = 5,          /* a kernel launch failed                           */
+    PKV_ERR_SCRATCH_LIMIT = 8 /* the call needs more than the static decode scratch */
 };
 
 /* Returns PKV_ABI_VERSION. */
@@ -189,6 +190,36 @@ int32_t pkv_paged_gqa_decode_append(uint16_t* out, const uint16_t* q,
                                     int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                     float scale, void* workspace, size_t workspace_bytes,
                                     void* stream);
+
+/*
+ * paged_gqa_decode_append_static: pkv_paged_gqa_decode_append without a
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The same kernels run on the library's own scratch: a static 32 MiB array
+ * on each GPU the library is used on, held until the process ends.  Nothing
+ * is allocated or freed, here or by the caller's runtime.
+ *
+ *   arguments        as for pkv_paged_gqa_decode_append, minus workspace
+ *
+ * Returns PKV_ERR_SCRATCH_LIMIT, launching nothing, when the call's plan
+ * needs more than 32 MiB (pkv_decode_workspace_bytes(...) > 32 MiB: e.g.
+ * more than about 1900 (sequence, split) partials at 32 query heads and
+ * head_dim 128); other errors as for pkv_paged_gqa_decode_append.  The first
+ * call on a device zeroes the scratch's chunk counters with a kernel on
+ * `stream`.  Every call on one GPU shares that GPU's scratch, which keeps the
+ * last call's contents: calls that overlap on one GPU (different streams,
+ * or host threads without ordering) race and must not be issued; calls on
+ * one stream are ordered and safe.  A call that does not complete leaves the
+ * scratch's counters undefined for the rest of the process.
+ */
+int32_t pkv_paged_gqa_decode_append_static(uint16_t* out, const uint16_t* q,
+                                           const uint16_t* k_new, const uint16_t* v_new,
+                                           uint16_t* k_pool, uint16_t* v_pool,
+                                           const int32_t* block_table, int32_t max_blocks_per_seq,
+                                           const int32_t* seq_lens, int32_t max_seq_len, int64_t total_kv_tokens,
+                                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                           float scale, void* stream);
 
 /*
  * paged_gqa_prefill: causal attention for a chunk of q_len_s query rows per

@@ -23,10 +23,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 STATUS = {0: "PKV_OK", 1: "PKV_ERR_NULL_POINTER", 2: "PKV_ERR_BAD_SHAPE", 3: "PKV_ERR_MISALIGNED",
-          4: "PKV_ERR_WORKSPACE", 5: "PKV_ERR_HIP", 6: "PKV_ERR_NO_BLOCKS", 7: "PKV_ERR_UNKNOWN_SEQ"}
+          4: "PKV_ERR_WORKSPACE", 5: "PKV_ERR_HIP", 6: "PKV_ERR_NO_BLOCKS", 7: "PKV_ERR_UNKNOWN_SEQ",
+          8: "PKV_ERR_SCRATCH_LIMIT"}
 EXPORTS = ("pkv_abi_version", "pkv_status_string", "pkv_kv_append", "pkv_decode_workspace_bytes",
            "pkv_decode_workspace_reset", "pkv_paged_gqa_decode", "pkv_paged_gqa_decode_append",
-           "pkv_paged_gqa_prefill")
+           "pkv_paged_gqa_decode_append_static", "pkv_paged_gqa_prefill")
 BLOCK_EXPORTS = ("pkv_bm_create", "pkv_bm_destroy", "pkv_bm_available", "pkv_bm_seq_len", "pkv_bm_append",
                  "pkv_bm_free_sequence", "pkv_bm_block_table", "pkv_bm_cache_prefix", "pkv_bm_fork",
                  "pkv_copy_blocks")
@@ -62,6 +63,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_paged_gqa_decode_append.restype = I32
     lib.pkv_paged_gqa_decode_append.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I64, I32, I32, I32, I32, I32, I32,
                                                 F32, P, SZ, P]
+    lib.pkv_paged_gqa_decode_append_static.restype = I32
+    lib.pkv_paged_gqa_decode_append_static.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I64, I32, I32, I32, I32,
+                                                       I32, I32, F32, P]
     lib.pkv_bm_create.restype = P
     lib.pkv_bm_create.argtypes = [I32, I32]
     lib.pkv_bm_destroy.restype = None

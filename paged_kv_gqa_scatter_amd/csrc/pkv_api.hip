@@ -67,6 +67,7 @@ const char* pkv_status_string(int32_t status) {
         case PKV_ERR_HIP: return "a kernel launch failed";
         case PKV_ERR_NO_BLOCKS: return "not enough free or evictable KV blocks";
         case PKV_ERR_UNKNOWN_SEQ: return "no sequence with that id";
+        case PKV_ERR_SCRATCH_LIMIT: return "the call needs more decode scratch than the library's static 32 MiB";
         default: return "unknown status";
     }
 }
@@ -255,6 +256,68 @@ int32_t pkv_paged_gqa_decode_append(uint16_t* out, const uint16_t* q, const uint
     if (!k_new || !v_new) return PKV_ERR_NULL_POINTER;
     if (!aligned16(k_new) || !aligned16(v_new)) return PKV_ERR_MISALIGNED;
     return hip_status(launch_decode(a, pl, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// The decode scratch of pkv_paged_gqa_decode_append_static: one array per
+// GPU the library runs on (each holds its own copy), kept until the process
+// ends.  In host code `scratch` names a host-side stand-in, never the device
+// memory: its device address comes from hipGetSymbolAddress, once per device,
+// and only that address is handed to kernels.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex scratch_mu;
+std::vector<void*> scratch_ptr;  // per device: the device address of `scratch`
+
+// The current device's scratch address; on the first call on a device its
+// chunk counters are zeroed by a kernel on `stream` (before anything else
+// that stream runs on the scratch).
+int32_t device_scratch(void** ptr, hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return PKV_ERR_HIP;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if ((int)scratch_ptr.size() <= dev) scratch_ptr.resize(dev + 1, nullptr);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PKV_ERR_HIP;
+        if (launch_workspace_reset(p, stream) != hipSuccess) return PKV_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *ptr = scratch_ptr[dev];
+    return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pkv_paged_gqa_decode_append_static(uint16_t* out, const uint16_t* q, const uint16_t* k_new,
+                                           const uint16_t* v_new, uint16_t* k_pool, uint16_t* v_pool,
+                                           const int32_t* block_table, int32_t max_blocks_per_seq,
+                                           const int32_t* seq_lens, int32_t max_seq_len, int64_t total_kv_tokens,
+                                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                                           void* stream) {
+    // validate everything with a stand-in address (aligned, never touched) so
+    // that a rejected call launches nothing, not even the first-call clear
+    void* const stand_in = reinterpret_cast<void*>(uintptr_t(256));
+    DecodeArgs a{out, q, k_pool, v_pool, block_table, max_blocks_per_seq, seq_lens, max_seq_len, total_kv_tokens,
+                 num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, stand_in,
+                 kScratchBytes, k_new, v_new, k_pool, v_pool};
+    DecodePlan pl{};
+    const int32_t st = check_decode(a, pl, k_pool, v_pool, kDecodeTileKeys);
+    if (st == PKV_ERR_WORKSPACE) return PKV_ERR_SCRATCH_LIMIT;
+    if (st != PKV_OK || num_seqs == 0) return st;
+    if (!k_new || !v_new) return PKV_ERR_NULL_POINTER;
+    if (!aligned16(k_new) || !aligned16(v_new)) return PKV_ERR_MISALIGNED;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int32_t sst = device_scratch(&a.workspace, s);
+    if (sst != PKV_OK) return sst;
+    return hip_status(launch_decode(a, pl, s));
 }
 
 int32_t pkv_paged_gqa_decode_int8(uint16_t* out, const uint16_t* q, const int8_t* k_codes, const int8_t* v_codes,

@@ -56,7 +56,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.pkv_abi_version() == 1
-    for code in range(8):
+    for code in range(9):
         assert lib.pkv_status_string(code)
     assert lib.pkv_status_string(99) == b"unknown status"
 
@@ -256,3 +256,26 @@ def test_decode_append_int8_rejects(lib):
     assert f(*args(vn=A16 + 2)) == 3
     assert f(*args(ws=None)) == 4
     assert f(*args(S=0)) == 0
+
+
+def test_decode_append_static_rejects(lib):
+    # the static-scratch step validates on the host and launches nothing when
+    # it rejects; a plan beyond the 32 MiB scratch gets its own status
+    f = lib.pkv_paged_gqa_decode_append_static
+    f.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64] + \
+        [ctypes.c_int32] * 6 + [ctypes.c_float, ctypes.c_void_p]
+    ok = lambda **kw: dict(dict(out=A16, q=A16, kn=A16, vn=A16, kp=A16, vp=A16, table=A16, mbs=9, lens=A16,
+                                maxlen=2049, total=0, S=8, hq=32, hkv=8, d=128, bs=256, nb=90, scale=0.088,
+                                stream=None), **kw)
+    args = lambda a: tuple(a[k] for k in ("out", "q", "kn", "vn", "kp", "vp", "table", "mbs", "lens", "maxlen",
+                                          "total", "S", "hq", "hkv", "d", "bs", "nb", "scale", "stream"))
+    assert f(*args(ok(hq=30))) == 2
+    assert f(*args(ok(q=None))) == 1
+    assert f(*args(ok(kn=None))) == 1
+    assert f(*args(ok(vn=A16 + 2))) == 3
+    assert f(*args(ok(S=0))) == 0
+    big = ok(S=8192, mbs=256, maxlen=65536, nb=100000)
+    assert lib.pkv_decode_workspace_bytes(8192, 32, 8, 128, 65536, 0) > 32 << 20
+    assert f(*args(big)) == 8
+    assert lib.pkv_status_string(8) == b"the call needs more decode scratch than the library's static 32 MiB"
+
