@@ -642,3 +642,40 @@ def test_decode_workspace_reset():
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), good.view(torch.int16)), "decode on the reset workspace differs"
     assert int(torch.count_nonzero(ws[:16384])) == 0, "counters left non-zero"
+
+
+@pytest.mark.parametrize("d,bs,hq,hkv,lens", [
+    (128, 256, 32, 8, [1800, 0, 3, 16, 17, 255, 257, 4000]),            # an empty sequence mid-batch
+    (64, 64, 8, 1, list(np.random.default_rng(71).integers(1, 600, 32))),  # 32 sequences, the most one round takes
+    (128, 64, 16, 2, [20000]),                                         # one sequence cut into ~125 chunks
+    (128, 128, 32, 4, list(np.random.default_rng(72).integers(1, 3000, 12))),
+    (64, 32, 16, 2, [1, 2, 5, 33, 64, 65]),                            # shorter than a tile per wave
+])
+def test_decode_few_sequences(orc, d, bs, hq, hkv, lens):
+    # few sequences of mixed lengths (an empty one among them, a single long
+    # one, lengths shorter than a tile per wave): decode_append, pools bit
+    # for bit and outputs against the oracle
+    import paged_kv_gqa_scatter_amd as pkv
+    lens = [int(x) for x in lens]
+    live = [L for L in lens if L > 0]
+    rng = np.random.default_rng(4000 + d + bs + len(lens))
+    case = W.build_case(f"decode_few_d{d}_b{bs}_{len(lens)}seqs", rng, hq=hq, hkv=hkv, d=d, bs=bs,
+                        ctx_lens=[L - 1 for L in live], new_lens=[1] * len(live), kinds="d" * len(live))
+    a, dec = case.steps[0].append, case.steps[0].decode
+    S = len(lens)
+    q = W.bf16_normal(rng, (S, hq, d))
+    k_new = W.bf16_normal(rng, (S, hkv, d))
+    v_new = W.bf16_normal(rng, (S, hkv, d))
+    table = np.full((S, dec.block_table.shape[1]), -1, np.int32)
+    seq_lens = np.zeros(S, np.int32)
+    j = 0
+    for s, L in enumerate(lens):
+        if L > 0:
+            q[s], k_new[s], v_new[s] = dec.q[j], a.k_new[j], a.v_new[j]
+            table[s], seq_lens[s] = dec.block_table[j], dec.seq_lens[j]
+            j += 1
+    _say(f"case {case.name}: lens {lens}")
+    out = _decode_append_check(orc, case, k_new, v_new, q, seq_lens, table, "decode_append, few sequences")
+    for s, L in enumerate(lens):
+        if L == 0:
+            assert np.array_equal(out[s], np.zeros_like(out[s])), "empty sequence must give zeros"
