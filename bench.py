@@ -211,8 +211,24 @@ def traffic_record(op: str):
             if line.startswith("traffic-record:"):
                 rec = json.loads(line.split(":", 1)[1])
                 if rec.get("op") == op and rec.get("source_sha256") == want:
+                    rec["file"] = os.path.relpath(f, ROOT)
                     return rec
     return None
+
+
+def attach_traffic(roofline: dict, op: str) -> None:
+    """roofline["traffic"]: HBM bytes per launch from the committed counter
+    record for `op`, with where it came from; null (and why) when no record
+    matches the current kernel sources -- the counters are not taken in
+    this run."""
+    rec = traffic_record(op)
+    if rec is None:
+        roofline["traffic"] = None
+        roofline["traffic_source"] = "none: no counter record in profiles/ matches the current kernel sources"
+    else:
+        roofline["traffic"] = int(rec["hbm_bytes_per_launch"])
+        roofline["traffic_source"] = (f"{rec['file']}: rocprofv3 --pmc FETCH_SIZE + WRITE_SIZE of an earlier run of "
+                                      f"the same sources (SHA-256 matched), copy-calibrated; not measured in this run")
 
 
 def _timed_replays(graphs, n, warmup):
@@ -375,15 +391,39 @@ def time_mixed_step(args):
     flops = W.prefill_causal_flops(case, st.prefill)
     dc = DeviceCase(case)
     dc.run_fills()
+    n = max(20, args.steps // 4)
     g = dc.capture_step(0)
-    ms = _timed_replays([g], max(20, args.steps // 4), 20)
-    del g, dc
+    ms = _timed_replays([g], n, 20)
+    del g
+    # each branch on its own: the decode (decode_append of its 64 rows), and
+    # the prefill (its 1024 rows appended once beforehand)
+    dec, pre = dc._mixed_parts(0)
+    step = dc.steps[0]
+    gd = dc.capture(lambda: dc.decode_append(dec, step["decode"]))
+    dms = _timed_replays([gd], n, 20)
+    del gd
+    dc.append(pre)
+    gp = dc.capture(lambda: dc.prefill(step["prefill"]))
+    pms = _timed_replays([gp], n, 20)
+    del gp, dc
     torch.cuda.empty_cache()
+    gbs = kv_bytes / (dms * 1e-3) / 1e9
+    tfs = flops / (pms * 1e-3) / 1e12
     return {"workload": "qwen3-8b mixed step: 64 decode seqs (ctx log-uniform [128, 8192]) + 2 x 512-row chunks on "
                         "1024 cached; 32q/8kv, d128, block 256; one HIP graph, decode_append and "
                         "kv_append + prefill as parallel branches",
             "ms": round(ms, 5), "decode_unique_kv_bytes": int(kv_bytes), "prefill_causal_flops": int(flops),
-            "decode_gbs_if_alone": round(kv_bytes / (ms * 1e-3) / 1e9, 2)}
+            "decode_alone": {"ms": round(dms, 5), "what": "the decode branch alone (decode_append of the 64 "
+                                                          "sequences' rows), graph replays",
+                             "roofline": {"bound": "hbm", "kernel": "paged_gqa_decode_append (decode_kernel)",
+                                          "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                          "frac": round(gbs / HBM_PEAK_GBS, 4)}},
+            "prefill_alone": {"ms": round(pms, 5), "what": "the prefill branch's attention alone (two 512-row "
+                                                           "chunks on 1024 cached keys), graph replays",
+                              "roofline": {"bound": "mfma", "kernel": "paged_gqa_prefill (prefill_kernel)",
+                                           "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
+                                           "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}},
+            "overlap": round((dms + pms) / ms, 3)}
 
 
 def time_prefill_workload(args):
@@ -486,7 +526,7 @@ def time_long_decode(args):
     del dc
     torch.cuda.empty_cache()
     gbs = uniq / (ms * 1e-3) / 1e9
-    return {"workload": "qwen3-8b decode, 256 seqs sharing a 4096-token prefix + U[0,2048] private, 16 seqs x 32768; "
+    res = {"workload": "qwen3-8b decode, 256 seqs sharing a 4096-token prefix + U[0,2048] private, 16 seqs x 32768; "
                         "32q/8kv, d128, block 256",
             "ms": round(ms, 5), "ms_median": round(float(np.median(times)), 5),
             "ms_min": round(float(np.min(times)), 5),
@@ -494,9 +534,9 @@ def time_long_decode(args):
             "value": round(gbs, 2), "unit": "GB/s", "logical_gbs": round(logical / (ms * 1e-3) / 1e9, 2),
             "roofline": {"bound": "hbm", "kernel": "paged_gqa_decode (decode_kernel + decode_merge_kernel)",
                          "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": (lambda r: int(r["hbm_bytes_per_launch"]) if r else None)(
-                             traffic_record("long_decode"))}}
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    attach_traffic(res["roofline"], "long_decode")
+    return res
 
 
 def time_private_long_decode(args):
@@ -578,10 +618,8 @@ def time_int8(args, bf16_step_ms, bf16_long_ms):
         "roofline": {"bound": "hbm", "kernel": "paged_gqa_decode_append_int8 (decode_int8_kernel, split "
                                                 "sequences merged in the kernel)",
                      "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
-    rec = traffic_record("int8_decode_append")
-    if rec is not None:
-        res["decode_step"]["roofline"]["traffic"] = int(rec["hbm_bytes_per_launch"])
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    attach_traffic(res["decode_step"]["roofline"], "int8_decode_append")
     if not args.no_long:
         case = W.config5_prefix_long(draw_values=False)
         dec = case.steps[0].decode
@@ -605,7 +643,6 @@ def time_int8(args, bf16_step_ms, bf16_long_ms):
         del dc
         torch.cuda.empty_cache()
         gbs = nbytes / (lms * 1e-3) / 1e9
-        rec = traffic_record("int8_long_decode")
         res["long_context_decode"] = {
             "workload": "the long-context decode (256 seqs on a shared 4096-token prefix + 16 x 32768) over an "
                         "INT8 cache",
@@ -613,8 +650,8 @@ def time_int8(args, bf16_step_ms, bf16_long_ms):
             "speedup_vs_bf16": round(bf16_long_ms / lms, 3) if bf16_long_ms else None,
             "roofline": {"bound": "hbm", "kernel": "paged_gqa_decode_int8 (decode_int8_kernel + decode_merge_kernel)",
                          "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": int(rec["hbm_bytes_per_launch"]) if rec else None}}
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+        attach_traffic(res["long_context_decode"]["roofline"], "int8_long_decode")
     return res
 
 
@@ -663,7 +700,6 @@ def time_qkv(args):
         flops = 2 * T * n_out * dm
         nbytes = (n_out * dm + T * dm + T * n_out) * 2
         r = {"tokens": T, "ms": round(ms, 5), "flops": int(flops), "bytes": int(nbytes)}
-        rec = traffic_record("qkv" if name == "prefill_prompts" else "qkv_decode")
         if name == "prefill_prompts":
             tfs = flops / (ms * 1e-3) / 1e12
             r["roofline"] = {"bound": "mfma", "kernel": "qkv_project_append (qkv_append_kernel)",
@@ -674,7 +710,7 @@ def time_qkv(args):
             r["roofline"] = {"bound": "hbm", "kernel": "qkv_project_append (qkv_append_skinny_kernel)",
                              "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(gbs / HBM_PEAK_GBS, 4)}
-        r["roofline"]["traffic"] = int(rec["hbm_bytes_per_launch"]) if rec else None
+        attach_traffic(r["roofline"], "qkv" if name == "prefill_prompts" else "qkv_decode")
         res[name] = r
         del x, kp, vp, q
         torch.cuda.empty_cache()
@@ -683,29 +719,78 @@ def time_qkv(args):
     return res
 
 
-def cpu_baseline(case, dec, kv_bytes, seconds):
-    """The fp64 oracle on the same decode step, repeated for about `seconds`."""
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(case, dec, kv_bytes, seconds, pcase=None):
+    """The fp64 oracle (plain C, OpenMP) on the host: the same decode step,
+    repeated for about `seconds`, with all cores and with one thread; and the
+    prefill workload, in full on all cores and on a sample of its rows (every
+    8th row of each prompt, all heads) on one thread.  Reference points only."""
     import oracle
     sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from case_oracle import oracle_pools
     orc = oracle.get()
-    K = case.empty_pool()
-    V = case.empty_pool()
-    for f in case.fills:
-        orc.kv_append(K, V, f.k_new, f.v_new, f.cu_new_lens, f.ctx_lens, f.block_table)
-    a = case.steps[0].append
-    orc.kv_append(K, V, a.k_new, a.v_new, a.cu_new_lens, a.ctx_lens, a.block_table)
-    reps = 0
-    t = time.perf_counter()
-    while True:
-        orc.decode(dec.q, K, V, dec.block_table, dec.seq_lens, case.scale)
-        reps += 1
+    cores = orc.max_threads()
+    K, V = oracle_pools(case, orc)
+
+    def decode_rate(threads, budget):
+        reps, t = 0, time.perf_counter()
+        while True:
+            orc.decode(dec.q, K, V, dec.block_table, dec.seq_lens, case.scale, num_threads=threads)
+            reps += 1
+            el = time.perf_counter() - t
+            if el >= budget:
+                return kv_bytes * reps / el / 1e9, reps, el
+
+    gbs, reps, el = decode_rate(cores, seconds)
+    gbs1, reps1, el1 = decode_rate(1, seconds / 2)
+    res = {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+           "sample": f"the whole decode step ({dec.seq_lens.shape[0]} seqs, {int(dec.seq_lens.sum())} keys, "
+                     f"32/8 heads, d128), fp64, repeated {reps}x over {el:.1f} s",
+           "cpu_model": _cpu_model(),
+           "one_thread": {"value": round(gbs1, 4), "unit": "GB/s", "cores": 1,
+                          "sample": f"the same step repeated {reps1}x over {el1:.1f} s"}}
+    if pcase is not None:
+        p = pcase.steps[0].prefill
+        PK, PV = oracle_pools(pcase, orc)
+        D, Hq = pcase.head_dim, pcase.num_q_heads
+        t = time.perf_counter()
+        orc.attention(p.q, p.cu_q_lens, PK, PV, p.block_table, p.seq_lens, Hq, pcase.scale, num_threads=cores)
         el = time.perf_counter() - t
-        if el >= seconds:
-            break
-    return {"value": round(kv_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": orc.max_threads(),
-            "kind": "oracle",
-            "sample": f"the whole decode step ({dec.seq_lens.shape[0]} seqs, {int(dec.seq_lens.sum())} keys, "
-                      f"32/8 heads, d128), fp64, repeated {reps}x over {el:.1f} s"}
+        S = p.seq_lens.shape[0]
+        flops = 0
+        items = []
+        for s in range(S):
+            n = int(p.cu_q_lens[s + 1] - p.cu_q_lens[s])
+            ctx = int(p.seq_lens[s]) - n
+            flops += 4 * D * Hq * (n * ctx + n * (n + 1) // 2)
+        sflops = 0
+        for s in range(S):
+            n = int(p.cu_q_lens[s + 1] - p.cu_q_lens[s])
+            ctx = int(p.seq_lens[s]) - n
+            for r in range(0, n, 8):
+                for h in range(Hq):
+                    items.append((s, r, h))
+                sflops += 4 * D * Hq * (ctx + r + 1)
+        t = time.perf_counter()
+        orc.attention_rows(np.array(items, np.int32), p.q, p.cu_q_lens, PK, PV, p.block_table, p.seq_lens, Hq,
+                           pcase.scale, num_threads=1)
+        el1 = time.perf_counter() - t
+        res["prefill"] = {"value": round(flops / el / 1e9, 3), "unit": "GFLOP/s", "cores": cores,
+                          "sample": f"the whole prefill workload ({int(p.cu_q_lens[-1])} rows x {Hq} heads, "
+                                    f"{flops / 1e9:.1f} GFLOP causal), fp64, once in {el:.1f} s",
+                          "one_thread": {"value": round(sflops / el1 / 1e9, 3), "unit": "GFLOP/s", "cores": 1,
+                                         "sample": f"every 8th row of each prompt, all heads ({len(items)} rows, "
+                                                   f"{sflops / 1e9:.1f} GFLOP) in {el1:.1f} s"}}
+    return res
 
 
 def main():
@@ -749,9 +834,7 @@ def main():
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": int(kv_bytes),
                      "ms": round(step_ms, 5), "decode_only_ms": round(dec_ms, 5)},
     }
-    rec = traffic_record("decode_append")
-    if rec is not None:
-        line["roofline"]["traffic"] = int(rec["hbm_bytes_per_launch"])
+    attach_traffic(line["roofline"], "decode_append")
     if not args.no_prefill:
         pcase, flops, pms, pmed, pmin = time_prefill_workload(args)
         tfs = flops / (pms * 1e-3) / 1e12
@@ -762,9 +845,7 @@ def main():
             "roofline": {"bound": "mfma", "kernel": "paged_gqa_prefill (prefill_kernel)", "achieved": round(tfs, 2),
                          "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
                          "traffic": None}}
-        prec = traffic_record("prefill")
-        if prec is not None:
-            line["prefill"]["roofline"]["traffic"] = int(prec["hbm_bytes_per_launch"])
+        attach_traffic(line["prefill"]["roofline"], "prefill")
     if not args.no_long:
         line["long_context_decode"] = time_long_decode(args)
         line["private_long_decode"] = time_private_long_decode(args)
@@ -778,7 +859,8 @@ def main():
         line["kv_append"] = time_kv_append(args)
     line["device"] = device_context()
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(case, dec, kv_bytes, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(case, dec, kv_bytes, args.cpu_seconds,
+                                            None if args.no_prefill else pcase)
     print(json.dumps(line), flush=True)
 
 
