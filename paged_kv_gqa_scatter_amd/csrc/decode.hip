@@ -423,7 +423,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeKernelArgs
 }  // namespace
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                       int32_t max_seq_len, int64_t total_kv_tokens, int32_t tile_keys, int32_t wgs_per_cu) {
+                       int32_t max_seq_len, int64_t total_kv_tokens, int32_t tile_keys, int32_t wgs_per_cu,
+                       int32_t max_chunk_keys) {
     DecodePlan pl{};
     const int64_t bound_tokens = (int64_t)num_seqs * max_seq_len;
     int64_t total = total_kv_tokens > 0 ? total_kv_tokens : bound_tokens;
@@ -439,7 +440,8 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
     // 4096-token prefix plus 16 of 32K tokens: a chunk that is not
     // a whole number of blocks also turns shared-chunk packing off).
     const int64_t slots = (int64_t)kPlanCus * wgs_per_cu;
-    const int max_chunk = kMaxTilesPerWave * tile_keys * kDecodeWaves;
+    int max_chunk = kMaxTilesPerWave * tile_keys * kDecodeWaves;
+    if (max_chunk_keys > 0 && max_chunk_keys < max_chunk) max_chunk = max_chunk_keys;
     int chunk = kDecodeWaves * 4 * tile_keys;
     int64_t best = -1;
     for (int c = chunk; c <= max_chunk; c *= 2) {

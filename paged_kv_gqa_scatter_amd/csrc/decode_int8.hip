@@ -31,6 +31,10 @@
 //  * Keys past the sequence end are masked to -inf and their v_scale taken
 //    as 0, so neither an unwritten code (any byte is a finite code) nor an
 //    unwritten scale (possibly NaN) reaches the result.
+//  * Sequences whose chunk is the same physical blocks (a shared prefix)
+//    are decoded together in the MFMA's spare columns, as in the bf16 kernel
+//    (decode_common.h): the chunk's codes are read and converted once for
+//    the whole pack instead of once per sequence.
 //  * decode_append_int8 folds the step's kv_append_int8 into the launch, as
 //    decode_append does for bf16: every workgroup quantises its sequence's
 //    new row (its lanes hold the row, the row maximum is a butterfly), and
@@ -42,6 +46,7 @@ namespace pkv {
 namespace {
 
 constexpr int kTile8 = kDecodeInt8TileKeys;  // keys per tile and per LDS stage of a wave
+constexpr int kInt8PackedChunk = 2048;       // keys per work item when sequences are packed
 
 typedef int i32x2_t __attribute__((vector_size(2 * sizeof(int))));
 typedef __attribute__((address_space(3))) i32x2_t lds_i32x2;
@@ -346,6 +351,7 @@ struct Int8Inputs {
     int ids0, ids1;
     u32x4 qf[D / 32];
     u32x4 kn, vn;  // decode_append_int8: this lane's 8 values of the new K/V row
+    PackInputs pk;  // sequences sharing the chunk
 };
 
 template <int D, int G>
@@ -354,13 +360,20 @@ __device__ __forceinline__ Int8Inputs<D> load_int8_inputs(const DecodeKernelArgs
     const int lane = threadIdx.x & 63, wave = wave_id();
     Int8Inputs<D> in;
     in.L_raw = a.seq_lens[s];
-    // Q^T fragment for MFMA cc: head lane % 16 (zero past G), dims
-    // (lane / 16) D/4 + 8 cc + [0, 8), the dims of the lane's K codes
+    // Q^T fragment for MFMA cc: column lane % 16, dims (lane / 16) D/4 +
+    // 8 cc + [0, 8), the dims of the lane's K codes; column h is head h of
+    // sequence s (zero past G), or, for the first sequence of a run that may
+    // pack, head h % G of sequence s + h / G
+    in.pk = load_pack_inputs<G>(p, s, c);
     const int h = lane & 15, j = lane >> 4;
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    const uint16_t* qp = a.q + ((int64_t)s * a.num_q_heads + g * G + min(h, G - 1)) * D + j * (D / 4);
+    const bool lead = in.pk.on && s % pack_width<G>() == 0;
+    const int qs = lead ? s + h / G : s;
+    const bool qv = lead ? qs < a.num_seqs : h < G;
+    const uint16_t* qp =
+        a.q + ((int64_t)min(qs, a.num_seqs - 1) * a.num_q_heads + g * G + h % G) * D + j * (D / 4);
 #pragma unroll
-    for (int cc = 0; cc < D / 32; ++cc) in.qf[cc] = h < G ? load16(qp + 8 * cc) : zero;
+    for (int cc = 0; cc < D / 32; ++cc) in.qf[cc] = qv ? load16(qp + 8 * cc) : zero;
     const int32_t* table = a.block_table + (int64_t)s * a.max_blocks_per_seq;
     const int k0 = c * p.chunk;
     const int last = a.max_blocks_per_seq - 1;
@@ -403,8 +416,6 @@ __device__ __forceinline__ void decode_int8_item(const DecodeKernelArgs& p, Deco
     w.L = L;
     w.append = a.k_new != nullptr;
     w.c = p.qk_scale_log2;
-#pragma unroll
-    for (int cc = 0; cc < D / 32; ++cc) w.qf[cc] = in.qf[cc];
     w.tl = int8_lanes<D>(lane);
     w.st = st;
 
@@ -413,8 +424,19 @@ __device__ __forceinline__ void decode_int8_item(const DecodeKernelArgs& p, Deco
     for (int db = 0; db < D / 16; ++db) ws.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     ws.m = -INFINITY;
     ws.l = 0.f;
-    wait_all_vm();  // the item's inputs are in
-    prefetch();     // the next item's inputs travel with this item's first tiles
+    wait_all_vm();  // the item's inputs (block ids, q, the pack's lengths and ids) are in
+    // sequences sharing the chunk: a member's item exits (its run's first
+    // item decodes it, converting the chunk's codes once for the whole
+    // pack); the first item keeps the columns of its pack
+    const int lead = s - s % pack_width<G>();
+    const uint32_t pack = pack_of<G>(p, in.pk, c);
+    prefetch();  // the next item's inputs travel with this item's first tiles
+    if (s != lead && ((pack >> (s - lead)) & 1)) return;
+    const bool packed = s == lead && pack != 0;
+    const int h = lane & 15;
+    const bool keep = h < G || (packed && ((pack >> (h / G)) & 1));
+#pragma unroll
+    for (int cc = 0; cc < D / 32; ++cc) w.qf[cc] = keep ? in.qf[cc] : u32x4{0u, 0u, 0u, 0u};
     w.kq = w.vq = u32x2{0u, 0u};
     w.ks_new = w.vs_new = 0.f;
     if (w.append) {  // every lane group of the wave holds the row: quantise it (the scheme of kv_append_int8)
@@ -422,7 +444,15 @@ __device__ __forceinline__ void decode_int8_item(const DecodeKernelArgs& p, Deco
         w.vq = quantize_piece<D / 8>(in.vn, &w.vs_new);
     }
     wave_tiles8<D, R>(w, ws);
-    finish_item<D, G>(p, sh, ws, s, g, nchunks, slot);
+    // the packed finish's merge buffer ([4 waves][16][D] floats) takes the
+    // code stages, its maxima and sums the V code stages
+    static_assert(R * kDecodeWaves * kTile8 * D >= kDecodeWaves * 16 * D * (int)sizeof(float),
+                  "the code stages hold the packed merge buffer");
+    if (packed)
+        finish_pack<D, G>(p, reinterpret_cast<float*>(st.k[0]), reinterpret_cast<float*>(st.v[0]), ws, lead, g, c,
+                          pack);
+    else
+        finish_item<D, G>(p, sh, ws, s, g, nchunks, slot);
 }
 
 // R: LDS ring depth per wave.  R = 4: 132 KB of stages at D = 128, one
@@ -459,7 +489,7 @@ hipError_t launch_decode_int8(const DecodeArgs& a, const DecodePlan& pl, hipStre
     kp.log2_block = ilog2(a.block_size);
     kp.max_chunks = pl.max_chunks;
     kp.persistent = pl.persistent;
-    kp.pack = 0;  // the INT8 kernel decodes every sequence on its own
+    kp.pack = pl.pack;
     kp.last_first = pl.last_first;
     kp.max_partials = pl.max_partials;
     char* ws = static_cast<char*>(a.workspace);
@@ -495,9 +525,15 @@ DecodePlan plan_decode_int8(int32_t num_seqs, int32_t num_q_heads, int32_t num_k
     const int wgs = head_dim == 128 ? (group == 8 ? 1 : 2) : 3;
     DecodePlan pl = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, total_kv_tokens,
                                 kTile8, wgs);
-    pl.ring = ring;
-    pl.pack = 0;
-    pl.fused = can_fuse_merge(pl, num_seqs, num_kv_heads);
+    // a launch that packs sequences sharing a chunk takes chunks of at most
+    // 2048 keys: a pack item then carries half of a 4096-key shared prefix,
+    // and the persistent grid's workgroups stay evenly loaded (256 sequences
+    // on a 4096-token prefix + 16 of 32K tokens: 568 us with the 4096-key
+    // chunks the cost model picks, 435-447 us at 2048, 470 us at 1024)
+    if (pl.pack)
+        pl = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, total_kv_tokens, kTile8, wgs,
+                         kInt8PackedChunk);
+    pl.ring = ring;  // plan_decode decides packing (items beyond two rounds) and the in-kernel merge
     return pl;
 }
 

@@ -149,8 +149,10 @@ inline int32_t can_fuse_merge(const DecodePlan& pl, int32_t num_seqs, int32_t nu
 // which wgs_per_cu workgroups are resident on one CU; the plan of each cache
 // format (which also picks its ring depth) comes from plan_decode_bf16 /
 // plan_decode_int8.
+// max_chunk_keys > 0 caps the keys per work item.
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                       int32_t max_seq_len, int64_t total_kv_tokens, int32_t tile_keys, int32_t wgs_per_cu);
+                       int32_t max_seq_len, int64_t total_kv_tokens, int32_t tile_keys, int32_t wgs_per_cu,
+                       int32_t max_chunk_keys = 0);
 DecodePlan plan_decode_bf16(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                             int32_t max_seq_len, int64_t total_kv_tokens);
 DecodePlan plan_decode_int8(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,

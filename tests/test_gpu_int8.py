@@ -275,3 +275,38 @@ def test_int8_decode_persistent_grid_2048_sequences(orc):
     cu = np.arange(2049, dtype=np.int32)
     ref = orc.attention_rows_int8(items, d.q, cu, *pools, d.block_table, d.seq_lens, case.num_q_heads, case.scale)
     compare(out[items[:, 0], items[:, 2]], ref, f"INT8 decode {len(pick)} of 2048 sequences x all heads")
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs,S,prefix,private,long_seq,cut", [
+    # G 4 (packs of 4) with runs missing members and a private first sequence
+    (32, 8, 128, 256, 64, 2048, (5, 17, 18, 20), None, {1: 1024, 2: 1500, 8: 1024, 13: 2048, 14: 1}),
+    # G 8 (packs of 2) over blocks of 32, one long private sequence
+    (64, 8, 128, 32, 65, 1024, (7,), 8191, {1: 1024, 2: 1000, 9: 32}),
+])
+def test_int8_decode_shared_prefix_packs(orc, hq, hkv, d, bs, S, prefix, private, long_seq, cut):
+    # launches with enough work items decode sequences whose chunk is the
+    # same physical blocks together (the chunk's codes converted once for
+    # the pack); outputs against the oracle's INT8 decode, for the decode
+    # step and then, on the same cache and workspace, for lengths cut at
+    # block and chunk boundaries inside the prefix
+    import paged_kv_gqa_scatter_amd as pkv
+    from test_gpu_parity import _shared_case
+    case = _shared_case(f"int8_shared_prefix_g{hq // hkv}_b{bs}", 8000 + hq + bs, hq, hkv, d, bs, S, prefix,
+                        private, long_seq)
+    _say(f"case {case.name}: {S} seqs, prefix {prefix}, private {private}, long {long_seq}, cut {cut}")
+    dc = _dev()(case)
+    out = dc.run_all()[0]["decode"]
+    ref, pools = oracle_int8(case, orc)
+    compare(out, ref[0], "INT8 decode step with shared chunks")
+    dd = dc.steps[0]["decode"]
+    lens = case.steps[0].decode.seq_lens.copy()
+    for s, n in cut.items():
+        lens[s] = n
+    got = pkv.paged_gqa_decode_int8(dd.q, *dc.pools[0], dd.block_table, torch.from_numpy(lens).cuda(),
+                                    float(case.scale), max_seq_len=dd.max_seq_len,
+                                    total_kv_tokens=dd.total_kv_tokens, workspace=dd.workspace)
+    torch.cuda.synchronize()
+    d_ = case.steps[0].decode
+    compare(got.float().cpu().numpy().astype(np.float64),
+            orc.decode_int8(d_.q, *pools, d_.block_table, lens, case.scale), "INT8 decode, cut lengths")
+
