@@ -24,8 +24,9 @@
  *  - bf16 tensors are passed as uint16_t bit patterns; int32 for indices.
  *  - Every pointer is a DEVICE pointer owned by the caller.  The library
  *    allocates nothing, frees nothing, keeps no pointer after a call returns
- *    and has no mutable global state; calls on different streams may run
- *    concurrently.
+ *    and has no mutable global state (one exception:
+ *    pkv_paged_gqa_decode_append_static's per-GPU static scratch); calls on
+ *    different streams may run concurrently.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Calls validate their
  *    scalar arguments on the host, enqueue kernels on `stream` and return
  *    without synchronising; nothing is read back from the device.
