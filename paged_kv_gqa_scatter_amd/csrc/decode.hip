@@ -111,8 +111,8 @@ struct Stages {
 
 
 // Copy tile rows [kt, kt + 16) of (block blk, KV head g) into a stage; rows at
-// or past kend repeat row kend - 1.
-template <int D>
+// or past kend repeat row kend - 1.  kStream: load with the non-temporal hint.
+template <int D, bool kStream>
 __device__ __forceinline__ void issue_tile(const DecodeArgs& a, int log2_block, int g, int blk, int kt, int kend,
                                            const TileLanes<D>& tl, uint32_t sk, uint32_t sv) {
     using T = TileLanes<D>;
@@ -125,15 +125,15 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, int log2_block, 
 #pragma unroll
         for (int i = 0; i < T::kLoads; ++i) {
             const uint32_t off = (uint32_t)(tl.row[i] * D + tl.piece8[i]) * 2u;
-            dma16(kb, off, sk + i * kWave * 16);
-            dma16(vb, off, sv + i * kWave * 16);
+            dma16<kStream>(kb, off, sk + i * kWave * 16);
+            dma16<kStream>(vb, off, sv + i * kWave * 16);
         }
     } else {
 #pragma unroll
         for (int i = 0; i < T::kLoads; ++i) {
             const uint32_t off = (uint32_t)(min(tl.row[i], last) * D + tl.piece8[i]) * 2u;
-            dma16(kb, off, sk + i * kWave * 16);
-            dma16(vb, off, sv + i * kWave * 16);
+            dma16<kStream>(kb, off, sk + i * kWave * 16);
+            dma16<kStream>(vb, off, sv + i * kWave * 16);
         }
     }
 }
@@ -146,6 +146,7 @@ struct WaveItem {
     int log2_block, g, k0, kend, wave, lane, n_tiles;
     int ids0, ids1;  // block id of tile t in lane t % 64 of ids(t / 64)
     int L;           // keys of the sequence
+    bool stream;     // no other item reads this chunk's rows: load them non-temporal
     bool append;     // decode_append: the new row (kn, vn: this lane's piece) is key L - 1
     u32x4 kn, vn;
     float c;         // scale * log2 e
@@ -170,8 +171,11 @@ __device__ __forceinline__ void issue(const WaveItem<D>& w, int t, int stage) {
     const int blk = tile_blk(w, t);
     const int b = (unsigned)blk < (unsigned)w.a->num_blocks ? blk : 0;  // a bad id reads block 0, masked below
     const uint32_t wave_bytes = (uint32_t)(w.wave * kTileKeys * D * 2);
-    issue_tile<D>(*w.a, w.log2_block, w.g, b, tile_key(w, t), w.kend, w.tl, lds_addr(w.st.k[stage]) + wave_bytes,
-                  lds_addr(w.st.v[stage]) + wave_bytes);
+    const uint32_t sk = lds_addr(w.st.k[stage]) + wave_bytes, sv = lds_addr(w.st.v[stage]) + wave_bytes;
+    if (w.stream)
+        issue_tile<D, true>(*w.a, w.log2_block, w.g, b, tile_key(w, t), w.kend, w.tl, sk, sv);
+    else
+        issue_tile<D, false>(*w.a, w.log2_block, w.g, b, tile_key(w, t), w.kend, w.tl, sk, sv);
 }
 
 // decode_append, on the tile holding key L - 1 (row r0 of the tile): the new
@@ -384,6 +388,7 @@ __device__ __forceinline__ void decode_item(const DecodeKernelArgs& p, DecodeSha
     prefetch();
     if (s != lead && ((pack >> (s - lead)) & 1)) return;
     const bool packed = s == lead && pack != 0;
+    w.stream = __builtin_amdgcn_readfirstlane(packed ? 0 : 1) != 0;  // a shared pack's rows are read by other packs
     const int h = lane & 15;
     const bool keep = h < G || (packed && ((pack >> (h / G)) & 1));
 #pragma unroll

@@ -111,8 +111,13 @@ struct Int8Stages {
 
 // global_load_lds_dwordx4 with a per-lane 64-bit address (the scale rows of K
 // and V live in different arrays): lane l's 16 bytes land at lds + 16 l.
+// kStream: the non-temporal hint, as dma16.
+template <bool kStream>
 __device__ __forceinline__ void dma16_addr(const void* addr, uint32_t lds) {
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(addr), "{m0}"(lds) : "memory");
+    if (kStream)
+        asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(addr), "{m0}"(lds) : "memory");
+    else
+        asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(addr), "{m0}"(lds) : "memory");
 }
 
 // Per-wave view of the item.
@@ -122,6 +127,7 @@ struct Int8WaveItem {
     int log2_block, g, k0, kend, wave, lane, n_tiles;
     int ids0, ids1;  // block id of tile t in lane t % 64 of ids(t / 64)
     int L;           // keys of the sequence
+    bool stream;     // no other item reads this chunk's rows: load them non-temporal
     bool append;     // decode_append_int8: the new row (this lane's codes, the scales) is key L - 1
     u32x2 kq, vq;
     float ks_new, vs_new;
@@ -145,9 +151,9 @@ __device__ __forceinline__ int tile_key8(const Int8WaveItem<D>& w, int t) {
 // Copy tile t (keys [kt, kt + 32) of one block) into a stage: the code rows
 // of K and V and, from lanes 0..15, the two 128-byte scale rows.  Rows past
 // the sequence end are copied too (they stay inside the block) and masked by
-// the consumer.
-template <int D>
-__device__ __forceinline__ void issue8(const Int8WaveItem<D>& w, int t, int stage) {
+// the consumer.  kStream: load with the non-temporal hint.
+template <int D, bool kStream>
+__device__ __forceinline__ void issue8_tile(const Int8WaveItem<D>& w, int t, int stage) {
     using T = Int8Lanes<D>;
     const DecodeArgs& a = *w.a;
     const int blk = tile_blk8(w, t);
@@ -160,13 +166,21 @@ __device__ __forceinline__ void issue8(const Int8WaveItem<D>& w, int t, int stag
     const uint32_t sk = lds_addr(w.st.k[stage]) + wave_bytes, sv = lds_addr(w.st.v[stage]) + wave_bytes;
 #pragma unroll
     for (int i = 0; i < T::kLoads; ++i) {
-        dma16(kb, w.tl.dma_off[i], sk + i * kWave * 16);
-        dma16(vb, w.tl.dma_off[i], sv + i * kWave * 16);
+        dma16<kStream>(kb, w.tl.dma_off[i], sk + i * kWave * 16);
+        dma16<kStream>(vb, w.tl.dma_off[i], sv + i * kWave * 16);
     }
     if (w.lane < 16) {
         const float* src = (w.lane < 8 ? a.k_scales : a.v_scales) + row0 + 4 * (w.lane & 7);
-        dma16_addr(src, lds_addr(w.st.sc[stage]) + (uint32_t)(w.wave * 2 * kTile8 * 4));
+        dma16_addr<kStream>(src, lds_addr(w.st.sc[stage]) + (uint32_t)(w.wave * 2 * kTile8 * 4));
     }
+}
+
+template <int D>
+__device__ __forceinline__ void issue8(const Int8WaveItem<D>& w, int t, int stage) {
+    if (w.stream)
+        issue8_tile<D, true>(w, t, stage);
+    else
+        issue8_tile<D, false>(w, t, stage);
 }
 
 // decode_append_int8, on the tile holding key L - 1 (row r0 of the tile):
@@ -433,6 +447,7 @@ __device__ __forceinline__ void decode_int8_item(const DecodeKernelArgs& p, Deco
     prefetch();  // the next item's inputs travel with this item's first tiles
     if (s != lead && ((pack >> (s - lead)) & 1)) return;
     const bool packed = s == lead && pack != 0;
+    w.stream = __builtin_amdgcn_readfirstlane(packed ? 0 : 1) != 0;  // a shared pack's rows are read by other packs
     const int h = lane & 15;
     const bool keep = h < G || (packed && ((pack >> (h / G)) & 1));
 #pragma unroll
