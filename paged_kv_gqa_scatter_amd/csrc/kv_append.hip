@@ -5,7 +5,10 @@
 // pos of sequence s is slot pos % B of block block_table[s][pos / B].  The copy
 // is a pure bit move and HBM-bound: every thread moves one 16-byte piece (8 bf16)
 // of K and the same piece of V, so a wave moves whole contiguous rows with
-// 16-byte accesses on both sides.
+// 16-byte accesses on both sides.  Rows are read and written with the
+// non-temporal hint (each byte is touched once; measured on 8130 prompt rows:
+// 16.9 -> 14.6 us).  The INT8 append keeps plain accesses: its 8-byte code
+// stores with the hint took 22.4 us against 20.3 us.
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -43,8 +46,8 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendArgs a)
 
     // the row's data does not depend on where it goes: load it first
     const int64_t src = ((int64_t)t * a.num_kv_heads + g) * D + piece * 8;
-    const u32x4 kv = load16(a.k_new + src);
-    const u32x4 vv = load16(a.v_new + src);
+    const u32x4 kv = load16_nt(a.k_new + src);
+    const u32x4 vv = load16_nt(a.v_new + src);
 
     const int s = owner_seq(a.cu_new_lens, a.num_seqs, a.total_new_tokens, t);
     const int64_t pos = (int64_t)a.ctx_lens[s] + (t - a.cu_new_lens[s]);
@@ -54,8 +57,8 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendArgs a)
     if (blk < 0 || blk >= a.num_blocks) return;
     const int slot = (int)(pos & (a.block_size - 1));
     const int64_t dst = (((int64_t)blk * a.num_kv_heads + g) * a.block_size + slot) * D + piece * 8;
-    store16(a.k_pool + dst, kv);
-    store16(a.v_pool + dst, vv);
+    store16_nt(a.k_pool + dst, kv);
+    store16_nt(a.v_pool + dst, vv);
 }
 
 // kv_append into an INT8 cache ("从零搭建AI工程能力：手写KV Cache与动态批处理实战"

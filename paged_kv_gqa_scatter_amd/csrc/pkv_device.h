@@ -34,6 +34,15 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void store16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// The same with the non-temporal hint (nt): for data read or written once,
+// which the caches should not keep in place of data that is reused.
+__device__ __forceinline__ u32x4 load16_nt(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void store16_nt(uint16_t* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
 // 2^x (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
