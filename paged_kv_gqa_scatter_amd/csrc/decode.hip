@@ -146,7 +146,7 @@ struct WaveItem {
     int log2_block, g, k0, kend, wave, lane, n_tiles;
     int ids0, ids1;  // block id of tile t in lane t % 64 of ids(t / 64)
     int L;           // keys of the sequence
-    bool stream;     // no other item reads this chunk's rows: load them non-temporal
+    bool stream;     // not a shared pack: load the chunk's rows with the non-temporal hint
     bool append;     // decode_append: the new row (kn, vn: this lane's piece) is key L - 1
     u32x4 kn, vn;
     float c;         // scale * log2 e

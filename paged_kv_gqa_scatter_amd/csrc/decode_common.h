@@ -124,10 +124,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // base + voff land at LDS byte address lds + 16 l.  Written as inline asm so
 // that the compiler, which cannot tell the four stages apart, does not wait
 // for every copy in flight before each LDS read; the ring's waits are
-// explicit (wait_vmcnt).  kStream sets the non-temporal hint (nt): for K/V
-// rows that no other item of the launch will read again, so that the caches
-// keep what is shared (a common prefix, q, tables, partials) instead of the
-// stream.  Measured with the hint on every chunk that is not a shared pack:
+// explicit (wait_vmcnt).  kStream sets the non-temporal hint (nt), used for
+// every chunk that is not a shared pack -- rows no other item is known to
+// read again -- so that the caches keep what is shared (a packed common
+// prefix, q, tables, partials) instead of the stream.  (A launch too small
+// to pack may still have sequences on shared blocks; their chunks stream
+// with the hint too, and run at once, so they meet in L2 all the same.)
+// Measured with the hint on every chunk that is not a shared pack:
 // the 8-sequence decode step 13.6 -> 12.4 us, 16 x 32K private keys
 // 381 -> 340 us, the shared-prefix batch 698 -> 626 us; with it on the
 // shared packs too that batch took 756 us.

@@ -127,7 +127,7 @@ struct Int8WaveItem {
     int log2_block, g, k0, kend, wave, lane, n_tiles;
     int ids0, ids1;  // block id of tile t in lane t % 64 of ids(t / 64)
     int L;           // keys of the sequence
-    bool stream;     // no other item reads this chunk's rows: load them non-temporal
+    bool stream;     // not a shared pack: load the chunk's rows with the non-temporal hint
     bool append;     // decode_append_int8: the new row (this lane's codes, the scales) is key L - 1
     u32x2 kq, vq;
     float ks_new, vs_new;
