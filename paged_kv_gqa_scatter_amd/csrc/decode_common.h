@@ -129,7 +129,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // read again -- so that the caches keep what is shared (a packed common
 // prefix, q, tables, partials) instead of the stream.  (A launch too small
 // to pack may still have sequences on shared blocks; their chunks stream
-// with the hint too, and run at once, so they meet in L2 all the same.)
+// with the hint too.)
 // Measured with the hint on every chunk that is not a shared pack:
 // the 8-sequence decode step 13.6 -> 12.4 us, 16 x 32K private keys
 // 381 -> 340 us, the shared-prefix batch 698 -> 626 us; with it on the
