@@ -471,10 +471,10 @@ def time_prefill_workload(args):
 
 
 def device_context():
-    """The device and a practical HBM ceiling: a 1 GiB device-to-device copy
-    (read + write bytes over its median time, 10 timed copies), and the
-    engine clock the driver reports as current when there is one GPU to
-    read it from."""
+    """The device and practical HBM ceilings: a 1 GiB device-to-device copy
+    (read + write bytes over its median time, 10 timed copies), a 2 GiB plain
+    read (pkv_read_probe, median of 10), and the engine clock the driver
+    reports as current when there is one GPU to read it from."""
     import glob
     import torch
     n = 1 << 29  # int16 elements: 1 GiB
@@ -491,10 +491,29 @@ def device_context():
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in evs)[len(evs) // 2]
     del src, dst
+    # plain reads: 2 GiB streamed once per call by the library's read probe
+    # (16-byte non-temporal loads, as the decode kernels stream K/V)
+    import paged_kv_gqa_scatter_amd as pkv
+    data = torch.zeros(1 << 30, dtype=torch.int16, device="cuda")
+    sink = torch.empty(16 * pkv.READ_PROBE_WORKGROUPS, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        pkv.read_probe(data, sink)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for a, b in evs:
+        a.record(s)
+        pkv.read_probe(data, sink)
+        b.record(s)
+    torch.cuda.synchronize()
+    rms = sorted(a.elapsed_time(b) for a, b in evs)[len(evs) // 2]
+    read_bytes = data.numel() * data.element_size()
+    del data, sink
     props = torch.cuda.get_device_properties(0)
     ctx = {"name": props.name, "compute_units": props.multi_processor_count,
            "copy_GBps": round(2 * 2 * n / (ms * 1e-3) / 1e9, 1),
-           "copy_note": "1 GiB device-to-device copy, read + write bytes: a practical ceiling for HBM-bound kernels"}
+           "copy_note": "1 GiB device-to-device copy, read + write bytes",
+           "read_GBps": round(read_bytes / (rms * 1e-3) / 1e9, 1),
+           "read_note": "2 GiB read once by pkv_read_probe (16-byte non-temporal loads): the practical read "
+                        "ceiling for the HBM-bound decode kernels"}
     clocks = []
     for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
         try:

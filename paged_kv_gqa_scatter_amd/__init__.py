@@ -34,6 +34,8 @@ BLOCK_EXPORTS = ("pkv_bm_create", "pkv_bm_destroy", "pkv_bm_available", "pkv_bm_
 INT8_EXPORTS = ("pkv_kv_append_int8", "pkv_decode_int8_workspace_bytes", "pkv_paged_gqa_decode_int8",
                 "pkv_paged_gqa_decode_append_int8")
 QKV_EXPORTS = ("pkv_qkv_project_append",)
+DIAG_EXPORTS = ("pkv_read_probe",)
+READ_PROBE_WORKGROUPS = 8192  # PKV_READ_PROBE_WORKGROUPS
 
 
 class PkvError(RuntimeError):
@@ -98,6 +100,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
                                                      I32, I32, F32, P, SZ, P]
     lib.pkv_qkv_project_append.restype = I32
     lib.pkv_qkv_project_append.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, I32, P]
+    lib.pkv_read_probe.restype = I32
+    lib.pkv_read_probe.argtypes = [P, SZ, P, SZ, P]
     lib.pkv_paged_gqa_prefill.restype = I32
     lib.pkv_paged_gqa_prefill.argtypes = [P, P, P, I32, I32, P, P, P, I32, P, I32, I32, I32, I32, I32, I32, I32,
                                           F32, P]
@@ -457,3 +461,15 @@ def paged_gqa_prefill(q, cu_q_lens, k_pool, v_pool, block_table, seq_lens, scale
                                     float(scale), _stream())
     _check(st, "paged_gqa_prefill")
     return out
+
+
+def read_probe(data: torch.Tensor, sink: torch.Tensor) -> None:
+    """Read every byte of ``data`` once on the current stream (see
+    ``pkv_read_probe`` in include/pkv_diag.h): the device's plain read rate.
+    ``sink`` is a device buffer of at least 16 * READ_PROBE_WORKGROUPS bytes
+    whose contents are unspecified afterwards."""
+    if not (data.is_cuda and sink.is_cuda and data.is_contiguous() and sink.is_contiguous()):
+        raise ValueError("data and sink must be contiguous device tensors")
+    st = lib().pkv_read_probe(data.data_ptr(), data.numel() * data.element_size(), sink.data_ptr(),
+                              sink.numel() * sink.element_size(), _stream())
+    _check(st, "read_probe")

@@ -14,6 +14,7 @@ HEADER = os.path.join(ROOT, "include", "pkv.h")
 BLOCKS_HEADER = os.path.join(ROOT, "include", "pkv_blocks.h")
 INT8_HEADER = os.path.join(ROOT, "include", "pkv_int8.h")
 QKV_HEADER = os.path.join(ROOT, "include", "pkv_qkv.h")
+DIAG_HEADER = os.path.join(ROOT, "include", "pkv_diag.h")
 
 
 @pytest.fixture(scope="module")
@@ -48,8 +49,25 @@ def test_qkv_header_declares_its_functions():
     assert set(declared_functions(QKV_HEADER)) == set(pkv.QKV_EXPORTS)
 
 
+def test_diag_header_declares_its_functions():
+    assert set(declared_functions(DIAG_HEADER)) == set(pkv.DIAG_EXPORTS)
+    text = open(DIAG_HEADER).read()
+    assert f"#define PKV_READ_PROBE_WORKGROUPS {pkv.READ_PROBE_WORKGROUPS}" in text
+
+
+def test_read_probe_rejects(lib):
+    sink_bytes = 16 * pkv.READ_PROBE_WORKGROUPS
+    assert lib.pkv_read_probe(None, 1 << 20, A16, sink_bytes, None) == 1
+    assert lib.pkv_read_probe(A16, 1 << 20, None, sink_bytes, None) == 1
+    assert lib.pkv_read_probe(A16 + 8, 1 << 20, A16, sink_bytes, None) == 3
+    assert lib.pkv_read_probe(A16, 1 << 20, A16 + 4, sink_bytes, None) == 3
+    assert lib.pkv_read_probe(A16, 0, A16, sink_bytes, None) == 2
+    assert lib.pkv_read_probe(A16, (1 << 20) + 8, A16, sink_bytes, None) == 2
+    assert lib.pkv_read_probe(A16, 1 << 20, A16, sink_bytes - 16, None) == 4
+
+
 def test_every_declared_symbol_is_exported(lib):
-    for header in (HEADER, BLOCKS_HEADER, INT8_HEADER, QKV_HEADER):
+    for header in (HEADER, BLOCKS_HEADER, INT8_HEADER, QKV_HEADER, DIAG_HEADER):
         for name in declared_functions(header):
             assert hasattr(lib, name), name
 

@@ -679,3 +679,15 @@ def test_decode_few_sequences(orc, d, bs, hq, hkv, lens):
     for s, L in enumerate(lens):
         if L == 0:
             assert np.array_equal(out[s], np.zeros_like(out[s])), "empty sequence must give zeros"
+
+
+def test_read_probe_reads_without_writing():
+    """pkv_read_probe over zeros: the status is OK and the sink, whose slots
+    are written only when a workgroup's XOR fold hits the probe's constant,
+    keeps its contents (a fold of zeros is zero)."""
+    import paged_kv_gqa_scatter_amd as pkv
+    data = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.full((16 * pkv.READ_PROBE_WORKGROUPS,), 0x5A, dtype=torch.uint8, device="cuda")
+    pkv.read_probe(data, sink)
+    torch.cuda.synchronize()
+    assert bool((sink == 0x5A).all())
