@@ -767,7 +767,8 @@ def cpu_baseline(case, dec, kv_bytes, seconds, pcase=None):
     """The fp64 oracle (plain C, OpenMP) on the host: the same decode step,
     repeated for about `seconds`, with all cores and with one thread; and the
     prefill workload, in full on all cores and on a sample of its rows (every
-    8th row of each prompt, all heads) on one thread.  Reference points only."""
+    8th row of each prompt, all heads) on one thread; and config 1 (_cpu_tiny).
+    Reference points only."""
     import oracle
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from case_oracle import oracle_pools
@@ -824,7 +825,43 @@ def cpu_baseline(case, dec, kv_bytes, seconds, pcase=None):
                           "one_thread": {"value": round(sflops / el1 / 1e9, 3), "unit": "GFLOP/s", "cores": 1,
                                          "sample": f"every 8th row of each prompt, all heads ({len(items)} rows, "
                                                    f"{sflops / 1e9:.1f} GFLOP) in {el1:.1f} s"}}
+    res["tiny"] = _cpu_tiny(orc, cores)
     return res
+
+
+def _cpu_tiny(orc, cores):
+    """Config 1 on the oracle: its 300-row prefill (4 query heads, d64) and a
+    decode step (301 keys), each repeated for about a second, on all cores and
+    on one thread."""
+    from case_oracle import oracle_pools
+    from paged_kv_gqa_scatter_amd import workloads as W
+    case = W.config1_tiny()
+    K, V = oracle_pools(case, orc)  # every step's rows; each call reads only its own positions
+    p, d = case.steps[0].prefill, case.steps[1].decode
+    D, Hq = case.head_dim, case.num_q_heads
+    n = int(p.cu_q_lens[1])
+    flops = 4 * D * Hq * (n * (int(p.seq_lens[0]) - n) + n * (n + 1) // 2)
+    kv = int(d.seq_lens.sum()) * case.num_kv_heads * D * 2 * 2
+
+    def rate(fn, threads, amount):
+        reps, t = 0, time.perf_counter()
+        while True:
+            fn(threads)
+            reps += 1
+            el = time.perf_counter() - t
+            if el >= 1.0:
+                return amount * reps / el / 1e9
+
+    pre = lambda th: orc.attention(p.q, p.cu_q_lens, K, V, p.block_table, p.seq_lens, Hq, case.scale,
+                                   num_threads=th)
+    dec = lambda th: orc.decode(d.q, K, V, d.block_table, d.seq_lens, case.scale, num_threads=th)
+    return {"workload": f"config 1: causal prefill of {n} rows ({Hq} query heads / 1 KV head, d{D}; "
+                        f"{flops / 1e6:.1f} MFLOP) and a decode step over {int(d.seq_lens.sum())} keys, fp64, "
+                        "each repeated for about 1 s",
+            "prefill": {"value": round(rate(pre, cores, flops), 3), "unit": "GFLOP/s", "cores": cores,
+                        "one_thread": round(rate(pre, 1, flops), 3)},
+            "decode": {"value": round(rate(dec, cores, kv), 4), "unit": "GB/s", "cores": cores,
+                       "one_thread": round(rate(dec, 1, kv), 4)}}
 
 
 def main():
