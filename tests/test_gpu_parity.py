@@ -691,3 +691,99 @@ def test_read_probe_reads_without_writing():
     pkv.read_probe(data, sink)
     torch.cuda.synchronize()
     assert bool((sink == 0x5A).all())
+
+
+def test_invalid_block_ids_stay_inside_their_sequence(orc):
+    # table entries are preconditions; a bad one (negative, or past the pool)
+    # is read as block 0 and its keys masked by the decode, and skipped by
+    # the append: nothing outside the buffers is touched, and every other
+    # sequence's output and every other pool slot come out as with valid
+    # tables (the corrupted sequence's own output is unspecified)
+    import paged_kv_gqa_scatter_amd as pkv
+    case = W.config2_decode()
+    ref, (K, V) = oracle_outputs(case, orc)
+    K0, V0 = oracle_pools(case, orc, upto_step=0)  # after the fills, before the step's rows
+    B = case.block_size
+    lens = case.steps[0].decode.seq_lens
+    table = case.steps[0].decode.block_table
+    s_bad = 3
+    assert lens[s_bad] > 2 * B + 1, "entries 0 and 1 must not hold the new row"
+    keep = np.arange(len(lens)) != s_bad
+
+    # decode over a table whose entries 0 and 1 of one sequence are invalid
+    d2 = _dev()(case)
+    d2.run_fills()
+    st = d2.steps[0]
+    d2.append(st["append"])
+    dd = st["decode"]
+    bad = dd.block_table.clone()
+    bad[s_bad, 0] = -1
+    bad[s_bad, 1] = case.num_blocks + 7
+    _say(f"case {case.name}: sequence {s_bad}'s table entries 0 and 1 set to -1 and num_blocks + 7")
+    out = pkv.paged_gqa_decode(dd.q, *d2.pools[0], bad, dd.seq_lens, case.scale, max_seq_len=dd.max_seq_len,
+                               total_kv_tokens=dd.total_kv_tokens, workspace=dd.workspace)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    compare(got[keep], ref[0]["decode"][keep], "decode, the other sequences")
+    Kg, Vg = d2.pools_numpy()
+    assert np.array_equal(Kg, K) and np.array_equal(Vg, V), "pools changed by a decode"
+
+    # decode_append whose new row's block entry is invalid: that row is skipped
+    d3 = _dev()(case)
+    d3.run_fills()
+    st3 = d3.steps[0]
+    dd3 = st3["decode"]
+    last = (int(lens[s_bad]) - 1) // B
+    bad3 = dd3.block_table.clone()
+    bad3[s_bad, last] = -1
+    a = st3["append"]
+    _say(f"  decode_append with sequence {s_bad}'s last block entry set to -1")
+    out3 = pkv.paged_gqa_decode_append(dd3.q, a.k_new, a.v_new, *d3.pools[0], bad3, dd3.seq_lens, case.scale,
+                                       max_seq_len=dd3.max_seq_len, total_kv_tokens=dd3.total_kv_tokens,
+                                       workspace=dd3.workspace)
+    torch.cuda.synchronize()
+    got3 = out3.float().cpu().numpy().astype(np.float64)
+    compare(got3[keep], ref[0]["decode"][keep], "decode_append, the other sequences")
+    want_k, want_v = K.copy(), V.copy()
+    blk, slot = int(table[s_bad, last]), (int(lens[s_bad]) - 1) % B
+    want_k[blk, :, slot] = K0[blk, :, slot]  # the skipped row's slot keeps what it held
+    want_v[blk, :, slot] = V0[blk, :, slot]
+    Kg3, Vg3 = d3.pools_numpy()
+    assert np.array_equal(Kg3, want_k) and np.array_equal(Vg3, want_v), "decode_append wrote outside its rows"
+
+
+def test_decode_concurrent_streams(orc):
+    # the library keeps no state between calls: two decode steps with their
+    # own workspaces (both merging split sequences inside the kernel through
+    # their workspace's counters), issued alternately on two streams with
+    # nothing ordering them, give exactly the outputs of the calls run alone
+    a_case, b_case = W.config2_decode(), W.config2_decode(seed=12)
+    da, db = _dev()(a_case), _dev()(b_case)
+    for d in (da, db):
+        d.run_fills()
+        d.append(d.steps[0]["append"])
+    sa_dec, sb_dec = da.steps[0]["decode"], db.steps[0]["decode"]
+    ra = da.decode(sa_dec).clone()
+    rb = db.decode(sb_dec).clone()
+    torch.cuda.synchronize()
+    ref_a, _ = oracle_outputs(a_case, orc)
+    ref_b, _ = oracle_outputs(b_case, orc)
+    compare(ra.float().cpu().numpy().astype(np.float64), ref_a[0]["decode"], "stream A alone")
+    compare(rb.float().cpu().numpy().astype(np.float64), ref_b[0]["decode"], "stream B alone")
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+    main = torch.cuda.current_stream()
+    sa.wait_stream(main)
+    sb.wait_stream(main)
+    _say("case: two decode steps, 40 calls each, alternating between two streams")
+    for _ in range(40):
+        with torch.cuda.stream(sa):
+            oa = da.decode(sa_dec)
+        with torch.cuda.stream(sb):
+            ob = db.decode(sb_dec)
+    main.wait_stream(sa)
+    main.wait_stream(sb)
+    torch.cuda.synchronize()
+    assert torch.equal(oa.view(torch.int16), ra.view(torch.int16)), "stream A differs from its lone call"
+    assert torch.equal(ob.view(torch.int16), rb.view(torch.int16)), "stream B differs from its lone call"
+    assert int(torch.count_nonzero(sa_dec.workspace[:16384])) == 0 and \
+        int(torch.count_nonzero(sb_dec.workspace[:16384])) == 0, "counters left non-zero"
