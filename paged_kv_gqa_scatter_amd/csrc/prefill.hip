@@ -432,18 +432,173 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillKern
         }
 }
 
+// ---- small launches: the key range split between two halves of a workgroup
+//
+// A launch with fewer workgroups than two per CU leaves one wave per SIMD,
+// and nothing hides its latencies.  Then a workgroup of 8 waves takes the
+// same 128 query rows: waves 0-3 the first half of the key tiles, waves 4-7
+// the second, each half streaming its own tiles through its own two stages
+// exactly as prefill_kernel does (one workgroup barrier per tile; the half
+// with fewer tiles passes its extra barriers idle).  At the end the second
+// half hands its running maximum, sum and O^T fragments to the first through
+// LDS, and the first merges the two states (each relative to its own
+// maximum) and writes the rows.
+constexpr int kSplitThreads = 512;
+
+// A tile step for a half that has no tile left: only the barrier.
+__device__ __forceinline__ void idle_step() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+}
+
+template <int D, bool kNegScale>
+__global__ __launch_bounds__(kSplitThreads, 2) void prefill_split_kernel(PrefillKernelArgs p) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2 * stage_elems<D>()];
+    const PrefillArgs& a = p.a;
+
+    // workgroup -> (query tile, sequence, query head), as prefill_kernel
+    const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, S = a.num_seqs;
+    int idx = blockIdx.x;
+    const int g = idx % Hkv;
+    idx /= Hkv;
+    const int hg = idx % p.group;
+    idx /= p.group;
+    const int s = idx % S;
+    const int tile = p.q_tiles - 1 - idx / S;
+    const int h = g * p.group + hg;
+
+    const int q0 = min(max(a.cu_q_lens[s], 0), a.total_q_tokens);
+    const int n = min(min(max(a.cu_q_lens[s + 1], q0), a.total_q_tokens) - q0, a.max_q_len);
+    if (tile * kTileQ >= n) return;
+    const int cap = a.max_blocks_per_seq << p.log2_block;
+    int L = a.seq_lens[s];
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    const int ctx = L - n;
+
+    const int lane = threadIdx.x & 63, wave8 = wave_id(), half = lane >> 5;
+    const int part = wave8 >> 2;  // which half of the key tiles
+    const int wave = wave8 & 3;   // 32-row block of the tile
+    const int qrow = tile * kTileQ + wave * 32 + (lane & 31);
+    const int wave_row0 = tile * kTileQ + wave * 32;
+
+    Loop<D> lp;
+    lp.p = &p;
+    lp.table = a.block_table + (int64_t)s * a.max_blocks_per_seq;
+    lp.g = g;
+    lp.kend = min(L, ctx + min((tile + 1) * kTileQ, n));
+    const int T = lp.kend > 0 ? (lp.kend + kTileK - 1) / kTileK : 0;
+    const int T0 = T / 2;                    // the first half's tiles: [0, T0); the second's: [T0, T)
+    const int tb = part ? T0 : 0, te = part ? T : T0;
+    const int steps = T - T0;                // the longer half's tile count: the barriers both halves pass
+    lp.ntiles = te;                          // tile_step copies tile t + 1 only while t + 1 < te
+    lp.wave = wave;
+    lp.lane = lane;
+    lp.qpos = ctx + qrow;
+    lp.wave_qpos_min = ctx + wave_row0;
+    lp.wave_qpos_max = ctx + min(wave_row0 + 31, n - 1);
+    lp.wave_rows = wave_row0 < n;
+    lp.c = p.qk_scale_log2;
+    lp.lds = lds[part];
+    lp.ln = lanes<D>(lane);
+
+    u32x4 qreg[D / 16];
+    {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        const uint16_t* qp = a.q + ((int64_t)(q0 + qrow) * Hq + h) * D + half * 8;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) qreg[ks] = qrow < n ? load16(qp + ks * 16) : zero;
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): q is in (see prefill_kernel)
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    float m = -INFINITY, lsum = 0.f;
+
+    BlockIds bi;
+    bi.ids = 0;
+    bi.win = 0;
+    if (te > tb) {
+        fill_ids<D>(lp, bi, tb);
+        copy_tile<D>(lp, tb * kTileK, tile_block<D>(lp, bi, tb), lp.lds);
+    }
+    for (int i = 0; i < steps; i += 2) {
+        const int t = tb + i;
+        if (t < te)
+            tile_step<D, 0, kNegScale>(lp, t, bi, qreg, acc, m, lsum);
+        else
+            idle_step();
+        if (i + 1 < steps) {
+            if (t + 1 < te)
+                tile_step<D, 1, kNegScale>(lp, t + 1, bi, qreg, acc, m, lsum);
+            else
+                idle_step();
+        }
+    }
+    lsum += __shfl_xor(lsum, 32, kWave);
+
+    // the second half's state to LDS (the stages are free once every wave is
+    // past its last tile), then the first half merges it into its own
+    __syncthreads();
+    float* xo = reinterpret_cast<float*>(&lds[0][0]);  // [4 waves][D / 32][16][64 lanes]
+    float* xm = xo + 4 * (D / 32) * 16 * kWave;        // [4 waves][64 lanes]
+    float* xl = xm + 4 * kWave;
+    if (part == 1) {
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) xo[((wave * (D / 32) + i) * 16 + r) * kWave + lane] = acc[i][r];
+        xm[wave * kWave + lane] = m;
+        xl[wave * kWave + lane] = lsum;
+    }
+    __syncthreads();
+    if (part == 1 || qrow >= n) return;
+    const float m1 = xm[wave * kWave + lane], l1 = xl[wave * kWave + lane];
+    const float mm = fmaxf(m, m1);
+    const float a0 = m == -INFINITY ? 0.f : fast_exp2(m - mm);  // a half without keys adds nothing
+    const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mm);
+    lsum = lsum * a0 + l1 * a1;
+    const float inv = (lp.qpos >= 0 && lsum > 0.f) ? 1.f / lsum : 0.f;  // a row with no key is zero
+    uint16_t* op = a.out + ((int64_t)(q0 + qrow) * Hq + h) * D;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+        float o[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[r] = acc[i][r] * a0 + xo[((wave * (D / 32) + i) * 16 + r) * kWave + lane] * a1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int d = i * 32 + j * 8 + half * 4;
+            u32x2 w = {pack_bf16x2(o[4 * j] * inv, o[4 * j + 1] * inv), pack_bf16x2(o[4 * j + 2] * inv, o[4 * j + 3] * inv)};
+            *reinterpret_cast<u32x2*>(op + d) = w;
+        }
+    }
+}
+
 int ilog2(int x) {
     int r = 0;
     while ((1 << r) < x) ++r;
     return r;
 }
 
+// Workgroups a launch needs for two per CU (the plan's CU count, as decode's).
+constexpr int64_t kSplitBelow = 2 * 256;
+
 template <int D>
 void launch_d(const PrefillKernelArgs& kp, int64_t blocks, hipStream_t stream) {
-    if (kp.qk_scale_log2 < 0.f)
+    if (blocks < kSplitBelow) {
+        if (kp.qk_scale_log2 < 0.f)
+            hipLaunchKernelGGL((prefill_split_kernel<D, true>), dim3((unsigned)blocks), dim3(kSplitThreads), 0,
+                               stream, kp);
+        else
+            hipLaunchKernelGGL((prefill_split_kernel<D, false>), dim3((unsigned)blocks), dim3(kSplitThreads), 0,
+                               stream, kp);
+    } else if (kp.qk_scale_log2 < 0.f) {
         hipLaunchKernelGGL((prefill_kernel<D, true>), dim3((unsigned)blocks), dim3(kPrefillThreads), 0, stream, kp);
-    else
+    } else {
         hipLaunchKernelGGL((prefill_kernel<D, false>), dim3((unsigned)blocks), dim3(kPrefillThreads), 0, stream, kp);
+    }
 }
 
 }  // namespace
