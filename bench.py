@@ -435,7 +435,9 @@ def time_mixed_step(args):
                                           "frac": round(gbs / HBM_PEAK_GBS, 4)}},
             "prefill_alone": {"ms": round(pms, 5), "what": "the prefill branch's attention alone (two 512-row "
                                                            "chunks on 1024 cached keys), %d per graph" % k,
-                              "roofline": {"bound": "mfma", "kernel": "paged_gqa_prefill (prefill_kernel)",
+                              "roofline": {"bound": "mfma",
+                                           "kernel": "paged_gqa_prefill (prefill_split_kernel: the launch "
+                                                     "has fewer than two workgroups per CU)",
                                            "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
                                            "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}},
             "overlap": round((dms + pms) / ms, 3)}
