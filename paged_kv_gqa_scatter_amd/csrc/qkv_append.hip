@@ -32,6 +32,8 @@
 //  * Epilogue: a lane holds one feature column and 16 token rows of each
 //    32 x 32 tile; the destination row of every token of the tile (its q_out
 //    row and its cache slot) is computed once per workgroup into LDS.
+//  * Calls with enough tokens to give every CU a 256 x 256 tile (prompt
+//    sizes) use those, 8 waves each, with half the L2 bytes per flop.
 //  * Calls with too few tokens to give every CU a 128 x 128 tile (decode
 //    steps) use tiles of 32 tokens x tn features, tn the widest multiple of 8
 //    up to 32 that still gives every CU a tile (24 at 6144 features: 256
@@ -228,6 +230,165 @@ __global__ __launch_bounds__(kQkvThreads) void qkv_append_kernel(QkvKernelArgs p
             store_tile(a, p.n_out, acc[i][jj], m0, 64 * wm + 32 * i, n0 + 64 * wn + 32 * jj + (lane & 31), s_dst);
 }
 
+// Many tokens (prompt sizes): 256 x 256 tiles, 8 waves, one workgroup per CU.
+// A 128 x 128 tile reads 32 KB from L2 per 64-deep step for 2 MFLOP, which
+// at the matrix cores' full rate is as much as an XCD's L2 delivers to its
+// CUs; a 256 x 256 tile reads 64 KB for 8 MFLOP, half the bytes per flop,
+// and its step lasts twice as long, giving the next step's copies twice the
+// time to land.  Wave w computes rows [128 (w % 2), +128) x columns
+// [64 (w / 2), +64) of the tile as 4 x 2 MFMA tiles (6 LDS reads per 8
+// MFMAs); wave w copies rows [32 w, 32 w + 32) of both slices.
+//  * The fragments of substep s + 1 are read while substep s is multiplied,
+//    one read after each of its first six MFMAs (fixed with scheduling-group
+//    barriers), the W fragments first, so the first MFMAs of s + 1 wait for
+//    reads issued five MFMAs earlier rather than for the last one issued.
+//  * Epilogue through LDS: the tile is staged as bf16 rows in the (then
+//    free) stage memory and leaves in 16-byte pieces, 32 lanes to a
+//    512-byte row, instead of as 2-byte stores straight from the MFMA
+//    layout.  A piece never straddles a head (D is a multiple of 8), so each
+//    has one destination: its q_out row or its token's cache slot.
+constexpr int kBigThreads = 512;
+constexpr int kBigM = 256;
+constexpr int kBigN = 256;
+constexpr int kBigStageBytes = kBigM * kRowBytes;
+constexpr int kBigGroupM = 4;  // token tiles per group: an XCD's 32 workgroups cover 4 x 8 tiles
+constexpr int kOutPitch = kBigN + 8;  // bf16 per staged output row: +16 bytes puts rows 4 apart on other banks
+constexpr int kBigLds = 4 * kBigStageBytes > kBigM * kOutPitch * 2 ? 4 * kBigStageBytes : kBigM * kOutPitch * 2;
+
+__global__ __launch_bounds__(kBigThreads) void qkv_append_big_kernel(QkvKernelArgs p) {
+    // two stages of the X and W slices; after the K loop, the staged output
+    __shared__ __attribute__((aligned(16))) uint8_t sm[kBigLds];
+    __shared__ int64_t s_dst[kBigM];
+    uint8_t(*sX)[kBigStageBytes] = reinterpret_cast<uint8_t(*)[kBigStageBytes]>(sm);
+    uint8_t(*sW)[kBigStageBytes] = reinterpret_cast<uint8_t(*)[kBigStageBytes]>(sm + 2 * kBigStageBytes);
+
+    const QkvArgs& a = p.a;
+    const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+    const int tile = xcd * p.per_xcd + j;
+    if (j >= p.per_xcd || tile >= p.tiles) return;
+    const int n_tiles = p.tiles / p.m_tiles;
+    const int group = tile / (kBigGroupM * n_tiles), first_m = group * kBigGroupM;
+    const int group_m = min(p.m_tiles - first_m, kBigGroupM);
+    const int within = tile - group * kBigGroupM * n_tiles;
+    const int m0 = (first_m + within % group_m) * kBigM;
+    const int n0 = (within / group_m) * kBigN;
+    const int T = a.total_new_tokens, K = a.d_model;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    if (threadIdx.x < kBigM) s_dst[threadIdx.x] = token_dst(a, m0 + threadIdx.x);
+
+    uint32_t xoff[4], woff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 32 * wave + 8 * i + lane / 8;
+        const int piece = swz(r, lane % 8);
+        xoff[i] = (uint32_t)((int64_t)min(m0 + r, T - 1) * K * 2 + piece * 16);
+        woff[i] = (uint32_t)((int64_t)min(n0 + r, p.n_out - 1) * K * 2 + piece * 16);
+    }
+    auto issue = [&](int step, int stage) {
+        const uint16_t* xb = a.x + (int64_t)step * kTileK;
+        const uint16_t* wb = a.w + (int64_t)step * kTileK;
+        const uint32_t lx = lds_addr(sX[stage]) + (uint32_t)(32 * wave * kRowBytes);
+        const uint32_t lw = lds_addr(sW[stage]) + (uint32_t)(32 * wave * kRowBytes);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            dma16(xb, xoff[i], lx + i * 1024);
+            dma16(wb, woff[i], lw + i * 1024);
+        }
+    };
+
+    // operand reads: lane -> row (lane % 32) of a 32-row block, piece
+    // 2 s + lane / 32 of substep s; the swizzle key depends on the row
+    // modulo 16 only, so one offset per substep serves every 32-row block
+    const int wm = wave & 1, wn = wave >> 1;
+    int aoff[4], boff[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int ra = 128 * wm + (lane & 31), rb = 64 * wn + (lane & 31);
+        aoff[s] = ra * kRowBytes + swz(ra, 2 * s + (lane >> 5)) * 16;
+        boff[s] = rb * kRowBytes + swz(rb, 2 * s + (lane >> 5)) * 16;
+    }
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][jj][e] = 0.f;
+
+    const int steps = K / kTileK;
+    issue(0, 0);
+    for (int st = 0; st < steps; ++st) {
+        const int cur = st & 1;
+        wait_vm_all();
+        __syncthreads();
+        if (st + 1 < steps) issue(st + 1, cur ^ 1);
+        const uint8_t* xs = sX[cur];
+        const uint8_t* ws = sW[cur];
+        u32x4 af[2][4], bfr[2][2];  // fragments of substeps s (s % 2) and s + 1
+        auto read = [&](int s) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) bfr[s & 1][t] = *reinterpret_cast<const u32x4*>(ws + boff[s] + t * 32 * kRowBytes);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) af[s & 1][t] = *reinterpret_cast<const u32x4*>(xs + aoff[s] + t * 32 * kRowBytes);
+        };
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (s == 0) read(0);
+            if (s + 1 < 4) read(s + 1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[s & 1][i]),
+                                                                         as_bf16x8(bfr[s & 1][jj]), acc[i][jj], 0, 0, 0);
+            if (s == 0) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // substep 0's own reads first
+            if (s + 1 < 4) {
+#pragma unroll
+                for (int i = 0; i < 6; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read of substep s + 1
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            } else {
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            }
+        }
+    }
+
+    __syncthreads();  // every wave is done with the stages
+    uint16_t* so = reinterpret_cast<uint16_t*>(sm);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int c = 64 * wn + 32 * jj + (lane & 31);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = 128 * wm + 32 * i + 8 * (e / 4) + 4 * (lane >> 5) + (e & 3);
+                so[r * kOutPitch + c] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][jj][e]);
+            }
+        }
+    __syncthreads();
+    const int nq = a.num_q_heads * a.head_dim, nkv = a.num_kv_heads * a.head_dim;
+#pragma unroll 4
+    for (int it = 0; it < kBigM * (kBigN / 8) / kBigThreads; ++it) {
+        const int q = it * kBigThreads + threadIdx.x;
+        const int r = q / (kBigN / 8), n = n0 + 8 * (q % (kBigN / 8));  // row and first feature of the piece
+        const int t = m0 + r;
+        if (t >= T || n >= p.n_out) continue;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(so + r * kOutPitch + (n - n0));
+        if (n < nq) {
+            store16(a.q_out + (int64_t)t * nq + n, v);
+        } else if (s_dst[r] >= 0) {
+            const int f = n < nq + nkv ? n - nq : n - nq - nkv;
+            uint16_t* base = n < nq + nkv ? a.k_pool : a.v_pool;
+            store16(base + s_dst[r] + (int64_t)(f / a.head_dim) * a.block_size * a.head_dim + f % a.head_dim, v);
+        }
+    }
+}
+
 // Few tokens (a decode step): the weight stream dominates and 128 x 128 tiles
 // would leave most CUs idle, so a workgroup takes a 32 x tn tile (computed as
 // 32 x 32, the columns past tn masked) and its
@@ -325,6 +486,17 @@ hipError_t launch_qkv_append(const QkvArgs& a, hipStream_t stream) {
         kp.per_xcd = (kp.tiles + kXcds - 1) / kXcds;
         hipLaunchKernelGGL(qkv_append_skinny_kernel, dim3((unsigned)(kp.per_xcd * kXcds)), dim3(kSkinnyThreads), 0,
                            stream, kp);
+        return hipGetLastError();
+    }
+    const int big_m = (a.total_new_tokens + kBigM - 1) / kBigM;
+    const int big_tiles = big_m * (int)((kp.n_out + kBigN - 1) / kBigN);
+    if (big_tiles >= device_cu_count()) {  // enough 256 x 256 tiles to give every CU one
+        kp.m_tiles = big_m;
+        kp.tiles = big_tiles;
+        kp.tn = kBigN;
+        kp.per_xcd = (kp.tiles + kXcds - 1) / kXcds;
+        hipLaunchKernelGGL(qkv_append_big_kernel, dim3((unsigned)(kp.per_xcd * kXcds)), dim3(kBigThreads), 0, stream,
+                           kp);
         return hipGetLastError();
     }
     kp.tn = kTileN;

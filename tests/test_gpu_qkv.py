@@ -158,6 +158,9 @@ def test_qkv_qwen3_prefill_sampled(orc):
     cu = a.cu_new_lens
     pick = set(rng.choice(T, 24, replace=False).tolist()) | set(cu[:-1].tolist()) | set((cu[1:] - 1).tolist())
     pick |= {127, 128, 255, 256, 511, 512, T - 257, T - 256, T - 1}
+    last = (T - 1) // 256 * 256  # first token of the last (ragged) 256-token tile
+    pick |= {last - 1, last, last + 1}
+    pick |= set(range(last + 64, last + 96))  # a whole 32-row block of an MFMA tile in the last tile
     _say(f"case qkv qwen3-8b prefill prompts: T {T}, {len(pick)} tokens sampled")
     _compare(orc, x, w, 32, 8, 128, 256, case.num_blocks, cu, a.ctx_lens, a.block_table, sorted(pick), "sampled")
 
@@ -175,6 +178,22 @@ def test_qkv_wide_tiles_ragged_tails(orc):
                                                                16384, T - 1}
     _say(f"case qkv wide tiles: T {T}, n_out {(hq + 2 * hkv) * d}, {len(pick)} tokens sampled")
     _compare(orc, x, w, hq, hkv, d, bs, nb, cu, ctx, table, sorted(pick), "wide, ragged tails")
+
+
+def test_qkv_big_tiles_ragged_tails(orc):
+    # enough tokens for the 256 x 256 tile path (86 x 3 = 258 tiles), with a
+    # ragged token tail (22000 = 85 * 256 + 240), a ragged feature tail
+    # (n_out 576 = 2.25 x 256) and a d_model of three 64-deep steps
+    rng = np.random.default_rng(43)
+    hq, hkv, d, bs, dm = 3, 3, 64, 16, 192
+    table, cu, ctx, nb = _placement(rng, [5, 0, 250], [9000, 12000, 1000], bs)
+    x, w = _inputs(rng, int(cu[-1]), dm, (hq + 2 * hkv) * d)
+    T = int(cu[-1])
+    pick = set(rng.choice(T, 60, replace=False).tolist()) | {0, 1, 255, 256, 511, 512, 8999, 9000, 20999, 21000,
+                                                               T - 241, T - 240, T - 239, T - 2, T - 1}
+    pick |= set(range(21760, 21760 + 32))  # a whole 32-row block of the ragged last tile
+    _say(f"case qkv big tiles: T {T}, n_out {(hq + 2 * hkv) * d}, dm {dm}, {len(pick)} tokens sampled")
+    _compare(orc, x, w, hq, hkv, d, bs, nb, cu, ctx, table, sorted(pick), "big, ragged tails")
 
 
 @pytest.mark.parametrize("dm", [256, 192])
