@@ -473,10 +473,11 @@ def time_prefill_workload(args):
 
 
 def device_context():
-    """The device and practical HBM ceilings: a 1 GiB device-to-device copy
+    """The device and practical ceilings: a 1 GiB device-to-device copy
     (read + write bytes over its median time, 10 timed copies), a 2 GiB plain
-    read (pkv_read_probe, median of 10), and the engine clock the driver
-    reports as current when there is one GPU to read it from."""
+    read (pkv_read_probe, median of 10), a plain bf16 MFMA stream
+    (pkv_mfma_probe, median of 10), and the engine clock the driver reports
+    as current when there is one GPU to read it from."""
     import glob
     import torch
     n = 1 << 29  # int16 elements: 1 GiB
@@ -509,13 +510,31 @@ def device_context():
     rms = sorted(a.elapsed_time(b) for a, b in evs)[len(evs) // 2]
     read_bytes = data.numel() * data.element_size()
     del data, sink
+    # the bf16 matrix cores' rate on a plain MFMA stream (pkv_mfma_probe:
+    # the instruction of the prefill and the fused QKV projection)
+    iters = 4096
+    sink = torch.empty(4 * 256 * pkv.MFMA_PROBE_WORKGROUPS, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        pkv.mfma_probe(iters, sink)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for a, b in evs:
+        a.record(s)
+        pkv.mfma_probe(iters, sink)
+        b.record(s)
+    torch.cuda.synchronize()
+    mms = sorted(a.elapsed_time(b) for a, b in evs)[len(evs) // 2]
+    del sink
     props = torch.cuda.get_device_properties(0)
     ctx = {"name": props.name, "compute_units": props.multi_processor_count,
            "copy_GBps": round(2 * 2 * n / (ms * 1e-3) / 1e9, 1),
            "copy_note": "1 GiB device-to-device copy, read + write bytes",
            "read_GBps": round(read_bytes / (rms * 1e-3) / 1e9, 1),
            "read_note": "2 GiB read once by pkv_read_probe (16-byte non-temporal loads): the practical read "
-                        "ceiling for the HBM-bound decode kernels"}
+                        "ceiling for the HBM-bound decode kernels",
+           "mfma_bf16_TFLOPs": round(pkv.mfma_probe_flops(iters) / (mms * 1e-3) / 1e12, 1),
+           "mfma_note": "pkv_mfma_probe: two chains of v_mfma_f32_32x32x16_bf16 per wave, two waves per SIMD, no "
+                        "memory traffic (median of 10): the practical ceiling for the MFMA-bound prefill and "
+                        "projection (the part runs below 2.4 GHz under this load)"}
     clocks = []
     for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
         try:

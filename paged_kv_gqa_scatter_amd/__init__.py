@@ -34,8 +34,10 @@ BLOCK_EXPORTS = ("pkv_bm_create", "pkv_bm_destroy", "pkv_bm_available", "pkv_bm_
 INT8_EXPORTS = ("pkv_kv_append_int8", "pkv_decode_int8_workspace_bytes", "pkv_paged_gqa_decode_int8",
                 "pkv_paged_gqa_decode_append_int8")
 QKV_EXPORTS = ("pkv_qkv_project_append",)
-DIAG_EXPORTS = ("pkv_read_probe",)
+DIAG_EXPORTS = ("pkv_read_probe", "pkv_mfma_probe")
 READ_PROBE_WORKGROUPS = 8192  # PKV_READ_PROBE_WORKGROUPS
+MFMA_PROBE_WORKGROUPS = 512  # PKV_MFMA_PROBE_WORKGROUPS
+MFMA_PROBE_MAX_ITERS = 1 << 20  # PKV_MFMA_PROBE_MAX_ITERS
 
 
 class PkvError(RuntimeError):
@@ -102,6 +104,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_qkv_project_append.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, I32, P]
     lib.pkv_read_probe.restype = I32
     lib.pkv_read_probe.argtypes = [P, SZ, P, SZ, P]
+    lib.pkv_mfma_probe.restype = I32
+    lib.pkv_mfma_probe.argtypes = [I32, P, SZ, P]
     lib.pkv_paged_gqa_prefill.restype = I32
     lib.pkv_paged_gqa_prefill.argtypes = [P, P, P, I32, I32, P, P, P, I32, P, I32, I32, I32, I32, I32, I32, I32,
                                           F32, P]
@@ -473,3 +477,19 @@ def read_probe(data: torch.Tensor, sink: torch.Tensor) -> None:
     st = lib().pkv_read_probe(data.data_ptr(), data.numel() * data.element_size(), sink.data_ptr(),
                               sink.numel() * sink.element_size(), _stream())
     _check(st, "read_probe")
+
+
+def mfma_probe_flops(iters: int) -> int:
+    """Flops of one pkv_mfma_probe launch of ``iters`` rounds."""
+    return MFMA_PROBE_WORKGROUPS * 4 * 8 * iters * 2 * 32 * 32 * 16
+
+
+def mfma_probe(iters: int, sink: torch.Tensor) -> None:
+    """Run the bf16 MFMA stream of ``pkv_mfma_probe`` (include/pkv_diag.h)
+    on the current stream: ``mfma_probe_flops(iters)`` flop, no memory reads.
+    ``sink`` is a device buffer of at least 4 * 256 * MFMA_PROBE_WORKGROUPS
+    bytes whose contents are unspecified afterwards."""
+    if not (sink.is_cuda and sink.is_contiguous()):
+        raise ValueError("sink must be a contiguous device tensor")
+    st = lib().pkv_mfma_probe(int(iters), sink.data_ptr(), sink.numel() * sink.element_size(), _stream())
+    _check(st, "mfma_probe")

@@ -53,6 +53,19 @@ def test_diag_header_declares_its_functions():
     assert set(declared_functions(DIAG_HEADER)) == set(pkv.DIAG_EXPORTS)
     text = open(DIAG_HEADER).read()
     assert f"#define PKV_READ_PROBE_WORKGROUPS {pkv.READ_PROBE_WORKGROUPS}" in text
+    assert f"#define PKV_MFMA_PROBE_WORKGROUPS {pkv.MFMA_PROBE_WORKGROUPS}" in text
+    assert "#define PKV_MFMA_PROBE_MAX_ITERS (1 << 20)" in text and pkv.MFMA_PROBE_MAX_ITERS == 1 << 20
+
+
+def test_mfma_probe_rejects(lib):
+    sink_bytes = 4 * 256 * pkv.MFMA_PROBE_WORKGROUPS
+    assert lib.pkv_mfma_probe(16, None, sink_bytes, None) == 1
+    assert lib.pkv_mfma_probe(16, A16 + 2, sink_bytes, None) == 3
+    assert lib.pkv_mfma_probe(0, A16, sink_bytes, None) == 2
+    assert lib.pkv_mfma_probe(-5, A16, sink_bytes, None) == 2
+    assert lib.pkv_mfma_probe(pkv.MFMA_PROBE_MAX_ITERS + 1, A16, sink_bytes, None) == 2
+    assert lib.pkv_mfma_probe(16, A16, sink_bytes - 4, None) == 4
+    assert pkv.mfma_probe_flops(1) == pkv.MFMA_PROBE_WORKGROUPS * 4 * 8 * 32768
 
 
 def test_read_probe_rejects(lib):

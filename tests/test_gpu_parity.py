@@ -693,6 +693,16 @@ def test_read_probe_reads_without_writing():
     assert bool((sink == 0x5A).all())
 
 
+def test_mfma_probe_runs_without_writing():
+    """pkv_mfma_probe for 16 rounds: the status is OK and the sink keeps its
+    contents (a slot is written only if a finite fold had a NaN's bits)."""
+    import paged_kv_gqa_scatter_amd as pkv
+    sink = torch.full((4 * 256 * pkv.MFMA_PROBE_WORKGROUPS,), 0x5A, dtype=torch.uint8, device="cuda")
+    pkv.mfma_probe(16, sink)
+    torch.cuda.synchronize()
+    assert bool((sink == 0x5A).all())
+
+
 def test_invalid_block_ids_stay_inside_their_sequence(orc):
     # table entries are preconditions; a bad one (negative, or past the pool)
     # is read as block 0 and its keys masked by the decode, and skipped by
