@@ -594,6 +594,35 @@ def time_long_decode(args):
     return res
 
 
+def _private_long_case():
+    """16 sequences of 32768 cached tokens + 1 new, private blocks (seeded
+    lengths and placement, values drawn on the device)."""
+    from paged_kv_gqa_scatter_amd import workloads as W
+    rng = np.random.default_rng(16)
+    return W.build_case("qwen3_8b_16x32k_private", rng, hq=32, hkv=8, d=128, bs=256,
+                        ctx_lens=np.full(16, 32768), new_lens=np.ones(16, np.int64), kinds="d" * 16,
+                        draw_values=False)
+
+
+def _time_decode_calls(dc, n):
+    """Events around each of n decode calls of step 0 (after its append and
+    3 untimed calls): the per-call times in ms."""
+    import torch
+    step = dc.steps[0]
+    dc.append(step["append"])
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        dc.decode(step["decode"])
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record(stream)
+        dc.decode(step["decode"])
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
 def time_private_long_decode(args):
     """Decode over private long contexts only: 16 sequences of 32768 cached
     tokens + 1 (2.15 GB of K/V, no block shared), the streaming rate of the
@@ -603,28 +632,11 @@ def time_private_long_decode(args):
     from paged_kv_gqa_scatter_amd import workloads as W
     from paged_kv_gqa_scatter_amd.runner import DeviceCase
 
-    rng = np.random.default_rng(16)
-    case = W.build_case("qwen3_8b_16x32k_private", rng, hq=32, hkv=8, d=128, bs=256,
-                        ctx_lens=np.full(16, 32768), new_lens=np.ones(16, np.int64), kinds="d" * 16,
-                        draw_values=False)
-    dec = case.steps[0].decode
-    uniq = W.decode_unique_kv_bytes(case, dec)
+    case = _private_long_case()
+    uniq = W.decode_unique_kv_bytes(case, case.steps[0].decode)
     dc = DeviceCase(case)
     dc.run_fills()
-    step = dc.steps[0]
-    dc.append(step["append"])
-    stream = torch.cuda.current_stream()
-    for _ in range(3):
-        dc.decode(step["decode"])
-    torch.cuda.synchronize()
-    n = max(5, args.prefill_steps)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    for a, b in evs:
-        a.record(stream)
-        dc.decode(step["decode"])
-        b.record(stream)
-    torch.cuda.synchronize()
-    times = [a.elapsed_time(b) for a, b in evs]
+    times = _time_decode_calls(dc, max(5, args.prefill_steps))
     ms = float(np.mean(times))
     del dc
     torch.cuda.empty_cache()
@@ -638,11 +650,14 @@ def time_private_long_decode(args):
                          "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
-def time_int8(args, bf16_step_ms, bf16_long_ms):
+def time_int8(args, bf16_step_ms, bf16_long_ms, bf16_private_ms=None):
     """The INT8 KV cache (quantising kv_append_int8, paged_gqa_decode_int8) on
     the headline decode step (both calls in one HIP graph per pool copy,
-    rotated past the last-level cache) and on the long-context decode; bytes
-    are the unique code and scale bytes a call must read (D + 4 per row)."""
+    rotated past the last-level cache), on the long-context decode and on
+    the private long-context decode (16 x 32769 keys, no shared block: the
+    streaming rate, where half the bytes should show as up to twice the
+    speed); bytes are the unique code and scale bytes a call must read
+    (D + 4 per row)."""
     import torch
     from paged_kv_gqa_scatter_amd import workloads as W
     from paged_kv_gqa_scatter_amd.runner import Int8DeviceCase
@@ -681,20 +696,7 @@ def time_int8(args, bf16_step_ms, bf16_long_ms):
         nbytes = W.decode_unique_int8_kv_bytes(case, dec)
         dc = Int8DeviceCase(case)
         dc.run_fills()
-        step = dc.steps[0]
-        dc.append(step["append"])
-        stream = torch.cuda.current_stream()
-        for _ in range(3):
-            dc.decode(step["decode"])
-        torch.cuda.synchronize()
-        n = max(5, args.prefill_steps)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        for a, b in evs:
-            a.record(stream)
-            dc.decode(step["decode"])
-            b.record(stream)
-        torch.cuda.synchronize()
-        lms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        lms = float(np.mean(_time_decode_calls(dc, max(5, args.prefill_steps))))
         del dc
         torch.cuda.empty_cache()
         gbs = nbytes / (lms * 1e-3) / 1e9
@@ -707,6 +709,21 @@ def time_int8(args, bf16_step_ms, bf16_long_ms):
                          "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4)}}
         attach_traffic(res["long_context_decode"]["roofline"], "int8_long_decode")
+        case = _private_long_case()
+        nbytes = W.decode_unique_int8_kv_bytes(case, case.steps[0].decode)
+        dc = Int8DeviceCase(case)
+        dc.run_fills()
+        pms = float(np.mean(_time_decode_calls(dc, max(5, args.prefill_steps))))
+        del dc
+        torch.cuda.empty_cache()
+        gbs = nbytes / (pms * 1e-3) / 1e9
+        res["private_long_decode"] = {
+            "workload": "the private long-context decode (16 seqs x 32769 keys, no shared block) over an INT8 cache",
+            "ms": round(pms, 5), "unique_kv_bytes": int(nbytes),
+            "speedup_vs_bf16": round(bf16_private_ms / pms, 3) if bf16_private_ms else None,
+            "roofline": {"bound": "hbm", "kernel": "paged_gqa_decode_int8 (decode_int8_kernel + decode_merge_kernel)",
+                         "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}}
     return res
 
 
@@ -944,7 +961,8 @@ def main():
     if not args.no_qkv:
         line["qkv_project_append"] = time_qkv(args)
     if not args.no_int8:
-        line["int8_kv_cache"] = time_int8(args, step_ms, line.get("long_context_decode", {}).get("ms"))
+        line["int8_kv_cache"] = time_int8(args, step_ms, line.get("long_context_decode", {}).get("ms"),
+                                          line.get("private_long_decode", {}).get("ms"))
     if not args.no_mixed:
         line["mixed_step"] = time_mixed_step(args)
     if not args.no_append:
