@@ -160,15 +160,20 @@ def test_config3_prefill_sampled(orc):
     compare(gpu, ref, f"prefill {len(items)} sampled rows")
 
 
-def test_prefill_reduced_full(orc):
-    # several 128-row tiles with ragged tails, GQA 4, full comparison
+@pytest.mark.parametrize("d,new_lens", [(128, [300, 129, 517]), (128, [300, 129, 517, 200]),
+                                        (64, [300, 129, 517, 200])])
+def test_prefill_reduced_full(orc, d, new_lens):
+    # several 128-row tiles with ragged tails, GQA 4, full comparison; 480
+    # workgroups (under two per CU: the kernel that splits each workgroup's
+    # keys between two halves) and 640 (the one-pass kernel), at head_dim
+    # 128 and 64
     rng = np.random.default_rng(303)
-    case = W.build_case("prefill_reduced", rng, hq=32, hkv=8, d=128, bs=256, ctx_lens=[0, 0, 0],
-                        new_lens=[300, 129, 517], kinds="ppp")
+    case = W.build_case(f"prefill_reduced_d{d}", rng, hq=32, hkv=8, d=d, bs=256, ctx_lens=[0] * len(new_lens),
+                        new_lens=new_lens, kinds="p" * len(new_lens))
     _say(f"case {case.name}")
     outs = _dev()(case).run_all()
     ref, _ = oracle_outputs(case, orc)
-    compare(outs[0]["prefill"], ref[0]["prefill"], "prefill 3 prompts")
+    compare(outs[0]["prefill"], ref[0]["prefill"], f"prefill {len(new_lens)} prompts, d{d}")
 
 
 def test_config4_mixed(orc):
@@ -222,12 +227,14 @@ def test_decode_edge_lengths(orc, d, bs, hq, hkv):
     assert np.array_equal(out[-1], np.zeros_like(out[-1])), "empty sequence must give zeros"
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (32, 8)])
 @pytest.mark.parametrize("ctx", [0, 1000])
-def test_prefill_edge_qlens(orc, ctx):
+def test_prefill_edge_qlens(orc, ctx, hq, hkv):
+    # 8 / 2 heads: 168 workgroups (the split kernel); 32 / 8: 672 (one pass)
     qlens = [1, 127, 128, 129, 255, 256, 257]
     rng = np.random.default_rng(2000 + ctx)
-    case = W.build_case(f"prefill_edges_ctx{ctx}", rng, hq=8, hkv=2, d=128, bs=256, ctx_lens=[ctx] * len(qlens),
-                        new_lens=qlens, kinds="p" * len(qlens))
+    case = W.build_case(f"prefill_edges_ctx{ctx}_h{hq}", rng, hq=hq, hkv=hkv, d=128, bs=256,
+                        ctx_lens=[ctx] * len(qlens), new_lens=qlens, kinds="p" * len(qlens))
     _say(f"case {case.name}: q_lens {qlens}")
     out = _dev()(case).run_all()[0]["prefill"]
     ref, _ = oracle_outputs(case, orc)
