@@ -5,9 +5,11 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import paged_kv_gqa_scatter_amd as pkv
+from paged_kv_gqa_scatter_amd import workloads as W
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pkv.h")
@@ -310,3 +312,19 @@ def test_decode_append_static_rejects(lib):
     assert f(*args(big)) == 8
     assert lib.pkv_status_string(8) == b"the call needs more decode scratch than the library's static 32 MiB"
 
+
+
+def test_run_cli_arguments():
+    # the workload runner's command line (python -m paged_kv_gqa_scatter_amd.run):
+    # argument checks and the named cases, without a GPU
+    from paged_kv_gqa_scatter_amd import run
+    a = run.parse_args(["--config", "3", "--seed", "7", "--repeat", "2"])
+    assert (a.config, a.seed, a.repeat, a.int8) == (3, 7, 2, False)
+    for bad in (["--config", "9"], ["--config", "2", "--repeat", "0"], ["--config", "3", "--int8"], []):
+        with pytest.raises(SystemExit):
+            run.parse_args(bad)
+    assert run.parse_args(["--config", "5", "--int8"]).int8
+    assert run.build_case(4).name == W.config4_mixed().name
+    c = run.build_case(3, 7)
+    assert c.name == W.config3_prefill(seed=7, draw_values=False).name
+    assert np.array_equal(c.steps[0].prefill.cu_q_lens, W.config3_prefill(seed=7, draw_values=False).steps[0].prefill.cu_q_lens)
